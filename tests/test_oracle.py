@@ -1,0 +1,317 @@
+"""Pins for the CPU oracle: each test checks it against something other than
+itself — a library routine, a closed form, brute force, or an invariant the
+method fixes.  CPU only."""
+import math
+import struct
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import predictor as O
+from rvq_codebook_code_amd import synth
+
+
+def micro_geometry(**over):
+    base = dict(d_talker=48, d_model=32, n_layers=2, n_q_heads=4, n_kv_heads=2,
+                head_dim=8, d_ffn=64, vocab=32, rms_eps=1e-6, rope_base=1e4,
+                weight_dtype="f32", emb_format="f32")
+    base.update(over)
+    return synth.Geometry(**base)
+
+
+def model_and_inputs(geom, B, wseed=7, iseed=8):
+    W = synth.make_weights(geom, wseed)
+    H, q0 = synth.make_inputs(geom, B, 1, iseed)
+    return W, O.OracleModel(W, geom), H[0], q0[0]
+
+
+# ----------------------------------------------------------------------------
+# building blocks against closed forms and library routines
+# ----------------------------------------------------------------------------
+
+def test_rope_matches_complex_rotation():
+    """Rotate-half RoPE == multiplying z_i = x_i + j*x_{i+hd/2} by
+    exp(j*pos*base**(-2i/hd)) (the rotation written with complex numbers)."""
+    rng = np.random.default_rng(0)
+    hd, base = 16, 1e4
+    for pos in [0, 1, 5, 15]:
+        x = rng.standard_normal(hd)
+        y = O.rope(x, pos, base)
+        z = x[: hd // 2] + 1j * x[hd // 2:]
+        theta = pos * base ** (-2.0 * np.arange(hd // 2) / hd)
+        w = z * np.exp(1j * theta)
+        np.testing.assert_allclose(y[: hd // 2], w.real, atol=1e-13)
+        np.testing.assert_allclose(y[hd // 2:], w.imag, atol=1e-13)
+
+
+def test_rope_identity_at_zero_and_relative_scores():
+    rng = np.random.default_rng(1)
+    hd, base = 128, 1e6
+    q, k = rng.standard_normal(hd), rng.standard_normal(hd)
+    np.testing.assert_array_equal(O.rope(q, 0, base), q)
+    # q_m . k_n depends only on m - n
+    ref = O.rope(q, 7, base) @ O.rope(k, 3, base)
+    for s in [1, 4, 8]:
+        assert abs(O.rope(q, 7 + s, base) @ O.rope(k, 3 + s, base) - ref) < 1e-10
+    # every (i, i+hd/2) pair keeps its length
+    y = O.rope(q, 11, base)
+    np.testing.assert_allclose(y[:64] ** 2 + y[64:] ** 2, q[:64] ** 2 + q[64:] ** 2, rtol=1e-12)
+
+
+def test_rms_norm_matches_torch():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((3, 5, 64))
+    g = 1 + 0.1 * rng.standard_normal(64)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (64,), torch.from_numpy(g), eps=1e-6)
+    np.testing.assert_allclose(O.rms_norm(x, g, 1e-6), ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_silu_matches_torch():
+    z = np.linspace(-20, 20, 101)
+    np.testing.assert_allclose(O.silu(z), torch.nn.functional.silu(torch.from_numpy(z)).numpy(),
+                               rtol=1e-12, atol=1e-15)
+
+
+def test_bf16_bit_patterns():
+    bits = np.array([0x3F80, 0xC000, 0x3F81, 0x0000, 0x8000, 0x7F7F], dtype=np.uint16)
+    vals = O.bf16_bits_to_f64(bits)
+    assert list(vals[:5]) == [1.0, -2.0, 1.0078125, 0.0, -0.0]
+    assert vals[5] == (2 - 2 ** -7) * 2.0 ** 127
+
+
+def test_q8_0_dequant_hand_built_block():
+    """A 34-byte block: f16 scale 0.5 then codes -16..15 -> values 0.5*q."""
+    codes = list(range(-16, 16))
+    blk = struct.pack("<e32b", 0.5, *codes)
+    blk2 = struct.pack("<e32b", -0.25, *([127] * 32))
+    packed = np.frombuffer(blk + blk2, dtype=np.uint8).reshape(1, 68)
+    w = O.dequant_q8_0(packed, 64)
+    np.testing.assert_array_equal(w[0, :32], 0.5 * np.array(codes))
+    np.testing.assert_array_equal(w[0, 32:], np.full(32, -0.25 * 127))
+
+
+def test_q8_0_round_trip_error_bound():
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((8, 96)) * 0.02).astype(np.float32)
+    x[0, :32] = 0.0                                  # all-zero block
+    packed = synth.pack_q8_0(x)
+    w = O.dequant_q8_0(packed, 96)
+    d = packed.reshape(8, 3, 34)[..., :2].copy().view(np.float16).astype(np.float64)
+    err = np.abs(x.astype(np.float64).reshape(8, 3, 32) - w.reshape(8, 3, 32))
+    assert np.all(err <= d / 2 + 1e-12)
+    assert np.all(w[0, :32] == 0)
+
+
+def test_ema_codebook_recovers_direction():
+    """With embedding_sum = z * usage the EMA table equals z up to the
+    1e-7 regulariser: E = z * u / (u + 1e-7)."""
+    rng = np.random.default_rng(4)
+    u = rng.gamma(2.0, 1.0, size=64)
+    z = rng.standard_normal((64, 16))
+    E = O.ema_codebook(z * u[:, None], u)
+    np.testing.assert_allclose(E, z, rtol=2e-6 / u.min())
+    # a transposed broadcast (dividing column j by u[j]) would fail this:
+    np.testing.assert_allclose(E * (u[:, None] + 1e-7), z * u[:, None], rtol=1e-12)
+
+
+def test_argmax_lowest_index_on_ties():
+    lg = np.array([[0.1, 0.5, 0.5, -1.0], [2.0, 2.0, 2.0, 2.0], [-3, -2, -1, -1]], dtype=np.float64)
+    assert list(O.argmax_lowest(lg)) == [1, 0, 2]
+
+
+# ----------------------------------------------------------------------------
+# the loop against brute force and the library's code predictor
+# ----------------------------------------------------------------------------
+
+def test_cached_loop_equals_uncached_brute_force():
+    geom = micro_geometry()
+    _, model, H, q0 = model_and_inputs(geom, B=3)
+    out = O.run_frames(model, H, q0)
+    for b in range(3):
+        ref = O.run_frame_uncached(model, H[b], int(q0[b]))
+        np.testing.assert_allclose(out["logits"][b], ref["logits"], atol=1e-12)
+        np.testing.assert_array_equal(out["tokens"][b], ref["tokens"])
+        np.testing.assert_allclose(out["embsum"][b], ref["embsum"], atol=1e-15)
+
+
+def _library_predictor(W, model, geom):
+    """transformers' Qwen3-Omni talker code predictor with our weights.  Its
+    inputs live in the predictor width, so the projection is folded into its
+    tables: table j-1 := E_j @ W_p^T + b_p (an exact rewrite of a linear map).
+    """
+    from transformers.models.qwen3_omni_moe.configuration_qwen3_omni_moe import (
+        Qwen3OmniMoeTalkerCodePredictorConfig)
+    from transformers.models.qwen3_omni_moe.modeling_qwen3_omni_moe import (
+        Qwen3OmniMoeTalkerCodePredictorModelForConditionalGeneration)
+    g = geom
+    cfg = Qwen3OmniMoeTalkerCodePredictorConfig(
+        vocab_size=g.vocab, hidden_size=g.d_model, intermediate_size=g.d_ffn,
+        num_hidden_layers=g.n_layers, num_attention_heads=g.n_q_heads,
+        num_key_value_heads=g.n_kv_heads, head_dim=g.head_dim, rms_norm_eps=g.rms_eps,
+        rope_parameters={"rope_type": "default", "rope_theta": g.rope_base},
+        num_code_groups=g.n_codebooks)
+    cfg._attn_implementation = "eager"
+    m = Qwen3OmniMoeTalkerCodePredictorModelForConditionalGeneration(cfg).double().eval()
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))
+    with torch.no_grad():
+        for li, lw in enumerate(model.layers):
+            L = m.model.layers[li]
+            L.input_layernorm.weight.copy_(T(lw["attn_norm"]))
+            L.post_attention_layernorm.weight.copy_(T(lw["ffn_norm"]))
+            L.self_attn.q_proj.weight.copy_(T(lw["wq"]))
+            L.self_attn.k_proj.weight.copy_(T(lw["wk"]))
+            L.self_attn.v_proj.weight.copy_(T(lw["wv"]))
+            L.self_attn.o_proj.weight.copy_(T(lw["wo"]))
+            L.self_attn.q_norm.weight.copy_(T(lw["q_norm"]))
+            L.self_attn.k_norm.weight.copy_(T(lw["k_norm"]))
+            L.mlp.gate_proj.weight.copy_(T(lw["w_gate"]))
+            L.mlp.up_proj.weight.copy_(T(lw["w_up"]))
+            L.mlp.down_proj.weight.copy_(T(lw["w_down"]))
+        m.model.norm.weight.copy_(T(model.out_norm))
+        for j in range(g.n_codebooks - 1):
+            m.lm_head[j].weight.copy_(T(model.lm_head[j]))
+            if j + 1 < g.n_codebooks:
+                tab = torch.from_numpy(model.emb[j + 1]) @ T(model.proj_w).T + T(model.proj_b)
+                m.model.codec_embedding[j].weight.copy_(tab)
+    return m
+
+
+def _library_logits(m, model, H, q0, feed):
+    """Drive the library predictor: prefill [proj(H), proj(E_0[q0])], then
+    decode steps fed with ``feed`` [B,15] tokens; return logits [B,15,V]."""
+    prefill = np.stack([O.project(model, H), O.project(model, model.emb[0][q0])], axis=1)
+    out = []
+    with torch.no_grad():
+        r = m(inputs_embeds=torch.from_numpy(prefill), use_cache=True)
+        out.append(r.logits[:, -1].numpy())
+        past = r.past_key_values
+        for k in range(1, 15):
+            r = m(input_ids=torch.from_numpy(feed[:, k - 1:k].astype(np.int64)),
+                  past_key_values=past, generation_steps=k, use_cache=True)
+            out.append(r.logits[:, -1].numpy())
+            past = r.past_key_values
+    return np.stack(out, axis=1)
+
+
+@pytest.mark.parametrize("which", ["tiny", "mha", "b1_shape"])
+def test_loop_matches_library_code_predictor(which):
+    if which == "tiny":
+        geom, B = synth.WORKLOADS["tiny"].geom, 4
+        W = synth.make_weights(geom, synth.WORKLOADS["tiny"].weight_seed)
+        H, q0 = synth.make_inputs(geom, B, 1, 99)
+    elif which == "mha":
+        geom, B = micro_geometry(n_q_heads=4, n_kv_heads=4, rope_base=1e6), 3
+        W = synth.make_weights(geom, 11)
+        H, q0 = synth.make_inputs(geom, B, 1, 12)
+    else:
+        # the 1.7B predictor's shape with a reduced layer count and vocab to
+        # keep the CPU suite short (head_dim 128, 16/8 heads, base 1e6, bf16)
+        geom = synth.scaled_geometry(synth.WORKLOADS["b1"].geom, n_layers=2, vocab=512)
+        B = 2
+        W = synth.make_weights(geom, 13)
+        H, q0 = synth.make_inputs(geom, B, 1, 14)
+    model = O.OracleModel(W, geom)
+    out = O.run_frames(model, H[0], q0[0])
+    lib = _library_predictor(W, model, geom)
+    lg = _library_logits(lib, model, H[0], q0[0], out["tokens"])
+    # the library takes its norms and RoPE tables in fp32
+    np.testing.assert_allclose(out["logits"], lg, atol=2e-5, rtol=0)
+    sure = out["margin"] > 1e-4
+    np.testing.assert_array_equal(out["tokens"][sure], lg.argmax(-1)[sure])
+
+
+def test_zero_layers_closed_form():
+    """With no layers, step k's logits are LM_k . RMSNorm(W_p E_{k-1}[q_{k-1}]
+    + b_p; g_out): H plays no part."""
+    geom = micro_geometry(n_layers=0)
+    W, model, H, q0 = model_and_inputs(geom, B=5)
+    out = O.run_frames(model, H, q0)
+    prev = q0.astype(np.int64)
+    for k in range(1, 16):
+        e = model.emb[k - 1][prev]
+        x = e @ model.proj_w.T + model.proj_b
+        xn = model.out_norm * x / np.sqrt((x * x).mean(-1, keepdims=True) + geom.rms_eps)
+        ref = xn @ model.lm_head[k - 1].T
+        np.testing.assert_allclose(out["logits"][:, k - 1], ref, atol=1e-13)
+        prev = out["tokens"][:, k - 1]
+    out2 = O.run_frames(model, H * 0 + 3.0, q0)
+    np.testing.assert_array_equal(out["logits"], out2["logits"])
+
+
+# ----------------------------------------------------------------------------
+# invariants of the loop
+# ----------------------------------------------------------------------------
+
+def test_batch_composition_invariance():
+    geom = micro_geometry()
+    _, model, H, q0 = model_and_inputs(geom, B=6)
+    full = O.run_frames(model, H, q0)
+    perm = np.array([4, 0, 5, 2])
+    sub = O.run_frames(model, H[perm], q0[perm])
+    np.testing.assert_allclose(sub["logits"], full["logits"][perm], atol=1e-12)
+    np.testing.assert_array_equal(sub["tokens"], full["tokens"][perm])
+    one = O.run_frames(model, H[3:4], q0[3:4])
+    np.testing.assert_allclose(one["embsum"], full["embsum"][3:4], atol=1e-15)
+
+
+def test_embsum_is_sum_of_lookups():
+    geom = micro_geometry()
+    _, model, H, q0 = model_and_inputs(geom, B=4)
+    out = O.run_frames(model, H, q0)
+    for b in range(4):
+        acc = model.emb[0][q0[b]].copy()
+        for j in range(1, 16):
+            acc += model.emb[j][out["tokens"][b, j - 1]]
+        np.testing.assert_allclose(out["embsum"][b], acc, atol=1e-15)
+
+
+def test_greedy_consistency_and_teacher_forcing_replay():
+    geom = micro_geometry()
+    _, model, H, q0 = model_and_inputs(geom, B=4)
+    out = O.run_frames(model, H, q0)
+    np.testing.assert_array_equal(out["tokens"], out["logits"].astype(np.float32).argmax(-1))
+    again = O.run_frames(model, H, q0, force=out["tokens"])
+    for key in ("tokens", "logits", "embsum"):
+        np.testing.assert_array_equal(again[key], out[key])
+    # forcing other tokens changes the fed-back path and the embedding sum
+    rng = np.random.default_rng(5)
+    forced = rng.integers(0, geom.vocab, size=(4, 15))
+    f = O.run_frames(model, H, q0, force=forced)
+    np.testing.assert_array_equal(f["logits"][:, 0], out["logits"][:, 0])
+    acc = model.emb[0][q0] + sum(model.emb[j][forced[:, j - 1]] for j in range(1, 16))
+    np.testing.assert_allclose(f["embsum"], acc, atol=1e-15)
+
+
+def test_position_zero_ignores_query_and_key_weights():
+    """At position 0 softmax over one key is 1 and RoPE(0) is the identity,
+    so perturbing W_q, W_k, g_q, g_k cannot change position 0's outputs,
+    while it must change later positions."""
+    geom = micro_geometry()
+    W, model, H, q0 = model_and_inputs(geom, B=2)
+    a = O.run_frames(model, H, q0, want_taps=True)
+    for lw in model.layers:
+        lw["wq"] = lw["wq"] * 1.7 + 0.01
+        lw["wk"] = -lw["wk"]
+        lw["q_norm"] = lw["q_norm"] * 3.0
+        lw["k_norm"] = lw["k_norm"] * 0.5
+    b = O.run_frames(model, H, q0, want_taps=True)
+    np.testing.assert_array_equal(a["taps"][0], b["taps"][0])
+    assert np.abs(a["taps"][1] - b["taps"][1]).max() > 1e-3
+
+
+def test_tiny_workload_is_not_degenerate():
+    """The tiny parity workload must exercise the comparison: most steps
+    carry a decisive margin and the tokens spread over the vocabulary."""
+    wl = synth.WORKLOADS["tiny"]
+    W = synth.make_weights(wl.geom, wl.weight_seed)
+    H, q0 = synth.make_inputs(wl.geom, wl.batch, wl.frames, wl.input_seed)
+    model = O.OracleModel(W, wl.geom)
+    toks, margins = [], []
+    for f in range(wl.frames):
+        out = O.run_frames(model, H[f], q0[f])
+        toks.append(out["tokens"])
+        margins.append(out["margin"])
+    margins = np.concatenate(margins).ravel()
+    assert (margins > 0.05).mean() > 0.4
+    assert len(np.unique(np.concatenate(toks))) >= wl.geom.vocab // 4
