@@ -1,0 +1,594 @@
+// Host side of the code-predictor library: the C ABI declared in qp.h,
+// create-time weight preparation, and the two frame drivers (one persistent
+// cooperative kernel per frame, or one kernel per phase).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "qp.h"
+#include "qp_common.h"
+#include "qp_phases.h"
+
+using namespace qp;
+
+// ---------------------------------------------------------------------------
+// device kernels
+// ---------------------------------------------------------------------------
+
+namespace {
+
+__device__ void grid_sync(unsigned long long* ctr, unsigned long long target, unsigned* err) {
+    __threadfence();  // every wave publishes its own stores (agent scope)
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __hip_atomic_fetch_add(ctr, 1ull, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        unsigned spins = 0;
+        while (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            __builtin_amdgcn_s_sleep(2);
+            ++spins;
+            // bounded wait: a barrier that never completes flags the frame
+            // and lets every workgroup run to its end
+            if ((spins & 255u) == 0u) {
+                if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kErrBarrierTimeout)
+                    break;
+                if (spins > (1u << 22)) {
+                    atomicOr(err, kErrBarrierTimeout);
+                    break;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+template <int WT>
+__global__ __launch_bounds__(kThreads) void k_persistent(Model m, RunArgs a) {
+    __shared__ float lds[kLdsFloats];
+    const int wg = blockIdx.x, nwg = gridDim.x;
+    unsigned long long bi = 0;
+    auto sync = [&]() {
+        ++bi;
+        grid_sync(m.bar, a.bar_base + bi * static_cast<unsigned long long>(nwg), m.err);
+    };
+    phase_init<WT>(m, a, lds, wg, nwg);
+    for (int s = 1; s <= kSteps; ++s) {
+        for (int l = 0; l < m.L; ++l) {
+            sync();
+            phase_qkv<WT>(m, a, s, l, lds, wg, nwg);
+            sync();
+            phase_attn(m, a, s, l, lds, wg, nwg);
+            sync();
+            phase_oproj<WT>(m, a, s, l, lds, wg, nwg);
+            sync();
+            phase_up<WT>(m, a, s, l, lds, wg, nwg);
+            sync();
+            phase_down<WT>(m, a, s, l, lds, wg, nwg);
+        }
+        sync();
+        phase_lm<WT>(m, a, s, lds, wg, nwg);
+        sync();
+        phase_next(m, a, s, wg, nwg);
+    }
+}
+
+template <int WT>
+__global__ __launch_bounds__(kThreads) void k_phase(Model m, RunArgs a, int ph, int s, int l) {
+    __shared__ float lds[kLdsFloats];
+    run_phase<WT>(m, a, ph, s, l, lds, blockIdx.x, gridDim.x);
+}
+
+// --- create-time kernels ----------------------------------------------------
+
+// EMA codebook: E[v][k] = S[v][k] / (u[v] + 1e-7), fp32 add then fp32 divide.
+__global__ void k_ema(const float* S, const float* u, float* E, int V, int dT) {
+    const size_t n = static_cast<size_t>(V) * dT;
+    for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
+         i += static_cast<size_t>(gridDim.x) * blockDim.x) {
+        const int v = static_cast<int>(i / dT);
+        E[i] = S[i] / (u[v] + 1e-7f);
+    }
+}
+
+__device__ float mat_elem(const Mat& W, int wt, int K, int n, int k) {
+    const size_t off = static_cast<size_t>(n) * K + k;
+    if (wt == WT_F32) return static_cast<const float*>(W.w)[off];
+    if (wt == WT_BF16) return bf16_to_f32(static_cast<const uint16_t*>(W.w)[off]);
+    return static_cast<float>(static_cast<const int8_t*>(W.w)[off]) *
+           W.scale[static_cast<size_t>(n) * (K / 32) + (k >> 5)];
+}
+
+// Projected codebook tables: P[j][v][n] = sum_k W_p[n][k] * E_j[v][k] + b_p[n]
+// for j = 0..14 (fp32, 64x64 output tiles, 32-wide k slices through LDS).
+__global__ __launch_bounds__(256) void k_ptab(Model m, float* P) {
+    __shared__ float As[32][65];  // [k][v]
+    __shared__ float Bs[32][65];  // [k][n]
+    const int j = blockIdx.z;
+    const int v0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    float acc[4][4] = {};
+    for (int k0 = 0; k0 < m.dT; k0 += 32) {
+        for (int idx = threadIdx.x; idx < 32 * 64; idx += 256) {
+            const int kk = idx & 31, rr = idx >> 5;
+            const int v = v0 + rr, n = n0 + rr, k = k0 + kk;
+            As[kk][rr] = (v < m.V && k < m.dT) ? emb_elem(m, j, v, k) : 0.f;
+            Bs[kk][rr] = (n < m.dP && k < m.dT) ? mat_elem(m.proj, m.wt, m.dT, n, k) : 0.f;
+        }
+        __syncthreads();
+        for (int kk = 0; kk < 32; ++kk) {
+            float av[4], bv[4];
+            for (int i = 0; i < 4; ++i) av[i] = As[kk][ty * 4 + i];
+            for (int i = 0; i < 4; ++i) bv[i] = Bs[kk][tx * 4 + i];
+            for (int i = 0; i < 4; ++i)
+                for (int q = 0; q < 4; ++q) acc[i][q] = fmaf(av[i], bv[q], acc[i][q]);
+        }
+        __syncthreads();
+    }
+    for (int i = 0; i < 4; ++i) {
+        const int v = v0 + ty * 4 + i;
+        if (v >= m.V) continue;
+        for (int q = 0; q < 4; ++q) {
+            const int n = n0 + tx * 4 + q;
+            if (n < m.dP) P[(static_cast<size_t>(j) * m.V + v) * m.dP + n] = acc[i][q] + m.proj_b[n];
+        }
+    }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+struct qp_handle {
+    int device = 0;
+    int nwg = 0;
+    Model m{};
+    std::vector<void*> allocs;
+    unsigned long long bar_base = 0;
+    uint32_t last_flags = 0;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+qp_status fail(qp_status st, const std::string& msg) {
+    g_last_error = msg;
+    return st;
+}
+
+struct DeviceGuard {
+    int prev = -1;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+        (void)hipSetDevice(dev);
+    }
+    ~DeviceGuard() {
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+};
+
+float half_to_float(uint16_t h) {
+    const uint32_t sign = (h & 0x8000u) << 16;
+    const uint32_t exp = (h >> 10) & 0x1Fu;
+    const uint32_t man = h & 0x3FFu;
+    float f;
+    if (exp == 0) {
+        f = std::ldexp(static_cast<float>(man), -24);  // zero or subnormal
+    } else if (exp == 31) {
+        uint32_t bits = 0x7F800000u | (man << 13);
+        std::memcpy(&f, &bits, 4);
+    } else {
+        uint32_t bits = ((exp + 112u) << 23) | (man << 13);
+        std::memcpy(&f, &bits, 4);
+    }
+    uint32_t b;
+    std::memcpy(&b, &f, 4);
+    b |= sign;
+    std::memcpy(&f, &b, 4);
+    return f;
+}
+
+struct Uploader {
+    qp_handle* h;
+    qp_status st = QP_OK;
+    std::string msg;
+
+    void* alloc(size_t bytes) {
+        if (st != QP_OK) return nullptr;
+        void* p = nullptr;
+        if (bytes == 0) bytes = 4;
+        if (hipMalloc(&p, bytes) != hipSuccess) {
+            st = QP_ERR_OOM;
+            msg = "hipMalloc of " + std::to_string(bytes) + " bytes failed";
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        h->allocs.push_back(p);
+        return p;
+    }
+    void* upload(const void* src, size_t bytes) {
+        void* p = alloc(bytes);
+        if (!p) return nullptr;
+        if (hipMemcpy(p, src, bytes, hipMemcpyHostToDevice) != hipSuccess) {
+            st = QP_ERR_HIP;
+            msg = "hipMemcpy to device failed";
+            return nullptr;
+        }
+        return p;
+    }
+    // Vertically stack matrices [N_i][K] of one storage type into one device
+    // matrix; Q8_0 rows are split into int8 codes and fp32 scales.
+    Mat stack(const std::vector<const void*>& parts, const std::vector<int>& rows, int K, int wt) {
+        Mat out{nullptr, nullptr};
+        size_t N = 0;
+        for (int r : rows) N += static_cast<size_t>(r);
+        if (wt == WT_F32 || wt == WT_BF16) {
+            const size_t esz = wt == WT_F32 ? 4 : 2;
+            std::vector<uint8_t> buf(N * K * esz);
+            size_t off = 0;
+            for (size_t i = 0; i < parts.size(); ++i) {
+                const size_t nb = static_cast<size_t>(rows[i]) * K * esz;
+                std::memcpy(buf.data() + off, parts[i], nb);
+                off += nb;
+            }
+            out.w = upload(buf.data(), buf.size());
+            return out;
+        }
+        const int nb = K / 32;
+        std::vector<int8_t> codes(N * K);
+        std::vector<float> scales(N * nb);
+        size_t row = 0;
+        for (size_t i = 0; i < parts.size(); ++i) {
+            const uint8_t* src = static_cast<const uint8_t*>(parts[i]);
+            for (int r = 0; r < rows[i]; ++r, ++row) {
+                const uint8_t* rp = src + static_cast<size_t>(r) * nb * 34;
+                for (int bk = 0; bk < nb; ++bk) {
+                    const uint8_t* blk = rp + static_cast<size_t>(bk) * 34;
+                    scales[row * nb + bk] = half_to_float(static_cast<uint16_t>(blk[0] | (blk[1] << 8)));
+                    std::memcpy(&codes[row * K + static_cast<size_t>(bk) * 32], blk + 2, 32);
+                }
+            }
+        }
+        out.w = upload(codes.data(), codes.size());
+        out.scale = static_cast<const float*>(upload(scales.data(), scales.size() * 4));
+        return out;
+    }
+    Mat one(const void* p, int N, int K, int wt) { return stack({p}, {N}, K, wt); }
+};
+
+bool check_hip(hipError_t e, const char* what, qp_status* st) {
+    if (e == hipSuccess) return true;
+    *st = fail(QP_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+    return false;
+}
+
+qp_status validate_geometry(const qp_geometry* g) {
+    if (g->n_codebooks != QP_N_CODEBOOKS)
+        return fail(QP_ERR_GEOMETRY, "n_codebooks must be 16");
+    if (g->d_talker <= 0 || g->d_model <= 0 || g->n_layers < 0 || g->n_q_heads <= 0 ||
+        g->n_kv_heads <= 0 || g->head_dim <= 0 || g->d_ffn <= 0 || g->vocab <= 0)
+        return fail(QP_ERR_GEOMETRY, "every dimension must be positive (n_layers >= 0)");
+    if (g->n_layers > 256) return fail(QP_ERR_GEOMETRY, "n_layers above 256");
+    if (g->n_q_heads % g->n_kv_heads != 0)
+        return fail(QP_ERR_GEOMETRY, "n_q_heads must be a multiple of n_kv_heads");
+    if (g->head_dim != 64 && g->head_dim != 128 && g->head_dim != 256)
+        return fail(QP_ERR_GEOMETRY, "head_dim must be 64, 128 or 256");
+    if (!(g->rms_eps > 0.f) || !(g->rope_base > 0.f) || !std::isfinite(g->rope_base))
+        return fail(QP_ERR_GEOMETRY, "rms_eps and rope_base must be positive");
+    if (g->max_batch < 1 || g->max_batch > 65536)
+        return fail(QP_ERR_GEOMETRY, "max_batch must be in [1, 65536]");
+    if (g->weight_dtype < QP_WEIGHT_F32 || g->weight_dtype > QP_WEIGHT_Q8_0)
+        return fail(QP_ERR_DTYPE, "unknown weight_dtype");
+    if (g->emb_format < QP_EMB_F32 || g->emb_format > QP_EMB_EMA)
+        return fail(QP_ERR_DTYPE, "unknown emb_format");
+    const int qd = g->n_q_heads * g->head_dim;
+    const int ins[4] = {g->d_talker, g->d_model, qd, g->d_ffn};
+    const int align = g->weight_dtype == QP_WEIGHT_Q8_0 ? 32 : 8;
+    for (int k : ins) {
+        if (k % align != 0)
+            return fail(QP_ERR_SHAPE, "every input width (dT, dP, nq*hd, F) must be a multiple of " +
+                                          std::to_string(align) + " for this weight dtype");
+        if (k > kLdsFloats) return fail(QP_ERR_SHAPE, "an input width exceeds 16384");
+    }
+    return QP_OK;
+}
+
+qp_status validate_weights(const qp_weights* w, const qp_geometry* g) {
+    if (!w->proj_w || !w->proj_b || !w->out_norm) return fail(QP_ERR_INVALID_ARG, "NULL projection/out_norm");
+    for (int j = 0; j < QP_N_CODEBOOKS; ++j) {
+        if (g->emb_format == QP_EMB_EMA) {
+            if (!w->ema_sum[j] || !w->ema_usage[j]) return fail(QP_ERR_INVALID_ARG, "NULL EMA table");
+        } else if (!w->emb[j]) {
+            return fail(QP_ERR_INVALID_ARG, "NULL codebook table");
+        }
+    }
+    for (int k = 0; k < QP_N_STEPS; ++k)
+        if (!w->lm_head[k]) return fail(QP_ERR_INVALID_ARG, "NULL lm_head");
+    if (g->n_layers > 0 && !w->layers) return fail(QP_ERR_INVALID_ARG, "NULL layers");
+    for (int l = 0; l < g->n_layers; ++l) {
+        const qp_layer_weights& L = w->layers[l];
+        if (!L.attn_norm || !L.wq || !L.wk || !L.wv || !L.wo || !L.q_norm || !L.k_norm || !L.ffn_norm ||
+            !L.w_gate || !L.w_up || !L.w_down)
+            return fail(QP_ERR_INVALID_ARG, "NULL tensor in layer " + std::to_string(l));
+    }
+    return QP_OK;
+}
+
+void free_all(qp_handle* h) {
+    for (void* p : h->allocs) (void)hipFree(p);
+    h->allocs.clear();
+}
+
+}  // namespace
+
+namespace {
+
+template <int WT>
+qp_status launch_frame(qp_handle* h, const RunArgs& a, hipStream_t stream, bool stepwise) {
+    qp_status st = QP_OK;
+    const Model& m = h->m;
+    if (stepwise) {
+        auto go = [&](int ph, int s, int l) {
+            hipLaunchKernelGGL(k_phase<WT>, dim3(h->nwg), dim3(kThreads), 0, stream, m, a, ph, s, l);
+        };
+        go(PH_INIT, 0, 0);
+        for (int s = 1; s <= kSteps; ++s) {
+            for (int l = 0; l < m.L; ++l) {
+                go(PH_QKV, s, l);
+                go(PH_ATTN, s, l);
+                go(PH_OPROJ, s, l);
+                go(PH_UP, s, l);
+                go(PH_DOWN, s, l);
+            }
+            go(PH_LM, s, 0);
+            go(PH_NEXT, s, 0);
+        }
+        if (!check_hip(hipGetLastError(), "phase kernel launch", &st)) return st;
+        return QP_OK;
+    }
+    RunArgs ra = a;
+    ra.bar_base = h->bar_base;
+    Model mm = m;
+    void* args[] = {&mm, &ra};
+    if (!check_hip(hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&k_persistent<WT>), dim3(h->nwg),
+                                              dim3(kThreads), args, 0, stream),
+                   "cooperative launch", &st))
+        return st;
+    h->bar_base += static_cast<unsigned long long>(phases_per_frame(m.L) - 1) * h->nwg;
+    return QP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qp_status_string(int32_t s) {
+    switch (s) {
+        case QP_OK: return "ok";
+        case QP_ERR_INVALID_ARG: return "invalid argument";
+        case QP_ERR_GEOMETRY: return "invalid geometry";
+        case QP_ERR_SHAPE: return "shape not supported by the weight format";
+        case QP_ERR_DTYPE: return "unknown dtype";
+        case QP_ERR_OOM: return "device out of memory";
+        case QP_ERR_HIP: return "HIP runtime error";
+        case QP_ERR_BATCH: return "batch size out of range";
+        case QP_ERR_DEVICE_FLAG: return "device flagged bad input or a barrier timeout";
+        default: return "unknown status";
+    }
+}
+
+const char* qp_last_error(void) { return g_last_error.c_str(); }
+
+qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, qp_handle** out) {
+    if (!out) return fail(QP_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (!w || !g) return fail(QP_ERR_INVALID_ARG, "weights or geometry is NULL");
+    qp_status st = validate_geometry(g);
+    if (st != QP_OK) return st;
+    st = validate_weights(w, g);
+    if (st != QP_OK) return st;
+
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev == 0) {
+        (void)hipGetLastError();
+        return fail(QP_ERR_HIP, "no HIP device");
+    }
+    if (device < 0 || device >= ndev) return fail(QP_ERR_INVALID_ARG, "device index out of range");
+    DeviceGuard guard(device);
+
+    qp_handle* h = new qp_handle();
+    h->device = device;
+    int cus = 0;
+    if (!check_hip(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device),
+                   "hipDeviceGetAttribute", &st)) {
+        delete h;
+        return st;
+    }
+    h->nwg = cus;
+
+    Model& m = h->m;
+    m.dT = g->d_talker;
+    m.dP = g->d_model;
+    m.L = g->n_layers;
+    m.nq = g->n_q_heads;
+    m.nkv = g->n_kv_heads;
+    m.hd = g->head_dim;
+    m.F = g->d_ffn;
+    m.V = g->vocab;
+    m.wt = g->weight_dtype;
+    m.nqkv = (m.nq + 2 * m.nkv) * m.hd;
+    m.max_batch = g->max_batch;
+    m.eps = g->rms_eps;
+    m.attn_scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(m.hd)));
+
+    Uploader up{h};
+    const int wt = m.wt;
+    m.proj = up.one(w->proj_w, m.dP, m.dT, wt);
+    m.proj_b = static_cast<const float*>(up.upload(w->proj_b, sizeof(float) * m.dP));
+    const size_t tab = static_cast<size_t>(m.V) * m.dT;
+    if (g->emb_format == QP_EMB_EMA) {
+        m.emb_bf16 = 0;
+        float* S = static_cast<float*>(up.alloc(tab * 4));
+        float* U = static_cast<float*>(up.alloc(static_cast<size_t>(m.V) * 4));
+        for (int j = 0; j < kCodebooks && up.st == QP_OK; ++j) {
+            float* E = static_cast<float*>(up.alloc(tab * 4));
+            if (up.st != QP_OK) break;
+            if (!check_hip(hipMemcpy(S, w->ema_sum[j], tab * 4, hipMemcpyHostToDevice), "hipMemcpy", &st) ||
+                !check_hip(hipMemcpy(U, w->ema_usage[j], static_cast<size_t>(m.V) * 4, hipMemcpyHostToDevice),
+                           "hipMemcpy", &st)) {
+                up.st = st;
+                break;
+            }
+            hipLaunchKernelGGL(k_ema, dim3(1024), dim3(256), 0, 0, S, U, E, m.V, m.dT);
+            if (!check_hip(hipDeviceSynchronize(), "EMA kernel", &st)) {
+                up.st = st;
+                break;
+            }
+            m.emb[j] = E;
+        }
+    } else {
+        m.emb_bf16 = g->emb_format == QP_EMB_BF16 ? 1 : 0;
+        const size_t esz = m.emb_bf16 ? 2 : 4;
+        for (int j = 0; j < kCodebooks; ++j) m.emb[j] = up.upload(w->emb[j], tab * esz);
+    }
+    std::vector<LayerDev> layers(static_cast<size_t>(m.L));
+    const int kd = m.nkv * m.hd, qd = m.nq * m.hd;
+    for (int l = 0; l < m.L && up.st == QP_OK; ++l) {
+        const qp_layer_weights& lw = w->layers[l];
+        LayerDev& d = layers[l];
+        d.qkv = up.stack({lw.wq, lw.wk, lw.wv}, {qd, kd, kd}, m.dP, wt);
+        d.o = up.one(lw.wo, m.dP, qd, wt);
+        d.gate = up.one(lw.w_gate, m.F, m.dP, wt);
+        d.up = up.one(lw.w_up, m.F, m.dP, wt);
+        d.down = up.one(lw.w_down, m.dP, m.F, wt);
+        d.attn_norm = static_cast<const float*>(up.upload(lw.attn_norm, sizeof(float) * m.dP));
+        d.q_norm = static_cast<const float*>(up.upload(lw.q_norm, sizeof(float) * m.hd));
+        d.k_norm = static_cast<const float*>(up.upload(lw.k_norm, sizeof(float) * m.hd));
+        d.ffn_norm = static_cast<const float*>(up.upload(lw.ffn_norm, sizeof(float) * m.dP));
+    }
+    m.layers = static_cast<const LayerDev*>(up.upload(layers.data(), sizeof(LayerDev) * (layers.empty() ? 1 : layers.size())));
+    m.out_norm = static_cast<const float*>(up.upload(w->out_norm, sizeof(float) * m.dP));
+    for (int k = 0; k < kSteps; ++k) m.lm[k] = up.one(w->lm_head[k], m.V, m.dP, wt);
+
+    // RoPE table, fp64 then rounded: angle(p, i) = p * base^(-2i/hd)
+    const int half = m.hd / 2;
+    std::vector<float> rc(static_cast<size_t>(kPositions) * half), rs(rc.size());
+    for (int p = 0; p < kPositions; ++p)
+        for (int i = 0; i < half; ++i) {
+            const double ang = p * std::pow(static_cast<double>(g->rope_base), -2.0 * i / m.hd);
+            rc[static_cast<size_t>(p) * half + i] = static_cast<float>(std::cos(ang));
+            rs[static_cast<size_t>(p) * half + i] = static_cast<float>(std::sin(ang));
+        }
+    m.rope_cos = static_cast<const float*>(up.upload(rc.data(), rc.size() * 4));
+    m.rope_sin = static_cast<const float*>(up.upload(rs.data(), rs.size() * 4));
+
+    // scratch for max_batch requests
+    const size_t rows = 2 * static_cast<size_t>(m.max_batch);
+    m.x = static_cast<float*>(up.alloc(rows * m.dP * 4));
+    m.qkv = static_cast<float*>(up.alloc(rows * m.nqkv * 4));
+    m.ao = static_cast<float*>(up.alloc(rows * qd * 4));
+    m.hb = static_cast<float*>(up.alloc(rows * m.F * 4));
+    const size_t kvn = static_cast<size_t>(m.L > 0 ? m.L : 1) * m.max_batch * kPositions * kd;
+    m.kc = static_cast<float*>(up.alloc(kvn * 4));
+    m.vc = static_cast<float*>(up.alloc(kvn * 4));
+    m.amax = static_cast<unsigned long long*>(up.alloc(static_cast<size_t>(m.max_batch) * 8));
+    m.err = static_cast<unsigned*>(up.alloc(256));
+    m.bar = static_cast<unsigned long long*>(up.alloc(256));
+    float* ptab = static_cast<float*>(up.alloc(static_cast<size_t>(kSteps) * m.V * m.dP * 4));
+    m.ptab = ptab;
+
+    if (up.st != QP_OK) {
+        st = fail(up.st, up.msg);
+        free_all(h);
+        delete h;
+        return st;
+    }
+    if (!check_hip(hipMemset(m.amax, 0, static_cast<size_t>(m.max_batch) * 8), "hipMemset", &st) ||
+        !check_hip(hipMemset(m.err, 0, 256), "hipMemset", &st) ||
+        !check_hip(hipMemset(m.bar, 0, 256), "hipMemset", &st)) {
+        free_all(h);
+        delete h;
+        return st;
+    }
+    hipLaunchKernelGGL(k_ptab, dim3((m.dP + 63) / 64, (m.V + 63) / 64, kSteps), dim3(256), 0, 0, m, ptab);
+    if (!check_hip(hipGetLastError(), "projected-table kernel launch", &st) ||
+        !check_hip(hipDeviceSynchronize(), "projected-table kernel", &st)) {
+        free_all(h);
+        delete h;
+        return st;
+    }
+    *out = h;
+    return QP_OK;
+}
+
+
+qp_status qp_run_frames_ex(qp_handle* h, int32_t B, const float* H, const int32_t* q0, int32_t* tokens_out,
+                           float* embsum_out, void* stream, const int32_t* force_tokens, float* logits_out,
+                           float* taps_out, uint32_t flags) {
+    if (!h) return fail(QP_ERR_INVALID_ARG, "handle is NULL");
+    if (B < 0 || B > h->m.max_batch)
+        return fail(QP_ERR_BATCH, "B=" + std::to_string(B) + " outside [0, " + std::to_string(h->m.max_batch) + "]");
+    if (flags & ~QP_FLAG_STEPWISE) return fail(QP_ERR_INVALID_ARG, "unknown flag bits");
+    if (B == 0) return QP_OK;
+    if (!H || !q0 || !tokens_out || !embsum_out) return fail(QP_ERR_INVALID_ARG, "NULL input or output pointer");
+    DeviceGuard guard(h->device);
+    RunArgs a{};
+    a.B = B;
+    a.H = H;
+    a.q0 = q0;
+    a.tok_out = tokens_out;
+    a.embsum = embsum_out;
+    a.force = force_tokens;
+    a.logits_out = logits_out;
+    a.taps = taps_out;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool stepwise = (flags & QP_FLAG_STEPWISE) != 0;
+    switch (h->m.wt) {
+        case WT_F32: return launch_frame<WT_F32>(h, a, s, stepwise);
+        case WT_BF16: return launch_frame<WT_BF16>(h, a, s, stepwise);
+        default: return launch_frame<WT_Q8>(h, a, s, stepwise);
+    }
+}
+
+qp_status qp_run_frames(qp_handle* h, int32_t B, const float* H, const int32_t* q0, int32_t* tokens_out,
+                        float* embsum_out, void* stream) {
+    return qp_run_frames_ex(h, B, H, q0, tokens_out, embsum_out, stream, nullptr, nullptr, nullptr, 0u);
+}
+
+qp_status qp_get_error(qp_handle* h) {
+    if (!h) return fail(QP_ERR_INVALID_ARG, "handle is NULL");
+    DeviceGuard guard(h->device);
+    qp_status st = QP_OK;
+    if (!check_hip(hipDeviceSynchronize(), "hipDeviceSynchronize", &st)) return st;
+    unsigned flags = 0;
+    if (!check_hip(hipMemcpy(&flags, h->m.err, 4, hipMemcpyDeviceToHost), "hipMemcpy", &st)) return st;
+    h->last_flags = flags;
+    if (flags == 0) return QP_OK;
+    if (!check_hip(hipMemset(h->m.err, 0, 4), "hipMemset", &st)) return st;
+    if (flags & kErrBarrierTimeout) {
+        // the barrier count is unknown after a timeout: restart it
+        if (!check_hip(hipMemset(h->m.bar, 0, 8), "hipMemset", &st)) return st;
+        h->bar_base = 0;
+    }
+    return fail(QP_ERR_DEVICE_FLAG, "device flags 0x" + std::to_string(flags));
+}
+
+uint32_t qp_last_device_flags(qp_handle* h) { return h ? h->last_flags : 0u; }
+
+void qp_destroy(qp_handle* h) {
+    if (!h) return;
+    {
+        DeviceGuard guard(h->device);
+        (void)hipDeviceSynchronize();
+        free_all(h);
+    }
+    delete h;
+}
+
+}  // extern "C"

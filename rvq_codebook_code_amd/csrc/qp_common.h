@@ -1,0 +1,82 @@
+// Shared device-side definitions of the code-predictor library (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qp {
+
+constexpr int kThreads = 256;            // 4 wave64 per workgroup
+constexpr int kWaves = kThreads / 64;
+constexpr int kCodebooks = 16;
+constexpr int kSteps = kCodebooks - 1;
+constexpr int kPositions = kCodebooks;   // positions 0..15 per frame
+constexpr int kLdsFloats = 16384;        // 64 KiB workgroup scratch
+constexpr int kMaxHeadDim = 256;
+constexpr int kMaxRowsPerChunk = 4;
+
+enum WeightType : int { WT_F32 = 0, WT_BF16 = 1, WT_Q8 = 2 };
+
+// Device error flag bits (also documented in qp.h).
+constexpr unsigned kErrBadQ0 = 1u;
+constexpr unsigned kErrBadForced = 2u;
+constexpr unsigned kErrBarrierTimeout = 4u;
+
+// A linear layer's weights on the device, row-major [N][K]:
+//   WT_F32: float, WT_BF16: uint16 bf16, WT_Q8: int8 codes with one fp32
+//   scale per 32-wide block along K in `scale` [N][K/32].
+struct Mat {
+    const void* w;
+    const float* scale;
+};
+
+struct LayerDev {
+    Mat qkv;          // [(nq+2nkv)*hd][dP]: q rows, then k rows, then v rows
+    Mat o;            // [dP][nq*hd]
+    Mat gate, up;     // [F][dP]
+    Mat down;         // [dP][F]
+    const float* attn_norm;
+    const float* q_norm;
+    const float* k_norm;
+    const float* ffn_norm;
+};
+
+// Everything a launch needs that does not change between calls.
+struct Model {
+    int dT, dP, L, nq, nkv, hd, F, V, wt, emb_bf16, nqkv, max_batch;
+    float eps, attn_scale;
+    Mat proj;
+    const float* proj_b;
+    const void* emb[kCodebooks];   // [V][dT] fp32 or bf16
+    const float* ptab;             // [15][V][dP]: W_p . E_j + b_p, j = 0..14
+    const LayerDev* layers;        // device array [L]
+    const float* out_norm;
+    Mat lm[kSteps];
+    const float* rope_cos;         // [16][hd/2]
+    const float* rope_sin;
+    // scratch (sized for max_batch)
+    float* x;                      // [2*maxB][dP]   residual stream rows
+    float* qkv;                    // [2*maxB][nqkv]
+    float* ao;                     // [2*maxB][nq*hd] attention output
+    float* hb;                     // [2*maxB][F]     SwiGLU activations
+    float* kc;                     // [L][maxB][16][nkv][hd]
+    float* vc;
+    unsigned long long* amax;      // [maxB] packed (logit, index) argmax keys
+    unsigned* err;                 // sticky flag word
+    unsigned long long* bar;       // grid barrier counter
+};
+
+// Per-call arguments.
+struct RunArgs {
+    int B;
+    const float* H;        // [B][dT]
+    const int* q0;         // [B]
+    int* tok_out;          // [B][15]
+    float* embsum;         // [B][dT]
+    const int* force;      // [B][15] or null
+    float* logits_out;     // [B][15][V] or null
+    float* taps;           // [16][L][B][dP] or null
+    unsigned long long bar_base;
+};
+
+}  // namespace qp
