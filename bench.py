@@ -1,0 +1,179 @@
+"""Benchmark of the code-predictor loop on one MI355X.
+
+One step = one frame of the whole hot path (projection, 15 greedy steps of
+the 5-layer predictor with lm_head argmax and embedding accumulation) for all
+B requests of the workload, i.e. one qp_run_frames call.  Inputs are seeded
+synthetic tensors already resident in HBM; weights are seeded synthetic draws
+with the 1.7B predictor's shapes.
+
+Prints one JSON line: frames/s (whole job), the roofline of the frame kernel
+(algorithmic weight bytes per frame-batch over the measured time per launch,
+against 8 TB/s HBM) and the CPU oracle's own rate on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload b1]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from rvq_codebook_code_amd import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+METRIC = "code-predictor frames/sec (15 tokens each) at B=1/16/128; % HBM/MFMA roofline"
+
+
+def bytes_per_weight(dtype: str) -> float:
+    return {"f32": 4.0, "bf16": 2.0, "q8_0": 34.0 / 32.0}[dtype]
+
+
+def algorithmic_bytes(g: synth.Geometry) -> int:
+    """Weights the method must stream per frame-batch: every layer matrix and
+    one lm_head per step (15 steps), plus the projection once per frame.  The
+    gathered embedding rows (B*16 rows) are left out: a lower bound."""
+    qd = g.n_q_heads * g.head_dim
+    nqkv = (g.n_q_heads + 2 * g.n_kv_heads) * g.head_dim
+    per_layer = nqkv * g.d_model + g.d_model * qd + 2 * g.d_ffn * g.d_model + g.d_model * g.d_ffn
+    per_step = g.n_layers * per_layer + g.vocab * g.d_model
+    bpw = bytes_per_weight(g.weight_dtype)
+    return int(round(15 * per_step * bpw + g.d_model * g.d_talker * bpw))
+
+
+def algorithmic_flops(g: synth.Geometry, B: int) -> int:
+    """2 flops per weight per request row (15 steps; the prefill's extra row
+    and attention are left out)."""
+    qd = g.n_q_heads * g.head_dim
+    nqkv = (g.n_q_heads + 2 * g.n_kv_heads) * g.head_dim
+    per_layer = nqkv * g.d_model + g.d_model * qd + 2 * g.d_ffn * g.d_model + g.d_model * g.d_ffn
+    per_step = g.n_layers * per_layer + g.vocab * g.d_model
+    return 2 * B * (15 * per_step + g.d_model * g.d_talker)
+
+
+def cpu_baseline(wl, W, H, q0, budget_s: float):
+    """The oracle as it stands, on the host, for about ``budget_s`` seconds of
+    frames of the same workload."""
+    from oracle import predictor as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    model = O.OracleModel(W, wl.geom)
+    B = H.shape[1]
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        O.run_frames(model, H[n % H.shape[0]], q0[n % H.shape[0]])
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= H.shape[0]:
+            break
+    return {"value": round(n * B / el, 3), "unit": "frames/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n} frame(s) of {B} request(s) of the {wl.name} workload, fp64 NumPy, "
+                      f"{el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="b1", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--stepwise", action="store_true", help="one kernel per phase instead of the persistent kernel")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(requests shard by replication, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from rvq_codebook_code_amd import binding as bd
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS[args.workload]
+    g = wl.geom
+    B = wl.batch
+    W = synth.make_weights(g, wl.weight_seed)
+    H, q0 = synth.make_inputs(g, B, wl.frames, wl.input_seed)
+    pred = bd.Predictor(W, g, max_batch=B)
+    Hd = torch.from_numpy(H).to(dev)
+    qd = torch.from_numpy(q0).to(dev)
+    tok = torch.zeros((B, 15), dtype=torch.int32, device=dev)
+    emb = torch.zeros((B, g.d_talker), dtype=torch.float32, device=dev)
+    F = H.shape[0]
+
+    for i in range(args.warmup):
+        pred.run(Hd[i % F], qd[i % F], tok, emb, stepwise=args.stepwise)
+    torch.cuda.synchronize()
+    if pred.get_error() != 0:
+        raise RuntimeError("device flag raised during warm-up")
+
+    stream = torch.cuda.current_stream(dev)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        pred.run(Hd[i % F], qd[i % F], tok, emb, stepwise=args.stepwise)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end)
+    if pred.get_error() != 0:
+        raise RuntimeError("device flag raised during the timed frames")
+    ms_per_step = ms / args.steps
+    frames_per_s = B * args.steps / (ms / 1e3)
+
+    nbytes = algorithmic_bytes(g)
+    achieved_gbs = nbytes / (ms_per_step / 1e3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, W, H, q0, args.cpu_budget)
+
+    dtype = {"f32": "f32", "bf16": "f32", "q8_0": "f32"}[g.weight_dtype]
+    line = {
+        "metric": METRIC,
+        "value": round(frames_per_s, 2),
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "frames_per_step": 1,
+                   "weights": g.weight_dtype, "embeddings": g.emb_format,
+                   "predictor": f"dP={g.d_model} L={g.n_layers} heads={g.n_q_heads}/{g.n_kv_heads}x{g.head_dim} "
+                                f"F={g.d_ffn} V={g.vocab} dT={g.d_talker}",
+                   "driver": "stepwise" if args.stepwise else "persistent",
+                   "tokens_per_s": round(15 * frames_per_s, 1),
+                   "algorithmic_bytes_per_step": nbytes,
+                   "algorithmic_flops_per_step": algorithmic_flops(g, B)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    pred.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -21,21 +21,43 @@ using namespace qp;
 
 namespace {
 
-__device__ void grid_sync(unsigned long long* ctr, unsigned long long target, unsigned* err) {
-    __threadfence();  // every wave publishes its own stores (agent scope)
+// Grid barrier.  Workgroups arrive on one of 8 group counters (contention is
+// what makes a single counter slow), the last arriver of a group bumps the top
+// counter and the last group publishes the barrier's generation; everybody
+// polls the generation word.  All words are 64-bit and only grow, so no reset
+// is needed between launches: the host passes how many barriers came before.
+// Phase data moves with device-scope loads/stores (ld_act/st_act), so the
+// barrier only has to make this workgroup's stores complete before arriving.
+constexpr int kBarGroups = 8;
+constexpr int kBarStride = 16;  // 128-byte spacing between barrier words
+
+__device__ void grid_sync(unsigned long long* bar, unsigned long long idx, unsigned* err, int wg, int nwg) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's stores are complete
     __syncthreads();
     if (threadIdx.x == 0) {
-        __hip_atomic_fetch_add(ctr, 1ull, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        const int ngroups = nwg < kBarGroups ? nwg : kBarGroups;
+        const int g = wg % ngroups;
+        const unsigned long long gsize = static_cast<unsigned long long>((nwg - g + ngroups - 1) / ngroups);
+        unsigned long long* top = bar + kBarGroups * kBarStride;
+        unsigned long long* gen = top + kBarStride;
+        const unsigned long long old =
+            __hip_atomic_fetch_add(bar + g * kBarStride, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (old == idx * gsize - 1) {
+            const unsigned long long t =
+                __hip_atomic_fetch_add(top, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (t == idx * static_cast<unsigned long long>(ngroups) - 1)
+                __hip_atomic_store(gen, idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         unsigned spins = 0;
-        while (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
-            __builtin_amdgcn_s_sleep(2);
+        while (__hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < idx) {
+            __builtin_amdgcn_s_sleep(1);
             ++spins;
             // bounded wait: a barrier that never completes flags the frame
             // and lets every workgroup run to its end
-            if ((spins & 255u) == 0u) {
+            if ((spins & 1023u) == 0u) {
                 if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kErrBarrierTimeout)
                     break;
-                if (spins > (1u << 22)) {
+                if (spins > (1u << 24)) {
                     atomicOr(err, kErrBarrierTimeout);
                     break;
                 }
@@ -43,18 +65,14 @@ __device__ void grid_sync(unsigned long long* ctr, unsigned long long target, un
         }
     }
     __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
 template <int WT>
 __global__ __launch_bounds__(kThreads) void k_persistent(Model m, RunArgs a) {
     __shared__ float lds[kLdsFloats];
     const int wg = blockIdx.x, nwg = gridDim.x;
-    unsigned long long bi = 0;
-    auto sync = [&]() {
-        ++bi;
-        grid_sync(m.bar, a.bar_base + bi * static_cast<unsigned long long>(nwg), m.err);
-    };
+    unsigned long long bi = a.bar_base;
+    auto sync = [&]() { grid_sync(m.bar, ++bi, m.err, wg, nwg); };
     phase_init<WT>(m, a, lds, wg, nwg);
     for (int s = 1; s <= kSteps; ++s) {
         for (int l = 0; l < m.L; ++l) {
@@ -360,7 +378,7 @@ qp_status launch_frame(qp_handle* h, const RunArgs& a, hipStream_t stream, bool 
                                               dim3(kThreads), args, 0, stream),
                    "cooperative launch", &st))
         return st;
-    h->bar_base += static_cast<unsigned long long>(phases_per_frame(m.L) - 1) * h->nwg;
+    h->bar_base += static_cast<unsigned long long>(phases_per_frame(m.L) - 1);
     return QP_OK;
 }
 
@@ -499,7 +517,7 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
     m.vc = static_cast<float*>(up.alloc(kvn * 4));
     m.amax = static_cast<unsigned long long*>(up.alloc(static_cast<size_t>(m.max_batch) * 8));
     m.err = static_cast<unsigned*>(up.alloc(256));
-    m.bar = static_cast<unsigned long long*>(up.alloc(256));
+    m.bar = static_cast<unsigned long long*>(up.alloc(4096));
     float* ptab = static_cast<float*>(up.alloc(static_cast<size_t>(kSteps) * m.V * m.dP * 4));
     m.ptab = ptab;
 
@@ -511,7 +529,7 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
     }
     if (!check_hip(hipMemset(m.amax, 0, static_cast<size_t>(m.max_batch) * 8), "hipMemset", &st) ||
         !check_hip(hipMemset(m.err, 0, 256), "hipMemset", &st) ||
-        !check_hip(hipMemset(m.bar, 0, 256), "hipMemset", &st)) {
+        !check_hip(hipMemset(m.bar, 0, 4096), "hipMemset", &st)) {
         free_all(h);
         delete h;
         return st;
@@ -573,7 +591,7 @@ qp_status qp_get_error(qp_handle* h) {
     if (!check_hip(hipMemset(h->m.err, 0, 4), "hipMemset", &st)) return st;
     if (flags & kErrBarrierTimeout) {
         // the barrier count is unknown after a timeout: restart it
-        if (!check_hip(hipMemset(h->m.bar, 0, 8), "hipMemset", &st)) return st;
+        if (!check_hip(hipMemset(h->m.bar, 0, 4096), "hipMemset", &st)) return st;
         h->bar_base = 0;
     }
     return fail(QP_ERR_DEVICE_FLAG, "device flags 0x" + std::to_string(flags));

@@ -14,11 +14,22 @@ namespace qp {
 // small helpers
 // ---------------------------------------------------------------------------
 
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_or_zero(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Sum over the 64 lanes with DPP moves (pairs, quads, half rows, rows, then
+// the two row broadcasts); the total lands in lane 63 and is broadcast.  The
+// summation tree is fixed, so every call reduces in the same order.
 __device__ __forceinline__ float wave_sum(float v) {
-    // xor butterfly: every lane ends with the same, order-fixed total
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    v += dpp_or_zero<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+    v += dpp_or_zero<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+    v += dpp_or_zero<0x141, 0xF>(v);  // row_half_mirror
+    v += dpp_or_zero<0x140, 0xF>(v);  // row_mirror
+    v += dpp_or_zero<0x142, 0xA>(v);  // row_bcast15 into rows 1, 3
+    v += dpp_or_zero<0x143, 0xC>(v);  // row_bcast31 into rows 2, 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ float block_sum(float v) {
@@ -31,6 +42,16 @@ __device__ __forceinline__ float block_sum(float v) {
 #pragma unroll
     for (int i = 0; i < kWaves; ++i) t += red[i];
     return t;
+}
+
+// Activations cross workgroups (and XCDs) between phases.  They move with
+// device-scope loads and stores, which bypass the per-XCD L2 copies, so the
+// grid barrier needs no cache writeback or invalidation.
+__device__ __forceinline__ float ld_act(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_act(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
@@ -89,14 +110,18 @@ __device__ __forceinline__ int argmax_index(unsigned long long key) {
 __device__ __forceinline__ void rms_row_to_lds(const float* x, const float* g, int K, float eps,
                                                float* dst) {
     float ss = 0.f;
-    for (int k = threadIdx.x; k < K; k += kThreads) ss += x[k] * x[k];
+    for (int k = threadIdx.x; k < K; k += kThreads) {
+        const float v = ld_act(x + k);
+        dst[k] = v;
+        ss += v * v;
+    }
     ss = block_sum(ss);
     const float rinv = 1.0f / sqrtf(ss / static_cast<float>(K) + eps);
-    for (int k = threadIdx.x; k < K; k += kThreads) dst[k] = g[k] * (x[k] * rinv);
+    for (int k = threadIdx.x; k < K; k += kThreads) dst[k] = g[k] * (dst[k] * rinv);
 }
 
 __device__ __forceinline__ void copy_row_to_lds(const float* x, int K, float* dst) {
-    for (int k = threadIdx.x; k < K; k += kThreads) dst[k] = x[k];
+    for (int k = threadIdx.x; k < K; k += kThreads) dst[k] = ld_act(x + k);
 }
 
 // ---------------------------------------------------------------------------
@@ -110,6 +135,8 @@ __device__ __forceinline__ void copy_row_to_lds(const float* x, int K, float* ds
 template <int WT, bool DUAL, class Pro, class Epi>
 __device__ void linear_phase(const Mat& W, const Mat& W2, int N, int K, int M, Pro pro, Epi epi,
                              float* lds, int wg, int nwg) {
+    constexpr int RB = 4;   // output rows per wave pass
+    constexpr int KC = 2;   // 512-wide k chunks whose loads are in flight together
     const int lane = threadIdx.x & 63;
     const int gw = wg * kWaves + (threadIdx.x >> 6);
     const int nw = nwg * kWaves;
@@ -120,40 +147,67 @@ __device__ void linear_phase(const Mat& W, const Mat& W2, int N, int K, int M, P
         __syncthreads();
         for (int i = 0; i < rc; ++i) pro(r0 + i, lds + i * K);
         __syncthreads();
-        for (int n = gw; n < N; n += nw) {
-            float acc[kMaxRowsPerChunk] = {0.f, 0.f, 0.f, 0.f};
-            float acc2[kMaxRowsPerChunk] = {0.f, 0.f, 0.f, 0.f};
-            for (int k0 = lane * 8; k0 < K; k0 += 512) {
-                float w[8], w2[8];
-                load_w8<WT>(W, K, n, k0, w);
-                if constexpr (DUAL) load_w8<WT>(W2, K, n, k0, w2);
+        for (int nb = gw * RB; nb < N; nb += nw * RB) {
+            float acc[kMaxRowsPerChunk][RB] = {};
+            float acc2[kMaxRowsPerChunk][RB] = {};
+            for (int kb = 0; kb < K; kb += 512 * KC) {
+                float w[RB][KC][8], w2[RB][KC][8];
+                // issue every load of this block before the arithmetic
+#pragma unroll
+                for (int q = 0; q < RB; ++q) {
+#pragma unroll
+                    for (int c = 0; c < KC; ++c) {
+                        const int n = nb + q, k0 = kb + c * 512 + lane * 8;
+                        if (n < N && k0 < K) {
+                            load_w8<WT>(W, K, n, k0, w[q][c]);
+                            if constexpr (DUAL) load_w8<WT>(W2, K, n, k0, w2[q][c]);
+                        } else {
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) { w[q][c][j] = 0.f; w2[q][c][j] = 0.f; }
+                        }
+                    }
+                }
 #pragma unroll
                 for (int i = 0; i < kMaxRowsPerChunk; ++i) {
                     if (i < rc) {
-                        const float* a = lds + i * K + k0;
-                        const float4 a0 = *reinterpret_cast<const float4*>(a);
-                        const float4 a1 = *reinterpret_cast<const float4*>(a + 4);
-                        const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-                        float s = acc[i], s2 = acc2[i];
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            s = fmaf(w[j], av[j], s);
-                            if constexpr (DUAL) s2 = fmaf(w2[j], av[j], s2);
+                        for (int c = 0; c < KC; ++c) {
+                            const int k0 = kb + c * 512 + lane * 8;
+                            if (k0 < K) {
+                                const float* a = lds + i * K + k0;
+                                const float4 a0 = *reinterpret_cast<const float4*>(a);
+                                const float4 a1 = *reinterpret_cast<const float4*>(a + 4);
+                                const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+                                for (int q = 0; q < RB; ++q) {
+                                    float s = acc[i][q], s2 = acc2[i][q];
+#pragma unroll
+                                    for (int j = 0; j < 8; ++j) {
+                                        s = fmaf(w[q][c][j], av[j], s);
+                                        if constexpr (DUAL) s2 = fmaf(w2[q][c][j], av[j], s2);
+                                    }
+                                    acc[i][q] = s;
+                                    acc2[i][q] = s2;
+                                }
+                            }
                         }
-                        acc[i] = s;
-                        acc2[i] = s2;
                     }
                 }
             }
 #pragma unroll
             for (int i = 0; i < kMaxRowsPerChunk; ++i) {
                 if (i < rc) {
-                    acc[i] = wave_sum(acc[i]);
-                    if constexpr (DUAL) acc2[i] = wave_sum(acc2[i]);
+#pragma unroll
+                    for (int q = 0; q < RB; ++q) {
+                        acc[i][q] = wave_sum(acc[i][q]);
+                        if constexpr (DUAL) acc2[i][q] = wave_sum(acc2[i][q]);
+                    }
                 }
             }
             if (lane == 0) {
-                for (int i = 0; i < rc; ++i) epi(r0 + i, n, acc[i], acc2[i]);
+                for (int i = 0; i < rc; ++i)
+                    for (int q = 0; q < RB; ++q)
+                        if (nb + q < N) epi(r0 + i, nb + q, acc[i][q], acc2[i][q]);
             }
         }
     }
@@ -187,21 +241,24 @@ __device__ void phase_init(const Model& m, const RunArgs& a, float* lds, int wg,
                 q = 0;
             }
             tok_s = q;
-            m.amax[b] = 0ull;
+            __hip_atomic_store(m.amax + b, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
         const int q = tok_s;
         const float* prow = m.ptab + static_cast<size_t>(q) * m.dP;
         float* xr = m.x + static_cast<size_t>(B + b) * m.dP;
-        for (int k = threadIdx.x; k < m.dP; k += kThreads) xr[k] = prow[k];
+        for (int k = threadIdx.x; k < m.dP; k += kThreads) st_act(xr + k, prow[k]);
         float* es = a.embsum + static_cast<size_t>(b) * m.dT;
         for (int k = threadIdx.x; k < m.dT; k += kThreads) es[k] = emb_elem(m, 0, q, k);
     }
     const Mat none{nullptr, nullptr};
     linear_phase<WT, false>(
         m.proj, none, m.dP, m.dT, B,
-        [&](int r, float* dst) { copy_row_to_lds(a.H + static_cast<size_t>(r) * m.dT, m.dT, dst); },
-        [&](int r, int n, float v, float) { m.x[static_cast<size_t>(r) * m.dP + n] = v + m.proj_b[n]; },
+        [&](int r, float* dst) {
+            const float* h = a.H + static_cast<size_t>(r) * m.dT;
+            for (int k = threadIdx.x; k < m.dT; k += kThreads) dst[k] = h[k];
+        },
+        [&](int r, int n, float v, float) { st_act(m.x + static_cast<size_t>(r) * m.dP + n, v + m.proj_b[n]); },
         lds, wg, nwg);
 }
 
@@ -215,7 +272,7 @@ __device__ void phase_qkv(const Model& m, const RunArgs& a, int s, int l, float*
         [&](int r, float* dst) {
             rms_row_to_lds(m.x + static_cast<size_t>(r) * m.dP, L.attn_norm, m.dP, m.eps, dst);
         },
-        [&](int r, int n, float v, float) { m.qkv[static_cast<size_t>(r) * m.nqkv + n] = v; },
+        [&](int r, int n, float v, float) { st_act(m.qkv + static_cast<size_t>(r) * m.nqkv + n, v); },
         lds, wg, nwg);
 }
 
@@ -229,7 +286,7 @@ __device__ __forceinline__ void norm_rope_wave(const float* src, const float* ga
     float v[4] = {0.f, 0.f, 0.f, 0.f};
     float ss = 0.f;
     for (int j = 0; j < J; ++j) {
-        v[j] = src[lane + 64 * j];
+        v[j] = ld_act(src + lane + 64 * j);
         ss += v[j] * v[j];
     }
     ss = wave_sum(ss);
@@ -275,8 +332,8 @@ __device__ void phase_attn(const Model& m, const RunArgs& a, int s, int l, float
         for (int idx = threadIdx.x; idx < p_first * hd; idx += kThreads) {
             const int t = idx / hd, d = idx - t * hd;
             const size_t off = kvb + (static_cast<size_t>(t) * nkv + g) * hd + d;
-            Ks[idx] = m.kc[off];
-            Vs[idx] = m.vc[off];
+            Ks[idx] = ld_act(m.kc + off);
+            Vs[idx] = ld_act(m.vc + off);
         }
         for (int pi = 0; pi < npos; ++pi) {
             const int p = p_first + pi;
@@ -289,13 +346,13 @@ __device__ void phase_attn(const Model& m, const RunArgs& a, int s, int l, float
                 for (int j = 0; j < J; ++j) Ks[p * hd + lane + 64 * j] = kr[j];
             } else if (wave == 1) {
                 const float* vr = row + (m.nq + nkv + g) * hd;
-                for (int j = 0; j < J; ++j) Vs[p * hd + lane + 64 * j] = vr[lane + 64 * j];
+                for (int j = 0; j < J; ++j) Vs[p * hd + lane + 64 * j] = ld_act(vr + lane + 64 * j);
             }
             __syncthreads();
             for (int d = threadIdx.x; d < hd; d += kThreads) {
                 const size_t off = kvb + (static_cast<size_t>(p) * nkv + g) * hd + d;
-                m.kc[off] = Ks[p * hd + d];
-                m.vc[off] = Vs[p * hd + d];
+                st_act(m.kc + off, Ks[p * hd + d]);
+                st_act(m.vc + off, Vs[p * hd + d]);
             }
             for (int i = wave; i < grp; i += kWaves) {
                 const int h = g * grp + i;
@@ -330,7 +387,7 @@ __device__ void phase_attn(const Model& m, const RunArgs& a, int s, int l, float
                     }
                 }
                 float* orow = m.ao + static_cast<size_t>(r) * (m.nq * hd) + h * hd;
-                for (int j = 0; j < J; ++j) orow[lane + 64 * j] = o[j];
+                for (int j = 0; j < J; ++j) st_act(orow + lane + 64 * j, o[j]);
             }
         }
     }
@@ -345,7 +402,10 @@ __device__ void phase_oproj(const Model& m, const RunArgs& a, int s, int l, floa
     linear_phase<WT, false>(
         L.o, none, m.dP, K, step_rows(s, a.B),
         [&](int r, float* dst) { copy_row_to_lds(m.ao + static_cast<size_t>(r) * K, K, dst); },
-        [&](int r, int n, float v, float) { m.x[static_cast<size_t>(r) * m.dP + n] += v; },
+        [&](int r, int n, float v, float) {
+            float* xp = m.x + static_cast<size_t>(r) * m.dP + n;
+            st_act(xp, ld_act(xp) + v);
+        },
         lds, wg, nwg);
 }
 
@@ -359,7 +419,7 @@ __device__ void phase_up(const Model& m, const RunArgs& a, int s, int l, float* 
             rms_row_to_lds(m.x + static_cast<size_t>(r) * m.dP, L.ffn_norm, m.dP, m.eps, dst);
         },
         [&](int r, int n, float gv, float uv) {
-            m.hb[static_cast<size_t>(r) * m.F + n] = (gv / (1.0f + expf(-gv))) * uv;
+            st_act(m.hb + static_cast<size_t>(r) * m.F + n, (gv / (1.0f + expf(-gv))) * uv);
         },
         lds, wg, nwg);
 }
@@ -375,8 +435,8 @@ __device__ void phase_down(const Model& m, const RunArgs& a, int s, int l, float
         [&](int r, float* dst) { copy_row_to_lds(m.hb + static_cast<size_t>(r) * m.F, m.F, dst); },
         [&](int r, int n, float v, float) {
             float* xp = m.x + static_cast<size_t>(r) * m.dP + n;
-            const float nv = *xp + v;
-            *xp = nv;
+            const float nv = ld_act(xp) + v;
+            st_act(xp, nv);
             if (a.taps) {
                 const int pos = row_pos(s, B, r), b = row_req(s, B, r);
                 a.taps[((static_cast<size_t>(pos) * m.L + l) * B + b) * m.dP + n] = nv;
@@ -412,8 +472,9 @@ __device__ void phase_next(const Model& m, const RunArgs& a, int s, int wg, int 
     for (int b = wg; b < B; b += nwg) {
         __syncthreads();
         if (threadIdx.x == 0) {
-            const unsigned long long key = m.amax[b];
-            m.amax[b] = 0ull;
+            const unsigned long long key =
+                __hip_atomic_load(m.amax + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(m.amax + b, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             const int tok = argmax_index(key);
             a.tok_out[b * kSteps + (s - 1)] = tok;
             int fed = a.force ? a.force[b * kSteps + (s - 1)] : tok;
@@ -430,7 +491,7 @@ __device__ void phase_next(const Model& m, const RunArgs& a, int s, int wg, int 
         if (s < kSteps) {
             const float* prow = m.ptab + (static_cast<size_t>(s) * m.V + t) * m.dP;
             float* xr = m.x + static_cast<size_t>(b) * m.dP;
-            for (int k = threadIdx.x; k < m.dP; k += kThreads) xr[k] = prow[k];
+            for (int k = threadIdx.x; k < m.dP; k += kThreads) st_act(xr + k, prow[k]);
         }
     }
 }
