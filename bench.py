@@ -88,6 +88,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="b1", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--stepwise", action="store_true", help="one kernel per phase instead of the persistent kernel")
+    ap.add_argument("--generic", action="store_true", help="the generic persistent kernel even where a specialised one exists")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -117,7 +118,7 @@ def main():
     F = H.shape[0]
 
     for i in range(args.warmup):
-        pred.run(Hd[i % F], qd[i % F], tok, emb, stepwise=args.stepwise)
+        pred.run(Hd[i % F], qd[i % F], tok, emb, stepwise=args.stepwise, generic=args.generic)
     torch.cuda.synchronize()
     if pred.get_error() != 0:
         raise RuntimeError("device flag raised during warm-up")
@@ -128,7 +129,7 @@ def main():
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
-        pred.run(Hd[i % F], qd[i % F], tok, emb, stepwise=args.stepwise)
+        pred.run(Hd[i % F], qd[i % F], tok, emb, stepwise=args.stepwise, generic=args.generic)
     t_end.record(stream)
     torch.cuda.synchronize()
     ms = t_start.elapsed_time(t_end)
@@ -164,7 +165,8 @@ def main():
                    "weights": g.weight_dtype, "embeddings": g.emb_format,
                    "predictor": f"dP={g.d_model} L={g.n_layers} heads={g.n_q_heads}/{g.n_kv_heads}x{g.head_dim} "
                                 f"F={g.d_ffn} V={g.vocab} dT={g.d_talker}",
-                   "driver": "stepwise" if args.stepwise else "persistent",
+                   "driver": "stepwise" if args.stepwise else ("generic" if args.generic or B > 2 or g.weight_dtype != "bf16"
+                                                                else "dataflow"),
                    "tokens_per_s": round(15 * frames_per_s, 1),
                    "algorithmic_bytes_per_step": nbytes,
                    "algorithmic_flops_per_step": algorithmic_flops(g, B)},

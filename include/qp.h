@@ -157,6 +157,9 @@ qp_status qp_run_frames(qp_handle* h, int32_t B, const float* H,
 
 /* Execution strategy hints for qp_run_frames_ex `flags`. */
 #define QP_FLAG_STEPWISE 0x1u   /* one kernel per phase (no persistent kernel) */
+#define QP_FLAG_GENERIC 0x2u    /* the generic persistent kernel even where a
+                                   specialised one exists (B <= 2, bf16, the
+                                   1.7B predictor geometry)                   */
 
 /* Same computation with test hooks (any hook may be NULL):
  *   force_tokens int32 [B, 15]  teacher forcing: the token fed back at step

@@ -12,6 +12,7 @@
 #include "qp.h"
 #include "qp_common.h"
 #include "qp_phases.h"
+#include "qp_stream.h"
 
 using namespace qp;
 
@@ -169,6 +170,10 @@ struct qp_handle {
     std::vector<void*> allocs;
     unsigned long long bar_base = 0;
     uint32_t last_flags = 0;
+    // dataflow kernel for small batches of the 1.7B predictor geometry
+    bool stream_ok = false;
+    qp::stream::Recs recs{};
+    uint32_t seq = 0;
 };
 
 namespace {
@@ -348,9 +353,26 @@ void free_all(qp_handle* h) {
 namespace {
 
 template <int WT>
-qp_status launch_frame(qp_handle* h, const RunArgs& a, hipStream_t stream, bool stepwise) {
+qp_status launch_frame(qp_handle* h, const RunArgs& a, hipStream_t stream, bool stepwise, bool generic) {
     qp_status st = QP_OK;
     const Model& m = h->m;
+    if constexpr (WT == WT_BF16) {
+        if (!stepwise && !generic && h->stream_ok && a.B <= 2) {
+            RunArgs ra = a;
+            ra.seq0 = h->seq;
+            Model mm = m;
+            qp::stream::Recs rc = h->recs;
+            void* args[] = {&mm, &ra, &rc};
+            const void* fn = a.B == 1 ? reinterpret_cast<const void*>(&qp::stream::k_stream<2>)
+                                      : reinterpret_cast<const void*>(&qp::stream::k_stream<4>);
+            if (!check_hip(hipLaunchCooperativeKernel(fn, dim3(qp::stream::kNwg), dim3(qp::stream::kThreadsS), args,
+                                                      0, stream),
+                           "cooperative launch (dataflow kernel)", &st))
+                return st;
+            h->seq += static_cast<uint32_t>(qp::stream::phases_per_frame(m.L));
+            return QP_OK;
+        }
+    }
     if (stepwise) {
         auto go = [&](int ph, int s, int l) {
             hipLaunchKernelGGL(k_phase<WT>, dim3(h->nwg), dim3(kThreads), 0, stream, m, a, ph, s, l);
@@ -521,6 +543,29 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
     float* ptab = static_cast<float*>(up.alloc(static_cast<size_t>(kSteps) * m.V * m.dP * 4));
     m.ptab = ptab;
 
+    // records of the dataflow kernel (1.7B geometry, bf16 weights, B <= 2)
+    {
+        namespace S = qp::stream;
+        h->stream_ok = m.dT == S::DT && m.dP == S::DP && m.nq == S::NQ && m.nkv == S::NKV && m.hd == S::HD &&
+                       m.F == S::F && m.V == S::V && wt == WT_BF16 && m.L >= 1 && m.L <= S::kMaxL;
+        if (h->stream_ok) {
+            constexpr int MR = 4;
+            const size_t nrec = static_cast<size_t>(MR) * (S::DP + S::NQKV + S::QD + S::F) + 2ull * S::kGW * 2;
+            uint64_t* r = static_cast<uint64_t*>(up.alloc(nrec * 8));
+            if (r) {
+                h->recs.X = r;
+                h->recs.QKV = h->recs.X + MR * S::DP;
+                h->recs.AO = h->recs.QKV + MR * S::NQKV;
+                h->recs.H = h->recs.AO + MR * S::QD;
+                h->recs.KEY = h->recs.H + MR * S::F;
+                if (hipMemset(r, 0, nrec * 8) != hipSuccess) {
+                    up.st = QP_ERR_HIP;
+                    up.msg = "hipMemset of the record buffers failed";
+                }
+            }
+        }
+    }
+
     if (up.st != QP_OK) {
         st = fail(up.st, up.msg);
         free_all(h);
@@ -552,7 +597,7 @@ qp_status qp_run_frames_ex(qp_handle* h, int32_t B, const float* H, const int32_
     if (!h) return fail(QP_ERR_INVALID_ARG, "handle is NULL");
     if (B < 0 || B > h->m.max_batch)
         return fail(QP_ERR_BATCH, "B=" + std::to_string(B) + " outside [0, " + std::to_string(h->m.max_batch) + "]");
-    if (flags & ~QP_FLAG_STEPWISE) return fail(QP_ERR_INVALID_ARG, "unknown flag bits");
+    if (flags & ~(QP_FLAG_STEPWISE | QP_FLAG_GENERIC)) return fail(QP_ERR_INVALID_ARG, "unknown flag bits");
     if (B == 0) return QP_OK;
     if (!H || !q0 || !tokens_out || !embsum_out) return fail(QP_ERR_INVALID_ARG, "NULL input or output pointer");
     DeviceGuard guard(h->device);
@@ -567,10 +612,11 @@ qp_status qp_run_frames_ex(qp_handle* h, int32_t B, const float* H, const int32_
     a.taps = taps_out;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const bool stepwise = (flags & QP_FLAG_STEPWISE) != 0;
+    const bool generic = (flags & QP_FLAG_GENERIC) != 0;
     switch (h->m.wt) {
-        case WT_F32: return launch_frame<WT_F32>(h, a, s, stepwise);
-        case WT_BF16: return launch_frame<WT_BF16>(h, a, s, stepwise);
-        default: return launch_frame<WT_Q8>(h, a, s, stepwise);
+        case WT_F32: return launch_frame<WT_F32>(h, a, s, stepwise, generic);
+        case WT_BF16: return launch_frame<WT_BF16>(h, a, s, stepwise, generic);
+        default: return launch_frame<WT_Q8>(h, a, s, stepwise, generic);
     }
 }
 

@@ -76,7 +76,8 @@ struct RunArgs {
     const int* force;      // [B][15] or null
     float* logits_out;     // [B][15][V] or null
     float* taps;           // [16][L][B][dP] or null
-    unsigned long long bar_base;
+    unsigned long long bar_base;  // grid barriers completed by earlier launches
+    uint32_t seq0;                // record epochs used by earlier launches
 };
 
 }  // namespace qp

@@ -44,7 +44,7 @@ def workload(name):
     return _cache[name]
 
 
-def gpu_frame(pred, H, q0, force=None, logits=True, taps=False, stepwise=False):
+def gpu_frame(pred, H, q0, force=None, logits=True, taps=False, stepwise=False, generic=False):
     dev = _dev()
     g = pred.geom
     B = H.shape[0]
@@ -56,7 +56,7 @@ def gpu_frame(pred, H, q0, force=None, logits=True, taps=False, stepwise=False):
     lg = torch.full((B, 15, g.vocab), float("nan"), dtype=torch.float32, device=dev) if logits else None
     tp = (torch.full((16, g.n_layers, B, g.d_model), float("nan"), dtype=torch.float32, device=dev)
           if taps else None)
-    pred.run(Ht, qt, tok, emb, force=ft, logits_out=lg, taps_out=tp, stepwise=stepwise)
+    pred.run(Ht, qt, tok, emb, force=ft, logits_out=lg, taps_out=tp, stepwise=stepwise, generic=generic)
     torch.cuda.synchronize()
     assert pred.get_error() == 0
     out = {"tokens": tok.cpu().numpy(), "embsum": emb.cpu().numpy()}
@@ -184,3 +184,33 @@ def test_full_size_sampled(name, frames, rows):
     rows = np.array(rows)
     for f in frames:
         check_against_oracle(name, model, pred, H[f], q0[f], rows)
+
+
+# ----------------------------------------------------------------------------
+# the small-batch dataflow kernel (1.7B geometry, bf16, B <= 2)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B", [1, 2])
+def test_dataflow_kernel_against_oracle_and_generic(B):
+    wl, W, model, pred = workload("b16")
+    H, q0 = synth.make_inputs(wl.geom, B, 3, 4242 + B)
+    rows = np.arange(B)
+    for f in range(3):
+        ref, got = check_against_oracle(f"dataflow B={B}", model, pred, H[f], q0[f], rows)
+        force = ref["tokens"].astype(np.int32)
+        gen = gpu_frame(pred, H[f], q0[f], force=force, generic=True)
+        assert np.abs(gen["logits"] - got["logits"]).max() <= 1e-4
+        assert np.abs(gen["embsum"] - got["embsum"]).max() <= 1e-5
+
+
+def test_dataflow_kernel_taps_and_repeat():
+    wl, W, model, pred = workload("b1")
+    H, q0 = synth.make_inputs(wl.geom, 1, 2, 777)
+    ref = O.run_frames(model, H[0], q0[0], want_taps=True)
+    got = gpu_frame(pred, H[0], q0[0], force=ref["tokens"].astype(np.int32), taps=True)
+    err = np.abs(got["taps"] - ref["taps"]).max()
+    print(f"[dataflow taps] max-abs {err:.3g}")
+    assert err <= 1e-3
+    again = gpu_frame(pred, H[0], q0[0], force=ref["tokens"].astype(np.int32), taps=True)
+    for key in ("tokens", "logits", "embsum", "taps"):
+        np.testing.assert_array_equal(again[key], got[key])
