@@ -550,7 +550,7 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
                        m.F == S::F && m.V == S::V && wt == WT_BF16 && m.L >= 1 && m.L <= S::kMaxL;
         if (h->stream_ok) {
             constexpr int MR = 4;
-            const size_t nrec = static_cast<size_t>(MR) * (S::DP + S::NQKV + S::QD + S::F) + 2ull * S::kGW * 2;
+            const size_t nrec = static_cast<size_t>(MR) * (S::DP + S::NQKV + S::QD + S::F) + 2ull * S::kNwg * 2;
             uint64_t* r = static_cast<uint64_t*>(up.alloc(nrec * 8));
             if (r) {
                 h->recs.X = r;

@@ -1,23 +1,23 @@
 // Dataflow frame kernel for small batches (B <= 2) of the 1.7B-shaped
 // predictor with bf16 weights.
 //
-// One persistent workgroup per CU (256), each with four compute waves and
-// one poller wave, and no grid barrier at all:
+// One persistent workgroup of four waves per CU (256) and no grid barrier:
 //  * every value that crosses workgroups is published as a 64-bit record
 //    (epoch << 32 | fp32 bits) with a device-scope store; the epoch is unique
 //    per phase instance, so a consumer knows a value is current by its tag;
-//  * the poller wave waits for exactly the records its workgroup needs next,
-//    copies them into one of two LDS slots, computes the RMS statistics, and
-//    releases the compute waves with one workgroup barrier per phase;
-//  * the compute waves never wait on remote data, so each phase's weight
-//    loads are issued one phase ahead into registers and land while the
-//    workgroup waits for that phase's inputs (only the poller issues polling
-//    loads, whose completion would otherwise be ordered behind them).
-// Ownership (256 workgroups x 4 compute waves = 1024 waves):
+//  * at the start of a phase the four waves each wait for a quarter of the
+//    records the workgroup needs (16-byte device-scope loads, two records per
+//    lane), stage them in one of two LDS slots and meet at one workgroup
+//    barrier; a single wave cannot pull the inputs fast enough alone;
+//  * each phase's weights are requested at the end of the previous phase,
+//    right after that phase's records were stored (a CU's memory requests
+//    drain roughly in order, so a store issued behind a weight burst would
+//    leave only after the burst), and land while the inputs are awaited.
+// Ownership (256 workgroups x 4 waves = 1024 waves):
 //    q/k/v rows 16*wg + 4*w + {0..3}, O / down / projection row 4*wg + w,
 //    gate/up rows 12*wg + 3*w + {0..2}, lm_head rows 8*wg + 2*w + {0,1},
 //    attention unit (request b, kv head g) on workgroup b*8 + g,
-//    embedding-sum elements 8*wg .. 8*wg+7.
+//    embedding-sum elements 8*wg .. 8*wg+7 (wave 3).
 #pragma once
 
 #include "qp_common.h"
@@ -29,13 +29,13 @@ namespace stream {
 // the Qwen3-TTS 1.7B code-predictor geometry
 constexpr int DT = 2048, DP = 1024, NQ = 16, NKV = 8, HD = 128, F = 3072, V = 2048;
 constexpr int QD = NQ * HD, NQKV = (NQ + 2 * NKV) * HD;
-constexpr int kCW = 4;                   // compute waves
-constexpr int kThreadsS = (kCW + 1) * 64;
+constexpr int kW = 4;                    // waves per workgroup
+constexpr int kThreadsS = kW * 64;
 constexpr int kNwg = 256;
-constexpr int kGW = kNwg * kCW;          // compute waves in the grid
 static_assert(NQKV == 16 * kNwg && DP == 4 * kNwg && F == 12 * kNwg && V == 8 * kNwg && DT == 8 * kNwg,
               "row ownership assumes the 1.7B predictor geometry");
 
+// INIT, then per step 5 phases per layer and the lm_head, then FINAL
 __host__ __device__ constexpr int phases_per_frame(int L) { return 1 + kSteps * (5 * L + 1) + 1; }
 __host__ __device__ constexpr int slot_floats(int MR) { return MR * F; }
 
@@ -44,7 +44,7 @@ struct Recs {
     uint64_t* QKV;  // [MR][NQKV]
     uint64_t* AO;   // [MR][QD]
     uint64_t* H;    // [MR][F]
-    uint64_t* KEY;  // [Bmax][kGW][2]
+    uint64_t* KEY;  // [Bmax][kNwg][2]: ordered logit bits, vocabulary index
 };
 
 __device__ __forceinline__ void st_rec(uint64_t* p, float v, uint32_t tag) {
@@ -55,9 +55,6 @@ __device__ __forceinline__ void st_rec_u(uint64_t* p, uint32_t v, uint32_t tag) 
     const uint64_t u = (static_cast<uint64_t>(tag) << 32) | v;
     __hip_atomic_store(p, u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint64_t ld_rec(const uint64_t* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // frame-relative phase indices
 __device__ __forceinline__ int ph_layer(int L, int s, int l, int t) { return 1 + (s - 1) * (5 * L + 1) + 5 * l + t; }
@@ -67,10 +64,6 @@ enum { T_QKV = 0, T_ATTN = 1, T_O = 2, T_UP = 3, T_DOWN = 4 };
 __device__ __forceinline__ bool timed_out(const unsigned* err) {
     return __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kErrBarrierTimeout;
 }
-
-// ---------------------------------------------------------------------------
-// poller side
-// ---------------------------------------------------------------------------
 
 __device__ __forceinline__ bool spin_wait(unsigned& spins, unsigned* err) {
     __builtin_amdgcn_s_sleep(1);
@@ -84,109 +77,122 @@ __device__ __forceinline__ bool spin_wait(unsigned& spins, unsigned* err) {
     return true;
 }
 
-// Wait for the 64*N records src[0 .. 64N) carrying `tag` and copy their
-// values to dst[0 .. 64N).  Every missing record is re-read each round; all of
-// a round's loads are in flight together.
-template <int N>
-__device__ __forceinline__ void poll_vec(const uint64_t* src, uint32_t tag, float* dst, unsigned* err) {
-    static_assert(N <= 64, "at most 64 records per lane");
-    const int lane = threadIdx.x & 63;
-    uint64_t pend = (N == 64) ? ~0ull : ((1ull << N) - 1ull);
-    const uint64_t* p = src + lane;
-    unsigned spins = 0;
-    while (true) {
-        uint64_t u[N];
-#pragma unroll
-        for (int i = 0; i < N; ++i)
-            if ((pend >> i) & 1ull) u[i] = ld_rec(p + 64 * i);
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            if (((pend >> i) & 1ull) && static_cast<uint32_t>(u[i] >> 32) == tag) {
-                dst[lane + 64 * i] = __uint_as_float(static_cast<uint32_t>(u[i]));
-                pend &= ~(1ull << i);
-            }
-        }
-        if (!__any(pend != 0ull)) break;
-        if (!spin_wait(spins, err)) break;
-    }
+// Weights stream through buffer loads: the matrix base lives in a scalar
+// resource (with the matrix size as its bound), the lane offset in one VGPR,
+// the row offset in an SGPR, so no per-row 64-bit addresses are kept.
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+// A pointer read from LDS is, to the compiler, a per-lane value; every lane
+// holds the same one, so move it to scalar registers.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+    const uint64_t u = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+    return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+__device__ __forceinline__ rsrc_t wrsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0), static_cast<int>(bytes),
+                                             0x00020000);
+}
+// 8 bf16 weights of row `row` (K wide) at k = kc*512 + lane*8
+__device__ __forceinline__ uint4 ldw(rsrc_t r, int row, int K, int kc, uint32_t lane16) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, lane16 + static_cast<uint32_t>(kc) * 1024u,
+                                                         static_cast<uint32_t>(row) * static_cast<uint32_t>(K) * 2u, 0);
+    return make_uint4(static_cast<uint32_t>(v[0]), static_cast<uint32_t>(v[1]), static_cast<uint32_t>(v[2]),
+                      static_cast<uint32_t>(v[3]));
 }
 
-// The four head vectors one attention unit needs from a q/k/v row: q heads
-// 2g and 2g+1, k head g, v head g (HD = 128 each) -> dst[0..512).
-__device__ __forceinline__ void poll_heads(const uint64_t* row, int g, uint32_t tag, float* dst, unsigned* err) {
+// ---------------------------------------------------------------------------
+// waiting for records
+// ---------------------------------------------------------------------------
+
+constexpr int kDeviceScope = 16;  // buffer-load cache policy bit: device-coherent
+
+// This wave's quarter of a row of K tagged records: records
+// [w*K/4, (w+1)*K/4), two per lane per 16-byte load.  Values go to dst[k]
+// (dst = the row's LDS base); returns this wave's part of the row's sum of
+// squares (fixed order).
+template <int K>
+__device__ __forceinline__ float poll_share(const uint64_t* row, int wave, uint32_t tag, float* dst, unsigned* err) {
+    constexpr int NJ = K / 512;  // 16-byte loads per lane
+    static_assert(NJ >= 1 && NJ <= 16, "row width");
     const int lane = threadIdx.x & 63;
-    const int col[4] = {(2 * g) * HD, (2 * g + 1) * HD, (NQ + g) * HD, (NQ + NKV + g) * HD};
-    uint32_t pend = 0xFFu;
+    const rsrc_t r = wrsrc(row + wave * (K / 4), (K / 4) * 8);
+    float* d = dst + wave * (K / 4);
+    uint32_t pend = (1u << NJ) - 1u;
+    float v[2 * NJ];
     unsigned spins = 0;
     while (true) {
-        uint64_t u[8];
+        decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0u, 0u, 0)) u[NJ];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if ((pend >> j) & 1u) u[j] = ld_rec(row + col[j >> 1] + lane + 64 * (j & 1));
+        for (int j = 0; j < NJ; ++j)
+            if ((pend >> j) & 1u) u[j] = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16u, 1024u * j, kDeviceScope);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (((pend >> j) & 1u) && static_cast<uint32_t>(u[j] >> 32) == tag) {
-                dst[(j >> 1) * HD + lane + 64 * (j & 1)] = __uint_as_float(static_cast<uint32_t>(u[j]));
+        for (int j = 0; j < NJ; ++j) {
+            if (((pend >> j) & 1u) && static_cast<uint32_t>(u[j][1]) == tag && static_cast<uint32_t>(u[j][3]) == tag) {
+                v[2 * j] = __int_as_float(u[j][0]);
+                v[2 * j + 1] = __int_as_float(u[j][2]);
                 pend &= ~(1u << j);
             }
         }
         if (!__any(pend != 0u)) break;
         if (!spin_wait(spins, err)) break;
     }
-}
-
-// 64 consecutive fp32 values (device-coherent) straight into LDS, one per
-// lane, without passing through registers: src and dst are wave-uniform.
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef const __attribute__((address_space(1))) void gbl_void_t;
-__device__ __forceinline__ void dma64(const float* src, float* dst) {
-    const int lane = threadIdx.x & 63;
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)(src + lane), (lds_void_t*)(dst), 4, 0,
-                                     16 /* device scope */);
-}
-
-// Sum of squares of n LDS values, fixed order, lane-uniform result.
-__device__ __forceinline__ float lds_sumsq(const float* x, int n) {
-    const int lane = threadIdx.x & 63;
-    float t = 0.f;
-    for (int k = lane; k < n; k += 64) t = fmaf(x[k], x[k], t);
-    return wave_sum(t);
-}
-
-// Global argmax over the per-wave key records of every request: returns the
-// token of request `b` in lane-uniform form.  Records: [b][gw][0] = ordered
-// logit bits, [b][gw][1] = vocabulary index, both tagged.
-__device__ int poll_argmax(const uint64_t* key, int b, uint32_t tag, unsigned* err) {
-    const int lane = threadIdx.x & 63;
-    uint64_t best = 0;
-    // 2*kGW records per request; poll them 64*32 at a time
-    const uint64_t* src = key + static_cast<size_t>(b) * kGW * 2;
-    constexpr int PER = 32;
-    for (int f0 = 0; f0 < 2 * kGW; f0 += 64 * PER) {
-        uint32_t val[PER];
-        uint32_t pending = 0xFFFFFFFFu;
-        unsigned spins = 0;
-        while (true) {
-            uint64_t u[PER];
+    float ss = 0.f;
 #pragma unroll
-            for (int i = 0; i < PER; ++i)
-                if (pending & (1u << i)) u[i] = ld_rec(src + f0 + 2 * lane + 128 * (i >> 1) + (i & 1));
+    for (int j = 0; j < NJ; ++j) {
+        *reinterpret_cast<float2*>(d + 2 * (lane + 64 * j)) = make_float2(v[2 * j], v[2 * j + 1]);
+        ss = fmaf(v[2 * j], v[2 * j], ss);
+        ss = fmaf(v[2 * j + 1], v[2 * j + 1], ss);
+    }
+    return wave_sum(ss);
+}
+
+// One head vector (HD = 128 tagged records) -> dst[0..128).
+__device__ __forceinline__ void poll_head(const uint64_t* src, uint32_t tag, float* dst, unsigned* err) {
+    const int lane = threadIdx.x & 63;
+    const rsrc_t r = wrsrc(src, HD * 8);
+    unsigned spins = 0;
+    while (true) {
+        const auto u = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16u, 0u, kDeviceScope);
+        const bool ok = static_cast<uint32_t>(u[1]) == tag && static_cast<uint32_t>(u[3]) == tag;
+        if (__all(ok)) {
+            *reinterpret_cast<float2*>(dst + 2 * lane) = make_float2(__int_as_float(u[0]), __int_as_float(u[2]));
+            break;
+        }
+        if (!spin_wait(spins, err)) break;
+    }
+}
+
+// Token of request b from the per-workgroup key records of one lm_head phase
+// (largest logit, lowest index on ties); lane-uniform.
+__device__ __forceinline__ int poll_argmax(const uint64_t* key, int b, uint32_t tag, unsigned* err) {
+    const int lane = threadIdx.x & 63;
+    constexpr int NJ = kNwg / 64;
+    const rsrc_t r = wrsrc(key + static_cast<size_t>(b) * kNwg * 2, kNwg * 16);
+    uint32_t ord[NJ], idx[NJ];
+    uint32_t pend = (1u << NJ) - 1u;
+    unsigned spins = 0;
+    while (true) {
+        decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0u, 0u, 0)) u[NJ];
 #pragma unroll
-            for (int i = 0; i < PER; ++i) {
-                if ((pending & (1u << i)) && static_cast<uint32_t>(u[i] >> 32) == tag) {
-                    val[i] = static_cast<uint32_t>(u[i]);
-                    pending &= ~(1u << i);
-                }
+        for (int j = 0; j < NJ; ++j)
+            if ((pend >> j) & 1u) u[j] = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16u, 1024u * j, kDeviceScope);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            if (((pend >> j) & 1u) && static_cast<uint32_t>(u[j][1]) == tag && static_cast<uint32_t>(u[j][3]) == tag) {
+                ord[j] = static_cast<uint32_t>(u[j][0]);
+                idx[j] = static_cast<uint32_t>(u[j][2]);
+                pend &= ~(1u << j);
             }
-            if (!__any(pending != 0u)) break;
-            if (!spin_wait(spins, err)) break;
         }
+        if (!__any(pend != 0u)) break;
+        if (!spin_wait(spins, err)) break;
+    }
+    uint64_t best = 0;
 #pragma unroll
-        for (int i = 0; i < PER; i += 2) {
-            // larger logit first, lower index on ties
-            const uint64_t k = (static_cast<uint64_t>(val[i]) << 32) | (0xFFFFFFFFu - val[i + 1]);
-            best = k > best ? k : best;
-        }
+    for (int j = 0; j < NJ; ++j) {
+        const uint64_t k = (static_cast<uint64_t>(ord[j]) << 32) | (0xFFFFFFFFu - idx[j]);
+        best = k > best ? k : best;
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
@@ -195,6 +201,15 @@ __device__ int poll_argmax(const uint64_t* key, int b, uint32_t tag, unsigned* e
         best = o > best ? o : best;
     }
     return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(best & 0xFFFFFFFFu));
+}
+
+// 64 consecutive fp32 values (device-coherent) straight into LDS, one per
+// lane, without passing through registers: src and dst are wave-uniform.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef const __attribute__((address_space(1))) void gbl_void_t;
+__device__ __forceinline__ void dma64(const float* src, float* dst) {
+    const int lane = threadIdx.x & 63;
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)(src + lane), (lds_void_t*)(dst), 4, 0, kDeviceScope);
 }
 
 // ---------------------------------------------------------------------------
@@ -211,22 +226,6 @@ __device__ __forceinline__ float dot8(const uint4 w, const float a[8], float acc
     acc = fmaf(__uint_as_float(w.w << 16), a[6], acc);
     acc = fmaf(__uint_as_float(w.w & 0xFFFF0000u), a[7], acc);
     return acc;
-}
-
-// Weights stream through buffer loads: the matrix base lives in a scalar
-// resource (with the matrix size as its bound), the lane offset in one VGPR,
-// the row offset in an SGPR, so no per-row 64-bit addresses are kept.
-using rsrc_t = __amdgpu_buffer_rsrc_t;
-__device__ __forceinline__ rsrc_t wrsrc(const void* p, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0), static_cast<int>(bytes),
-                                             0x00020000);
-}
-// 8 bf16 weights of row `row` (K wide) at k = kc*512 + lane*8
-__device__ __forceinline__ uint4 ldw(rsrc_t r, int row, int K, int kc, uint32_t lane16) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, lane16 + static_cast<uint32_t>(kc) * 1024u,
-                                                         static_cast<uint32_t>(row) * static_cast<uint32_t>(K) * 2u, 0);
-    return make_uint4(static_cast<uint32_t>(v[0]), static_cast<uint32_t>(v[1]), static_cast<uint32_t>(v[2]),
-                      static_cast<uint32_t>(v[3]));
 }
 
 __device__ __forceinline__ void lds8(const float* p, float a[8]) {
@@ -266,192 +265,68 @@ constexpr int kGainFloats = (2 * kMaxL + 1) * DP + 2 * kMaxL * HD;
 
 template <int MR>
 __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs rc) {
+    constexpr int BM = MR / 2;  // requests
     constexpr int SLOT = slot_floats(MR);
     __shared__ float slot[2][SLOT];
-    __shared__ float ssq[2][MR];
+    __shared__ float ssp[2][kW][MR];          // per-wave partial sums of squares
+    __shared__ uint64_t lmk[kW][BM];          // per-wave lm_head keys
     __shared__ float rope_s[2][kPositions * (HD / 2)];
     __shared__ float gains[kGainFloats];
     __shared__ LayerDev lay_s[kMaxL];
+
     const int wg = blockIdx.x;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int lane = threadIdx.x & 63;
     const int B = a.B;
     const int L = m.L;
     const uint32_t seq0 = a.seq0;
     auto tag_of = [&](int ph) { return seq0 + static_cast<uint32_t>(ph) + 1u; };
     const float eps = m.eps;
-    // the layer table lives in device memory; read it once into LDS so that
-    // no phase waits on a pointer load
+    unsigned* err = m.err;
+
+    // ---- tables into LDS: layer pointers, norm gains, RoPE
     if (threadIdx.x < L) lay_s[threadIdx.x] = m.layers[threadIdx.x];
     __syncthreads();
     const LayerDev* LD = lay_s;
+    for (int i = threadIdx.x; i < kPositions * (HD / 2); i += kThreadsS) {
+        rope_s[0][i] = m.rope_cos[i];
+        rope_s[1][i] = m.rope_sin[i];
+    }
+    for (int l = 0; l < L; ++l)
+        for (int i = threadIdx.x; i < DP; i += kThreadsS) {
+            gains[(2 * l) * DP + i] = LD[l].attn_norm[i];
+            gains[(2 * l + 1) * DP + i] = LD[l].ffn_norm[i];
+        }
+    for (int i = threadIdx.x; i < DP; i += kThreadsS) gains[2 * kMaxL * DP + i] = m.out_norm[i];
+    for (int l = 0; l < L; ++l)
+        for (int i = threadIdx.x; i < HD; i += kThreadsS) {
+            gains[(2 * kMaxL + 1) * DP + (2 * l) * HD + i] = LD[l].q_norm[i];
+            gains[(2 * kMaxL + 1) * DP + (2 * l + 1) * HD + i] = LD[l].k_norm[i];
+        }
     auto g_attn = [&](int l) { return gains + (2 * l) * DP; };
     auto g_ffn = [&](int l) { return gains + (2 * l + 1) * DP; };
     const float* g_out = gains + 2 * kMaxL * DP;
     auto g_q = [&](int l) { return gains + (2 * kMaxL + 1) * DP + (2 * l) * HD; };
     auto g_k = [&](int l) { return gains + (2 * kMaxL + 1) * DP + (2 * l + 1) * HD; };
 
-    if (wave == kCW) {
-        // ======================= poller wave =======================
-        int fed[2] = {0, 0};
-        float es = 0.f;  // embedding-sum element: request lane/8, column 8*wg + lane%8
-        const int eb = lane >> 3, ek = 8 * wg + (lane & 7);
-        // INIT: H rows, q0
-        for (int b = 0; b < B; ++b) {
-            int q = a.q0[b];
-            if (q < 0 || q >= V) {
-                if (lane == 0 && wg == 0) atomicOr(m.err, kErrBadQ0);
-                q = 0;
-            }
-            fed[b] = q;
-            const float4* hr = reinterpret_cast<const float4*>(a.H + static_cast<size_t>(b) * DT);
-            for (int k = lane; k < DT / 4; k += 64) reinterpret_cast<float4*>(slot[0] + b * DT)[k] = hr[k];
-        }
-        if (eb < B) es = emb_elem(m, 0, fed[eb], ek);
-        __syncthreads();
-        int ph = 1;
-        auto decide = [&](int s_prev) {
-            // tokens of step s_prev from the key records; returns via fed[]
-            const uint32_t lt = tag_of(ph_lm(L, s_prev));
-            for (int b = 0; b < B; ++b) {
-                const int tok = poll_argmax(rc.KEY, b, lt, m.err);
-                if (wg == 0 && lane == 0) a.tok_out[b * kSteps + (s_prev - 1)] = tok;
-                int f = a.force ? a.force[b * kSteps + (s_prev - 1)] : tok;
-                if (f < 0 || f >= V) {
-                    if (wg == 0 && lane == 0) atomicOr(m.err, kErrBadForced);
-                    f = 0;
-                }
-                fed[b] = f;
-            }
-        };
-        for (int s = 1; s <= kSteps; ++s) {
-            const int M = (s == 1) ? 2 * B : B;
-            for (int l = 0; l < L; ++l) {
-                // ---- QKV(l): x rows
-                {
-                    float* dst = slot[ph & 1];
-                    if (l == 0) {
-                        if (s == 1) {
-                            for (int b = 0; b < B; ++b) poll_vec<DP / 64>(rc.X + b * DP, tag_of(0), dst + b * DP, m.err);
-                        } else {
-                            decide(s - 1);
-                            if (eb < B) es += emb_elem(m, s - 1, fed[eb], ek);
-                        }
-                        const int r0 = (s == 1) ? B : 0;
-                        for (int b = 0; b < B; ++b) {
-                            const float4* prow =
-                                reinterpret_cast<const float4*>(m.ptab + (static_cast<size_t>(s - 1) * V + fed[b]) * DP);
-                            float4* d4 = reinterpret_cast<float4*>(dst + (r0 + b) * DP);
-#pragma unroll
-                            for (int i = 0; i < DP / 256; ++i) d4[lane + 64 * i] = prow[lane + 64 * i];
-                        }
-                    } else {
-                        const uint32_t t = tag_of(ph_layer(L, s, l - 1, T_DOWN));
-                        for (int r = 0; r < M; ++r) poll_vec<DP / 64>(rc.X + r * DP, t, dst + r * DP, m.err);
-                    }
-                    for (int r = 0; r < M; ++r) {
-                        const float t = lds_sumsq(dst + r * DP, DP);
-                        if (lane == 0) ssq[ph & 1][r] = t;
-                    }
-                    __syncthreads();
-                    ++ph;
-                }
-                // ---- ATTN(l): q/k/v head vectors of the unit + cached keys/values
-                {
-                    float* dst = slot[ph & 1];
-                    if (wg < B * NKV) {
-                        const int b = wg / NKV, g = wg % NKV;
-                        const int pf = (s == 1) ? 0 : s;
-                        const size_t kvb = ((static_cast<size_t>(l) * m.max_batch + b) * kPositions) * NKV * HD;
-                        // cached keys/values of earlier positions: LDS-direct loads,
-                        // all in flight while the new head vectors are polled
-                        for (int t = 0; t < pf; ++t) {
-                            const size_t off = kvb + (static_cast<size_t>(t) * NKV + g) * HD;
-                            dma64(m.kc + off, dst + t * HD);
-                            dma64(m.kc + off + 64, dst + t * HD + 64);
-                            dma64(m.vc + off, dst + 2048 + t * HD);
-                            dma64(m.vc + off + 64, dst + 2048 + t * HD + 64);
-                        }
-                        const uint32_t qt = tag_of(ph_layer(L, s, l, T_QKV));
-                        poll_heads(rc.QKV + static_cast<size_t>(b) * NQKV, g, qt, dst + 4096, m.err);
-                        if (s == 1) poll_heads(rc.QKV + static_cast<size_t>(B + b) * NQKV, g, qt, dst + 4096 + 512, m.err);
-                        __builtin_amdgcn_s_waitcnt(0);
-                    }
-                    __syncthreads();
-                    ++ph;
-                }
-                // ---- O(l): attention output rows
-                {
-                    const uint32_t t = tag_of(ph_layer(L, s, l, T_ATTN));
-                    for (int r = 0; r < M; ++r) poll_vec<QD / 64>(rc.AO + r * QD, t, slot[ph & 1] + r * QD, m.err);
-                    __syncthreads();
-                    ++ph;
-                }
-                // ---- UP(l): x rows after the attention residual
-                {
-                    const uint32_t t = tag_of(ph_layer(L, s, l, T_O));
-                    float* dst = slot[ph & 1];
-                    for (int r = 0; r < M; ++r) poll_vec<DP / 64>(rc.X + r * DP, t, dst + r * DP, m.err);
-                    for (int r = 0; r < M; ++r) {
-                        const float q = lds_sumsq(dst + r * DP, DP);
-                        if (lane == 0) ssq[ph & 1][r] = q;
-                    }
-                    __syncthreads();
-                    ++ph;
-                }
-                // ---- DOWN(l): SwiGLU rows
-                {
-                    const uint32_t t = tag_of(ph_layer(L, s, l, T_UP));
-                    for (int r = 0; r < M; ++r) poll_vec<F / 64>(rc.H + r * F, t, slot[ph & 1] + r * F, m.err);
-                    __syncthreads();
-                    ++ph;
-                }
-            }
-            // ---- LM(s): the rows at position s
-            {
-                const int r0 = (s == 1) ? B : 0;
-                const uint32_t t = tag_of(ph_layer(L, s, L - 1, T_DOWN));
-                float* dst = slot[ph & 1];
-                for (int b = 0; b < B; ++b) poll_vec<DP / 64>(rc.X + (r0 + b) * DP, t, dst + b * DP, m.err);
-                for (int b = 0; b < B; ++b) {
-                    const float q = lds_sumsq(dst + b * DP, DP);
-                    if (lane == 0) ssq[ph & 1][b] = q;
-                }
-                __syncthreads();
-                ++ph;
-            }
-        }
-        // ---- FINAL: last token, embedding sum out
-        decide(kSteps);
-        if (eb < B) {
-            es += emb_elem(m, kSteps, fed[eb], ek);
-            a.embsum[static_cast<size_t>(eb) * DT + ek] = es;
-        }
-        return;
-    }
-
-    // ======================= compute waves =======================
-    const int gw = wg * kCW + wave;
-    const int ctid = threadIdx.x;  // 0 .. 255 over the compute waves
-    uint4 wP[4], wQ[8], wO[4], wU[12], wD[6], wL[4];
-    float xr[MR];
-
+    // ---- weights in registers, one phase ahead
     const uint32_t lane16 = static_cast<uint32_t>(lane) * 16u;
+    uint4 wP[4], wQ[8], wO[4], wU[12], wD[6], wL[4];
     auto load_wQ = [&](int l) {
-        const rsrc_t W = wrsrc(LD[l].qkv.w, NQKV * DP * 2);
+        const rsrc_t W = wrsrc(uniform_ptr(LD[l].qkv.w), NQKV * DP * 2);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
             for (int c = 0; c < 2; ++c) wQ[q * 2 + c] = ldw(W, 16 * wg + 4 * wave + q, DP, c, lane16);
     };
     auto load_wO = [&](int l) {
-        const rsrc_t W = wrsrc(LD[l].o.w, DP * QD * 2);
+        const rsrc_t W = wrsrc(uniform_ptr(LD[l].o.w), DP * QD * 2);
 #pragma unroll
         for (int c = 0; c < 4; ++c) wO[c] = ldw(W, 4 * wg + wave, QD, c, lane16);
     };
     auto load_wU = [&](int l) {
-        const rsrc_t Wg = wrsrc(LD[l].gate.w, F * DP * 2);
-        const rsrc_t Wu = wrsrc(LD[l].up.w, F * DP * 2);
+        const rsrc_t Wg = wrsrc(uniform_ptr(LD[l].gate.w), F * DP * 2);
+        const rsrc_t Wu = wrsrc(uniform_ptr(LD[l].up.w), F * DP * 2);
 #pragma unroll
         for (int q = 0; q < 3; ++q)
 #pragma unroll
@@ -461,7 +336,7 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
             }
     };
     auto load_wD = [&](int l) {
-        const rsrc_t W = wrsrc(LD[l].down.w, DP * F * 2);
+        const rsrc_t W = wrsrc(uniform_ptr(LD[l].down.w), DP * F * 2);
 #pragma unroll
         for (int c = 0; c < 6; ++c) wD[c] = ldw(W, 4 * wg + wave, F, c, lane16);
     };
@@ -472,14 +347,14 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
 #pragma unroll
             for (int c = 0; c < 2; ++c) wL[q * 2 + c] = ldw(W, 8 * wg + 2 * wave + q, DP, c, lane16);
     };
-    // select vals[t] for a lane-dependent t (vals is a small register array)
-    auto pick = [&](const float* vals, int count, int t) {
-        float v = 0.f;
+    {
+        const rsrc_t W = wrsrc(m.proj.w, DP * DT * 2);
 #pragma unroll
-        for (int i = 0; i < 4 * MR; ++i)
-            if (i < count && i == t) v = vals[i];
-        return v;
-    };
+        for (int c = 0; c < 4; ++c) wP[c] = ldw(W, 4 * wg + wave, DT, c, lane16);
+    }
+    load_wQ(0);
+    sched_fence();
+
     // gain-weighted activations for k = c*512 + lane*8 .. +7
     auto act8 = [&](const float* xrow, const float* g, int c, float x8[8]) {
         float g8[8];
@@ -488,360 +363,413 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
 #pragma unroll
         for (int j = 0; j < 8; ++j) x8[j] *= g8[j];
     };
+    // sum of squares of LDS row r after the barrier: fixed order over waves
+    auto row_ss = [&](int par, int r) { return ((ssp[par][0][r] + ssp[par][1][r]) + ssp[par][2][r]) + ssp[par][3][r]; };
+    // x rows of the next phase: each wave waits for its quarter
+    auto gather_x = [&](const uint64_t* base, int nrows, uint32_t tg, int par) {
+        for (int r = 0; r < nrows; ++r) {
+            const float q = poll_share<DP>(base + static_cast<size_t>(r) * DP, wave, tg, slot[par] + r * DP, err);
+            if (lane == 0) ssp[par][wave][r] = q;
+        }
+    };
 
-    // kernel start: weights of the first two phases in flight, then the RoPE
-    // and norm-gain tables into LDS
-    {
-        const rsrc_t W = wrsrc(m.proj.w, DP * DT * 2);
+    // decide the tokens of step sp from the key records; all waves do it
+    int fed[BM];
+    auto decide = [&](int sp, int ph_lm_idx) {
+        const uint32_t lt = tag_of(ph_lm_idx);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) wP[c] = ldw(W, 4 * wg + wave, DT, c, lane16);
-    }
-    load_wQ(0);
-    sched_fence();
-    for (int i = ctid; i < kPositions * (HD / 2); i += kCW * 64) {
-        rope_s[0][i] = m.rope_cos[i];
-        rope_s[1][i] = m.rope_sin[i];
-    }
-    for (int l = 0; l < L; ++l)
-        for (int i = ctid; i < DP; i += kCW * 64) {
-            gains[(2 * l) * DP + i] = LD[l].attn_norm[i];
-            gains[(2 * l + 1) * DP + i] = LD[l].ffn_norm[i];
+        for (int b = 0; b < BM; ++b) {
+            if (b < B) {
+                const int tok = poll_argmax(rc.KEY, b, lt, err);
+                if (wg == 0 && wave == 0 && lane == 0) a.tok_out[b * kSteps + (sp - 1)] = tok;
+                int f = a.force ? a.force[b * kSteps + (sp - 1)] : tok;
+                if (f < 0 || f >= V) {
+                    if (wg == 0 && wave == 0 && lane == 0) atomicOr(err, kErrBadForced);
+                    f = 0;
+                }
+                fed[b] = f;
+            }
         }
-    for (int i = ctid; i < DP; i += kCW * 64) gains[2 * kMaxL * DP + i] = m.out_norm[i];
-    for (int l = 0; l < L; ++l)
-        for (int i = ctid; i < HD; i += kCW * 64) {
-            gains[(2 * kMaxL + 1) * DP + (2 * l) * HD + i] = LD[l].q_norm[i];
-            gains[(2 * kMaxL + 1) * DP + (2 * l + 1) * HD + i] = LD[l].k_norm[i];
-        }
+    };
 
-    // ---- INIT: x rows at position 0 = W_p . H + b_p
+    // ---- INIT: q0, embedding sum start, H rows
+    float es = 0.f;  // wave 3: embedding-sum element (request lane/8, column 8*wg + lane%8)
+    const int eb = lane >> 3, ek = 8 * wg + (lane & 7);
+#pragma unroll
+    for (int b = 0; b < BM; ++b) {
+        if (b < B) {
+            int q = a.q0[b];
+            if (q < 0 || q >= V) {
+                if (wg == 0 && wave == 0 && lane == 0) atomicOr(err, kErrBadQ0);
+                q = 0;
+            }
+            fed[b] = q;
+            const float4* hr = reinterpret_cast<const float4*>(a.H + static_cast<size_t>(b) * DT) + wave * (DT / 16);
+            float4* d4 = reinterpret_cast<float4*>(slot[0] + b * DT) + wave * (DT / 16);
+#pragma unroll
+            for (int i = 0; i < DT / 1024; ++i) d4[lane + 64 * i] = hr[lane + 64 * i];
+        }
+    }
+    if (wave == 3 && eb < B) {
+        int fb = fed[0];
+#pragma unroll
+        for (int b = 1; b < BM; ++b)
+            if (b == eb) fb = fed[b];
+        es = emb_elem(m, 0, fb, ek);
+    }
     __syncthreads();
-    int ph = 0;
     {
         const float* Hs = slot[0];
-        float acc[MR / 2];
-#pragma unroll
-        for (int r = 0; r < MR / 2; ++r) acc[r] = 0.f;
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-            for (int r = 0; r < MR / 2; ++r) {
-                if (r < B) {
-                    float x8[8];
-                    lds8(Hs + r * DT + c * 512 + lane * 8, x8);
-                    acc[r] = dot8(wP[c], x8, acc[r]);
-                }
-            }
         const int n = 4 * wg + wave;
         const float bias = m.proj_b[n];
 #pragma unroll
-        for (int r = 0; r < MR / 2; ++r) {
+        for (int r = 0; r < BM; ++r) {
             if (r < B) {
-                const float v = wave_sum(acc[r]) + bias;
-                if (lane == r) st_rec(rc.X + static_cast<size_t>(r) * DP + n, v, tag_of(0));
+                float acc = 0.f;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    float x8[8];
+                    lds8(Hs + r * DT + c * 512 + lane * 8, x8);
+                    acc = dot8(wP[c], x8, acc);
+                }
+                const float v = wave_sum(acc) + bias;
+                if (lane == 0) st_rec(rc.X + static_cast<size_t>(r) * DP + n, v, tag_of(0));
             }
         }
     }
-    ph = 1;
 
+    float xr[MR];  // this wave's residual-stream element (column 4*wg + wave) per row
+    int ph = 1;
     for (int s = 1; s <= kSteps; ++s) {
         const int M = (s == 1) ? 2 * B : B;
         for (int l = 0; l < L; ++l) {
             // ================= QKV(l) =================
-            __syncthreads();
             {
-                const float* xs = slot[ph & 1];
-                const float* ss = ssq[ph & 1];
+                const int par = ph & 1;
+                float* xs = slot[par];
+                if (l == 0) {
+                    if (s == 1) {
+                        gather_x(rc.X, B, tag_of(0), par);
+                    } else {
+                        decide(s - 1, ph_lm(L, s - 1));
+                        if (wave == 3 && eb < B) {
+                            int fb = fed[0];
+#pragma unroll
+                            for (int b = 1; b < BM; ++b)
+                                if (b == eb) fb = fed[b];
+                            es += emb_elem(m, s - 1, fb, ek);
+                        }
+                    }
+                    // rows fed by the codebook tables: P_{s-1}[fed], a quarter per wave
+                    const int r0 = (s == 1) ? B : 0;
+#pragma unroll
+                    for (int b = 0; b < BM; ++b) {
+                        if (b < B) {
+                            const float4* prow = reinterpret_cast<const float4*>(
+                                                     m.ptab + (static_cast<size_t>(s - 1) * V + fed[b]) * DP) +
+                                                 wave * (DP / 16);
+                            float4* d4 = reinterpret_cast<float4*>(xs + (r0 + b) * DP) + wave * (DP / 16);
+                            const float4 t = prow[lane];
+                            d4[lane] = t;
+                            const float q = wave_sum(t.x * t.x + t.y * t.y + t.z * t.z + t.w * t.w);
+                            if (lane == 0) ssp[par][wave][r0 + b] = q;
+                        }
+                    }
+                } else {
+                    gather_x(rc.X, M, tag_of(ph - 1), par);
+                }
+                __syncthreads();
                 if (l == 0) {
 #pragma unroll
                     for (int r = 0; r < MR; ++r) xr[r] = (r < M) ? xs[r * DP + 4 * wg + wave] : 0.f;
                 }
-                float acc[4 * MR];
-#pragma unroll
-                for (int i = 0; i < 4 * MR; ++i) acc[i] = 0.f;
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-#pragma unroll
-                    for (int r = 0; r < MR; ++r) {
-                        if (r < M) {
-                            float x8[8];
-                            act8(xs + r * DP, g_attn(l), c, x8);
-#pragma unroll
-                            for (int q = 0; q < 4; ++q) acc[q * MR + r] = dot8(wQ[q * 2 + c], x8, acc[q * MR + r]);
-                        }
-                    }
-                    sched_fence();
-                }
-                float res[4 * MR];
-#pragma unroll
-                for (int r = 0; r < MR; ++r) {
-                    const float rinv = (r < M) ? 1.0f / sqrtf(ss[r] / static_cast<float>(DP) + eps) : 0.f;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) res[q * MR + r] = (r < M) ? wave_sum(acc[q * MR + r]) * rinv : 0.f;
-                }
-                if (lane < 4 * M) {
-                    const int q = lane / M, r = lane - q * M;
-                    st_rec(rc.QKV + static_cast<size_t>(r) * NQKV + 16 * wg + 4 * wave + q,
-                           pick(res, 4 * MR, q * MR + r), tag_of(ph));
-                }
-            }
-            ++ph;
-            // ================= ATTN(l) =================
-            __syncthreads();
-            load_wO(l);
-            sched_fence();
-            if (wg < B * NKV && wave < 2) {
-                const float* sl = slot[ph & 1];
-                const int b = wg / NKV, g = wg % NKV, h = 2 * g + wave;
-                const int pf = (s == 1) ? 0 : s;
-                const int npos = (s == 1) ? 2 : 1;
-                const size_t kvb = ((static_cast<size_t>(l) * m.max_batch + b) * kPositions) * NKV * HD;
-                const float* gq = g_q(l);
-                const float* gk = g_k(l);
-                float kn[2][2] = {{0.f, 0.f}, {0.f, 0.f}}, vn[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-#pragma unroll
-                for (int pi = 0; pi < 2; ++pi) {
-                    if (pi >= npos) break;
-                    const int p = pf + pi;
-                    const int r = (s == 1) ? pi * B + b : b;
-                    const float* nd = sl + 4096 + pi * 512;
-                    const float c0 = rope_s[0][p * (HD / 2) + lane], s0 = rope_s[1][p * (HD / 2) + lane];
-                    {   // key: per-head RMSNorm, rotate-half RoPE (pair lane, lane+64)
-                        const float k0 = nd[256 + lane], k1 = nd[256 + lane + 64];
-                        const float rv = 1.0f / sqrtf(wave_sum(k0 * k0 + k1 * k1) / static_cast<float>(HD) + eps);
-                        const float a0 = gk[lane] * (k0 * rv), a1 = gk[lane + 64] * (k1 * rv);
-                        kn[pi][0] = a0 * c0 - a1 * s0;
-                        kn[pi][1] = a1 * c0 + a0 * s0;
-                        vn[pi][0] = nd[384 + lane];
-                        vn[pi][1] = nd[384 + lane + 64];
-                    }
-                    if (wave == 0) {
-                        const size_t off = kvb + (static_cast<size_t>(p) * NKV + g) * HD;
-                        st_act(m.kc + off + lane, kn[pi][0]);
-                        st_act(m.kc + off + lane + 64, kn[pi][1]);
-                        st_act(m.vc + off + lane, vn[pi][0]);
-                        st_act(m.vc + off + lane + 64, vn[pi][1]);
-                    }
-                    float q0v, q1v;
-                    {
-                        const float x0 = nd[wave * HD + lane], x1 = nd[wave * HD + lane + 64];
-                        const float rv = 1.0f / sqrtf(wave_sum(x0 * x0 + x1 * x1) / static_cast<float>(HD) + eps);
-                        const float a0 = gq[lane] * (x0 * rv), a1 = gq[lane + 64] * (x1 * rv);
-                        q0v = a0 * c0 - a1 * s0;
-                        q1v = a1 * c0 + a0 * s0;
-                    }
-                    float sc[kPositions];
-                    float mx = -__builtin_huge_valf();
-#pragma unroll
-                    for (int t = 0; t < kPositions; ++t) {
-                        if (t <= p) {
-                            float d;
-                            if (t < pf) {
-                                d = q0v * sl[t * HD + lane] + q1v * sl[t * HD + lane + 64];
-                            } else {
-                                const bool j0 = (t == pf);
-                                d = q0v * (j0 ? kn[0][0] : kn[1][0]) + q1v * (j0 ? kn[0][1] : kn[1][1]);
-                            }
-                            d = wave_sum(d) * m.attn_scale;
-                            sc[t] = d;
-                            mx = fmaxf(mx, d);
-                        }
-                    }
-                    float den = 0.f;
-#pragma unroll
-                    for (int t = 0; t < kPositions; ++t)
-                        if (t <= p) {
-                            sc[t] = expf(sc[t] - mx);
-                            den += sc[t];
-                        }
-                    float o0 = 0.f, o1 = 0.f;
-#pragma unroll
-                    for (int t = 0; t < kPositions; ++t) {
-                        if (t <= p) {
-                            const float pt = sc[t] / den;
-                            float v0, v1;
-                            if (t < pf) {
-                                v0 = sl[2048 + t * HD + lane];
-                                v1 = sl[2048 + t * HD + lane + 64];
-                            } else {
-                                const bool j0 = (t == pf);
-                                v0 = j0 ? vn[0][0] : vn[1][0];
-                                v1 = j0 ? vn[0][1] : vn[1][1];
-                            }
-                            o0 = fmaf(pt, v0, o0);
-                            o1 = fmaf(pt, v1, o1);
-                        }
-                    }
-                    uint64_t* orow = rc.AO + static_cast<size_t>(r) * QD + h * HD;
-                    st_rec(orow + lane, o0, tag_of(ph));
-                    st_rec(orow + lane + 64, o1, tag_of(ph));
-                }
-            }
-            ++ph;
-            // ================= O(l) =================
-            __syncthreads();
-            load_wU(l);
-            sched_fence();
-            {
-                const float* as = slot[ph & 1];
-                float acc[MR];
-#pragma unroll
-                for (int r = 0; r < MR; ++r) acc[r] = 0.f;
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-#pragma unroll
-                    for (int r = 0; r < MR; ++r)
-                        if (r < M) {
-                            float x8[8];
-                            lds8(as + r * QD + c * 512 + lane * 8, x8);
-                            acc[r] = dot8(wO[c], x8, acc[r]);
-                        }
-                    sched_fence();
-                }
-                const int n = 4 * wg + wave;
-                float res[MR];
-#pragma unroll
-                for (int r = 0; r < MR; ++r) {
-                    res[r] = 0.f;
-                    if (r < M) {
-                        xr[r] += wave_sum(acc[r]);
-                        res[r] = xr[r];
-                    }
-                }
-                if (lane < M) st_rec(rc.X + static_cast<size_t>(lane) * DP + n, pick(res, MR, lane), tag_of(ph));
-            }
-            ++ph;
-            // ================= UP(l) =================
-            __syncthreads();
-            load_wD(l);
-            sched_fence();
-            {
-                const float* xs = slot[ph & 1];
-                const float* ss = ssq[ph & 1];
-                float ag[3 * MR], au[3 * MR];
-#pragma unroll
-                for (int i = 0; i < 3 * MR; ++i) { ag[i] = 0.f; au[i] = 0.f; }
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-#pragma unroll
-                    for (int r = 0; r < MR; ++r)
-                        if (r < M) {
-                            float x8[8];
-                            act8(xs + r * DP, g_ffn(l), c, x8);
-#pragma unroll
-                            for (int q = 0; q < 3; ++q) {
-                                ag[q * MR + r] = dot8(wU[q * 2 + c], x8, ag[q * MR + r]);
-                                au[q * MR + r] = dot8(wU[6 + q * 2 + c], x8, au[q * MR + r]);
-                            }
-                        }
-                    sched_fence();
-                }
-                float res[3 * MR];
-#pragma unroll
-                for (int r = 0; r < MR; ++r) {
-                    const float rinv = (r < M) ? 1.0f / sqrtf(ss[r] / static_cast<float>(DP) + eps) : 0.f;
-#pragma unroll
-                    for (int q = 0; q < 3; ++q) {
-                        res[q * MR + r] = 0.f;
-                        if (r < M) {
-                            const float gv = wave_sum(ag[q * MR + r]) * rinv;
-                            const float uv = wave_sum(au[q * MR + r]) * rinv;
-                            res[q * MR + r] = (gv / (1.0f + expf(-gv))) * uv;
-                        }
-                    }
-                }
-                if (lane < 3 * M) {
-                    const int q = lane / M, r = lane - q * M;
-                    st_rec(rc.H + static_cast<size_t>(r) * F + 12 * wg + 3 * wave + q, pick(res, 3 * MR, q * MR + r),
-                           tag_of(ph));
-                }
-            }
-            ++ph;
-            // ================= DOWN(l) =================
-            __syncthreads();
-            if (l + 1 < L) load_wQ(l + 1); else load_wL(s);
-            sched_fence();
-            {
-                const float* hs = slot[ph & 1];
-                float acc[MR];
-#pragma unroll
-                for (int r = 0; r < MR; ++r) acc[r] = 0.f;
-#pragma unroll
-                for (int c = 0; c < 6; ++c) {
-#pragma unroll
-                    for (int r = 0; r < MR; ++r)
-                        if (r < M) {
-                            float x8[8];
-                            lds8(hs + r * F + c * 512 + lane * 8, x8);
-                            acc[r] = dot8(wD[c], x8, acc[r]);
-                        }
-                    sched_fence();
-                }
-                const int n = 4 * wg + wave;
-                float res[MR];
-#pragma unroll
-                for (int r = 0; r < MR; ++r) {
-                    res[r] = 0.f;
-                    if (r < M) {
-                        xr[r] += wave_sum(acc[r]);
-                        res[r] = xr[r];
-                    }
-                }
-                if (lane < M) {
-                    const float v = pick(res, MR, lane);
-                    st_rec(rc.X + static_cast<size_t>(lane) * DP + n, v, tag_of(ph));
-                    if (a.taps) {
-                        const int pos = (s == 1) ? (lane >= B ? 1 : 0) : s;
-                        const int b = (s == 1 && lane >= B) ? lane - B : lane;
-                        a.taps[((static_cast<size_t>(pos) * L + l) * B + b) * DP + n] = v;
-                    }
-                }
-            }
-            ++ph;
-        }
-        // ================= LM(s) =================
-        __syncthreads();
-        if (s < kSteps) load_wQ(0);
-        sched_fence();
-        {
-            const float* xs = slot[ph & 1];
-            const float* ss = ssq[ph & 1];
-            constexpr int BM = MR / 2;
-            float acc[2 * BM];
-#pragma unroll
-            for (int i = 0; i < 2 * BM; ++i) acc[i] = 0.f;
-#pragma unroll
-            for (int b = 0; b < BM; ++b)
-                if (b < B) {
+                const float* ga = g_attn(l);
+                for (int r = 0; r < M; ++r) {
+                    float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int c = 0; c < 2; ++c) {
                         float x8[8];
-                        act8(xs + b * DP, g_out, c, x8);
+                        act8(xs + r * DP, ga, c, x8);
 #pragma unroll
-                        for (int q = 0; q < 2; ++q) acc[q * BM + b] = dot8(wL[q * 2 + c], x8, acc[q * BM + b]);
+                        for (int q = 0; q < 4; ++q) acc[q] = dot8(wQ[q * 2 + c], x8, acc[q]);
+                    }
+                    const float rinv = 1.0f / sqrtf(row_ss(par, r) / static_cast<float>(DP) + eps);
+                    float v = 0.f;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float t = wave_sum(acc[q]) * rinv;
+                        v = (lane == q) ? t : v;
+                    }
+                    if (lane < 4) st_rec(rc.QKV + static_cast<size_t>(r) * NQKV + 16 * wg + 4 * wave + lane, v, tag_of(ph));
+                }
+                ++ph;
+            }
+            // ================= ATTN(l) =================
+            {
+                const int par = ph & 1;
+                float* hist = slot[par];
+                const bool unit = wg < B * NKV;
+                const int b = wg / NKV, g = wg % NKV;
+                const int pf = (s == 1) ? 0 : s;
+                const int npos = (s == 1) ? 2 : 1;
+                const size_t kvb = ((static_cast<size_t>(l) * m.max_batch + b) * kPositions) * NKV * HD;
+                if (unit) {
+                    // cached keys/values of earlier positions: LDS-direct loads
+                    if (wave == 0) {
+                        for (int tt = 0; tt < pf; ++tt) {
+                            const size_t off = kvb + (static_cast<size_t>(tt) * NKV + g) * HD;
+                            dma64(m.kc + off, hist + tt * HD);
+                            dma64(m.kc + off + 64, hist + tt * HD + 64);
+                            dma64(m.vc + off, hist + 2048 + tt * HD);
+                            dma64(m.vc + off + 64, hist + 2048 + tt * HD + 64);
+                        }
+                    }
+                    // new head vectors: wave w takes q 2g, q 2g+1, k g, v g
+                    const int col = wave < 2 ? (2 * g + wave) * HD : (wave == 2 ? (NQ + g) * HD : (NQ + NKV + g) * HD);
+                    const uint32_t qt = tag_of(ph - 1);
+                    for (int pi = 0; pi < npos; ++pi)
+                        poll_head(rc.QKV + static_cast<size_t>(pi * B + b) * NQKV + col, qt,
+                                  hist + 4096 + 512 * pi + wave * HD, err);
+                    __builtin_amdgcn_s_waitcnt(0);
+                }
+                __syncthreads();
+                if (unit && wave < 2) {
+                    const int h = 2 * g + wave;
+                    const float* gq = g_q(l);
+                    const float* gk = g_k(l);
+                    float* scr = hist + 5120 + 64 * wave;
+                    for (int pi = 0; pi < npos; ++pi) {
+                        const int p = pf + pi;
+                        const int r = (s == 1) ? pi * B + b : b;
+                        const float* nd = hist + 4096 + pi * 512;
+                        const float c0 = rope_s[0][p * (HD / 2) + lane], s0 = rope_s[1][p * (HD / 2) + lane];
+                        float kv0, kv1;
+                        {   // key: per-head RMSNorm, rotate-half RoPE (pair lane, lane+64)
+                            const float k0 = nd[256 + lane], k1 = nd[256 + lane + 64];
+                            const float rv = 1.0f / sqrtf(wave_sum(k0 * k0 + k1 * k1) / static_cast<float>(HD) + eps);
+                            const float a0 = gk[lane] * (k0 * rv), a1 = gk[lane + 64] * (k1 * rv);
+                            kv0 = a0 * c0 - a1 * s0;
+                            kv1 = a1 * c0 + a0 * s0;
+                        }
+                        const float vv0 = nd[384 + lane], vv1 = nd[384 + lane + 64];
+                        if (wave == 0) {
+                            const size_t off = kvb + (static_cast<size_t>(p) * NKV + g) * HD;
+                            st_act(m.kc + off + lane, kv0);
+                            st_act(m.kc + off + lane + 64, kv1);
+                            st_act(m.vc + off + lane, vv0);
+                            st_act(m.vc + off + lane + 64, vv1);
+                        }
+                        float q0v, q1v;
+                        {
+                            const float x0 = nd[wave * HD + lane], x1 = nd[wave * HD + lane + 64];
+                            const float rv = 1.0f / sqrtf(wave_sum(x0 * x0 + x1 * x1) / static_cast<float>(HD) + eps);
+                            const float a0 = gq[lane] * (x0 * rv), a1 = gq[lane + 64] * (x1 * rv);
+                            q0v = a0 * c0 - a1 * s0;
+                            q1v = a1 * c0 + a0 * s0;
+                        }
+                        // scores over positions 0..p (earlier ones from LDS, this one
+                        // from registers), softmax, weighted value sum
+                        const float sc_self = wave_sum(q0v * kv0 + q1v * kv1) * m.attn_scale;
+                        float mx = sc_self;
+                        for (int t = 0; t < p; ++t) {
+                            const float d = wave_sum(q0v * hist[t * HD + lane] + q1v * hist[t * HD + lane + 64]) * m.attn_scale;
+                            if (lane == t) scr[t] = d;
+                            mx = fmaxf(mx, d);
+                        }
+                        float den = 0.f, o0 = 0.f, o1 = 0.f;
+                        for (int t = 0; t < p; ++t) {
+                            const float e = expf(scr[t] - mx);
+                            den += e;
+                            o0 = fmaf(e, hist[2048 + t * HD + lane], o0);
+                            o1 = fmaf(e, hist[2048 + t * HD + lane + 64], o1);
+                        }
+                        {
+                            const float e = expf(sc_self - mx);
+                            den += e;
+                            o0 = fmaf(e, vv0, o0);
+                            o1 = fmaf(e, vv1, o1);
+                        }
+                        uint64_t* orow = rc.AO + static_cast<size_t>(r) * QD + h * HD;
+                        st_rec(orow + lane, o0 / den, tag_of(ph));
+                        st_rec(orow + lane + 64, o1 / den, tag_of(ph));
+                        // the prefill's second position attends to this one; both
+                        // waves write the same values, each before it reads them
+                        if (pi + 1 < npos) {
+                            hist[p * HD + lane] = kv0;
+                            hist[p * HD + lane + 64] = kv1;
+                            hist[2048 + p * HD + lane] = vv0;
+                            hist[2048 + p * HD + lane + 64] = vv1;
+                        }
                     }
                 }
+                // next phase's weights, after this phase's stores have left
+                sched_fence();
+                load_wO(l);
+                sched_fence();
+                ++ph;
+            }
+            // ================= O(l) =================
+            {
+                const int par = ph & 1;
+                float* as = slot[par];
+                const uint32_t tg = tag_of(ph - 1);
+                for (int r = 0; r < M; ++r) (void)poll_share<QD>(rc.AO + static_cast<size_t>(r) * QD, wave, tg, as + r * QD, err);
+                __syncthreads();
+                const int n = 4 * wg + wave;
+                for (int r = 0; r < M; ++r) {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        float x8[8];
+                        lds8(as + r * QD + c * 512 + lane * 8, x8);
+                        acc = dot8(wO[c], x8, acc);
+                    }
+                    const float d = wave_sum(acc);
+                    float nv = 0.f;
+#pragma unroll
+                    for (int i = 0; i < MR; ++i)
+                        if (i == r) { xr[i] += d; nv = xr[i]; }
+                    if (lane == 0) st_rec(rc.X + static_cast<size_t>(r) * DP + n, nv, tag_of(ph));
+                }
+                sched_fence();
+                load_wU(l);
+                sched_fence();
+                ++ph;
+            }
+            // ================= UP(l) =================
+            {
+                const int par = ph & 1;
+                float* xs = slot[par];
+                gather_x(rc.X, M, tag_of(ph - 1), par);
+                __syncthreads();
+                const float* gf = g_ffn(l);
+                for (int r = 0; r < M; ++r) {
+                    float ag[3] = {0.f, 0.f, 0.f}, au[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) {
+                        float x8[8];
+                        act8(xs + r * DP, gf, c, x8);
+#pragma unroll
+                        for (int q = 0; q < 3; ++q) {
+                            ag[q] = dot8(wU[q * 2 + c], x8, ag[q]);
+                            au[q] = dot8(wU[6 + q * 2 + c], x8, au[q]);
+                        }
+                    }
+                    const float rinv = 1.0f / sqrtf(row_ss(par, r) / static_cast<float>(DP) + eps);
+                    float v = 0.f;
+#pragma unroll
+                    for (int q = 0; q < 3; ++q) {
+                        const float gv = wave_sum(ag[q]) * rinv;
+                        const float uv = wave_sum(au[q]) * rinv;
+                        const float hv = (gv / (1.0f + expf(-gv))) * uv;
+                        v = (lane == q) ? hv : v;
+                    }
+                    if (lane < 3) st_rec(rc.H + static_cast<size_t>(r) * F + 12 * wg + 3 * wave + lane, v, tag_of(ph));
+                }
+                sched_fence();
+                load_wD(l);
+                sched_fence();
+                ++ph;
+            }
+            // ================= DOWN(l) =================
+            {
+                const int par = ph & 1;
+                float* hs = slot[par];
+                const uint32_t tg = tag_of(ph - 1);
+                for (int r = 0; r < M; ++r) (void)poll_share<F>(rc.H + static_cast<size_t>(r) * F, wave, tg, hs + r * F, err);
+                __syncthreads();
+                const int n = 4 * wg + wave;
+                for (int r = 0; r < M; ++r) {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int c = 0; c < 6; ++c) {
+                        float x8[8];
+                        lds8(hs + r * F + c * 512 + lane * 8, x8);
+                        acc = dot8(wD[c], x8, acc);
+                    }
+                    const float d = wave_sum(acc);
+                    float nv = 0.f;
+#pragma unroll
+                    for (int i = 0; i < MR; ++i)
+                        if (i == r) { xr[i] += d; nv = xr[i]; }
+                    if (lane == 0) {
+                        st_rec(rc.X + static_cast<size_t>(r) * DP + n, nv, tag_of(ph));
+                        if (a.taps) {
+                            const int pos = (s == 1) ? (r >= B ? 1 : 0) : s;
+                            const int bb = (s == 1 && r >= B) ? r - B : r;
+                            a.taps[((static_cast<size_t>(pos) * L + l) * B + bb) * DP + n] = nv;
+                        }
+                    }
+                }
+                sched_fence();
+                if (l + 1 < L) load_wQ(l + 1); else load_wL(s);
+                sched_fence();
+                ++ph;
+            }
+        }
+        // ================= LM(s) =================
+        {
+            const int par = ph & 1;
+            float* xs = slot[par];
+            const int r0 = (s == 1) ? B : 0;
+            gather_x(rc.X + static_cast<size_t>(r0) * DP, B, tag_of(ph - 1), par);
+            __syncthreads();
             const int v0 = 8 * wg + 2 * wave;
 #pragma unroll
             for (int b = 0; b < BM; ++b) {
                 if (b < B) {
-                    const float rinv = 1.0f / sqrtf(ss[b] / static_cast<float>(DP) + eps);
-                    const float l0 = wave_sum(acc[b]) * rinv;
-                    const float l1 = wave_sum(acc[BM + b]) * rinv;
+                    float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) {
+                        float x8[8];
+                        act8(xs + b * DP, g_out, c, x8);
+                        acc0 = dot8(wL[c], x8, acc0);
+                        acc1 = dot8(wL[2 + c], x8, acc1);
+                    }
+                    const float rinv = 1.0f / sqrtf(row_ss(par, b) / static_cast<float>(DP) + eps);
+                    const float l0 = wave_sum(acc0) * rinv;
+                    const float l1 = wave_sum(acc1) * rinv;
                     if (a.logits_out && lane < 2)
                         a.logits_out[(static_cast<size_t>(b) * kSteps + (s - 1)) * V + v0 + lane] = lane ? l1 : l0;
                     const bool second = ordered_bits(l1) > ordered_bits(l0);
-                    const uint32_t ob = ordered_bits(second ? l1 : l0);
-                    const uint32_t idx = static_cast<uint32_t>(v0 + (second ? 1 : 0));
-                    uint64_t* kr = rc.KEY + (static_cast<size_t>(b) * kGW + gw) * 2;
-                    if (lane == 0) st_rec_u(kr, ob, tag_of(ph));
-                    if (lane == 1) st_rec_u(kr + 1, idx, tag_of(ph));
+                    const uint64_t key = (static_cast<uint64_t>(ordered_bits(second ? l1 : l0)) << 32) |
+                                         (0xFFFFFFFFu - static_cast<uint32_t>(v0 + (second ? 1 : 0)));
+                    if (lane == 0) lmk[wave][b] = key;
                 }
             }
+            __syncthreads();
+            if (wave == 0 && lane < B) {
+                uint64_t best = 0;
+#pragma unroll
+                for (int w = 0; w < kW; ++w) {
+                    uint64_t k = 0;
+#pragma unroll
+                    for (int b = 0; b < BM; ++b)
+                        if (b == lane) k = lmk[w][b];
+                    best = k > best ? k : best;
+                }
+                uint64_t* kr = rc.KEY + (static_cast<size_t>(lane) * kNwg + wg) * 2;
+                st_rec_u(kr, static_cast<uint32_t>(best >> 32), tag_of(ph));
+                st_rec_u(kr + 1, 0xFFFFFFFFu - static_cast<uint32_t>(best & 0xFFFFFFFFu), tag_of(ph));
+            }
+            sched_fence();
+            if (s < kSteps) load_wQ(0);
+            sched_fence();
+            ++ph;
         }
-        ++ph;
+    }
+    // ================= FINAL: last token, embedding sum out =================
+    decide(kSteps, ph_lm(L, kSteps));
+    if (wave == 3 && eb < B) {
+        int fb = fed[0];
+#pragma unroll
+        for (int b = 1; b < BM; ++b)
+            if (b == eb) fb = fed[b];
+        es += emb_elem(m, kSteps, fb, ek);
+        a.embsum[static_cast<size_t>(eb) * DT + ek] = es;
     }
 }
+
 
 }  // namespace stream
 }  // namespace qp
