@@ -534,10 +534,14 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                 }
                 __syncthreads();
                 if (unit && wave < 2) {
+                    // one wave per query head; all <= 16 scores at once: key t on
+                    // lanes 4t..4t+3, each lane a 32-wide slice of the head
                     const int h = 2 * g + wave;
                     const float* gq = g_q(l);
                     const float* gk = g_k(l);
-                    float* scr = hist + 5120 + 64 * wave;
+                    float* qb = hist + 5120 + 128 * wave;     // this wave's rotated query
+                    float* eb = hist + 5376 + 16 * wave;      // its softmax weights
+                    const int kt = lane >> 2, kq = (lane & 3) * 32;
                     for (int pi = 0; pi < npos; ++pi) {
                         const int p = pf + pi;
                         const int r = (s == 1) ? pi * B + b : b;
@@ -559,47 +563,51 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                             st_act(m.vc + off + lane, vv0);
                             st_act(m.vc + off + lane + 64, vv1);
                         }
-                        float q0v, q1v;
+                        // this position's key/value join the history (both waves
+                        // write the same values, each before it reads them)
+                        hist[p * HD + lane] = kv0;
+                        hist[p * HD + lane + 64] = kv1;
+                        hist[2048 + p * HD + lane] = vv0;
+                        hist[2048 + p * HD + lane + 64] = vv1;
                         {
                             const float x0 = nd[wave * HD + lane], x1 = nd[wave * HD + lane + 64];
                             const float rv = 1.0f / sqrtf(wave_sum(x0 * x0 + x1 * x1) / static_cast<float>(HD) + eps);
                             const float a0 = gq[lane] * (x0 * rv), a1 = gq[lane + 64] * (x1 * rv);
-                            q0v = a0 * c0 - a1 * s0;
-                            q1v = a1 * c0 + a0 * s0;
+                            qb[lane] = a0 * c0 - a1 * s0;
+                            qb[lane + 64] = a1 * c0 + a0 * s0;
                         }
-                        // scores over positions 0..p (earlier ones from LDS, this one
-                        // from registers), softmax, weighted value sum
-                        const float sc_self = wave_sum(q0v * kv0 + q1v * kv1) * m.attn_scale;
-                        float mx = sc_self;
-                        for (int t = 0; t < p; ++t) {
-                            const float d = wave_sum(q0v * hist[t * HD + lane] + q1v * hist[t * HD + lane + 64]) * m.attn_scale;
-                            if (lane == t) scr[t] = d;
-                            mx = fmaxf(mx, d);
+                        // scores
+                        float sc = 0.f;
+                        if (kt <= p) {
+#pragma unroll
+                            for (int i = 0; i < 32; i += 4) {
+                                const float4 qv = *reinterpret_cast<const float4*>(qb + kq + i);
+                                const float4 kv = *reinterpret_cast<const float4*>(hist + kt * HD + kq + i);
+                                sc = fmaf(qv.x, kv.x, sc);
+                                sc = fmaf(qv.y, kv.y, sc);
+                                sc = fmaf(qv.z, kv.z, sc);
+                                sc = fmaf(qv.w, kv.w, sc);
+                            }
                         }
-                        float den = 0.f, o0 = 0.f, o1 = 0.f;
-                        for (int t = 0; t < p; ++t) {
-                            const float e = expf(scr[t] - mx);
-                            den += e;
-                            o0 = fmaf(e, hist[2048 + t * HD + lane], o0);
-                            o1 = fmaf(e, hist[2048 + t * HD + lane + 64], o1);
-                        }
-                        {
-                            const float e = expf(sc_self - mx);
-                            den += e;
-                            o0 = fmaf(e, vv0, o0);
-                            o1 = fmaf(e, vv1, o1);
+                        sc += dpp_or_zero<0xB1, 0xF>(sc);   // lanes of a quad: one key
+                        sc += dpp_or_zero<0x4E, 0xF>(sc);
+                        sc = (kt <= p) ? sc * m.attn_scale : -__builtin_huge_valf();
+                        float mx = sc;
+#pragma unroll
+                        for (int off = 32; off >= 4; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+                        const float e = (kt <= p) ? expf(sc - mx) : 0.f;
+                        const float den = wave_sum((lane & 3) == 0 ? e : 0.f);
+                        if ((lane & 3) == 0 && kt < kPositions) eb[kt] = e;
+                        // weighted values
+                        float o0 = 0.f, o1 = 0.f;
+                        for (int t = 0; t <= p; ++t) {
+                            const float w = eb[t];
+                            o0 = fmaf(w, hist[2048 + t * HD + lane], o0);
+                            o1 = fmaf(w, hist[2048 + t * HD + lane + 64], o1);
                         }
                         uint64_t* orow = rc.AO + static_cast<size_t>(r) * QD + h * HD;
                         st_rec(orow + lane, o0 / den, tag_of(ph));
                         st_rec(orow + lane + 64, o1 / den, tag_of(ph));
-                        // the prefill's second position attends to this one; both
-                        // waves write the same values, each before it reads them
-                        if (pi + 1 < npos) {
-                            hist[p * HD + lane] = kv0;
-                            hist[p * HD + lane + 64] = kv1;
-                            hist[2048 + p * HD + lane] = vv0;
-                            hist[2048 + p * HD + lane + 64] = vv1;
-                        }
                     }
                 }
                 // next phase's weights, after this phase's stores have left
