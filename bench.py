@@ -81,6 +81,46 @@ def cpu_baseline(wl, W, H, q0, budget_s: float):
                       f"{el:.1f} s"}
 
 
+COPY_BYTES = 1 << 30
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the dataflow kernel from the committed counter
+    summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy), or None when
+    there is none for this workload or the kernel's sources have changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"k_stream_{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if line.startswith("#") or ":" not in line:
+            continue
+        k, v = line.split(":", 1)
+        kv[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in kv.get("sources", "").split():
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != kv.get("sources_sha256"):
+        return None
+    return int(kv["traffic_bytes_per_launch"])
+
+
+def calibrate_copy(torch, dev):
+    """A plain copy of COPY_BYTES, five times: the reference for scaling the
+    FETCH_SIZE / WRITE_SIZE counters (each launch reads and writes exactly
+    COPY_BYTES)."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).uniform_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": COPY_BYTES, "launches": 5}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -91,6 +131,8 @@ def main():
     ap.add_argument("--generic", action="store_true", help="the generic persistent kernel even where a specialised one exists")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of known size (to scale HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -105,6 +147,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        calibrate_copy(torch, dev)
+        return
     wl = synth.WORKLOADS[args.workload]
     g = wl.geom
     B = wl.batch
@@ -124,24 +169,29 @@ def main():
         raise RuntimeError("device flag raised during warm-up")
 
     stream = torch.cuda.current_stream(dev)
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    # one event pair per frame call, on the stream the library launches on:
+    # for the single-kernel drivers that brackets exactly one kernel launch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t_start.record(stream)
     for i in range(args.steps):
+        ev[i][0].record(stream)
         pred.run(Hd[i % F], qd[i % F], tok, emb, stepwise=args.stepwise, generic=args.generic)
-    t_end.record(stream)
+        ev[i][1].record(stream)
     torch.cuda.synchronize()
-    ms = t_start.elapsed_time(t_end)
+    ms = ev[0][0].elapsed_time(ev[-1][1])
+    launch_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
     if pred.get_error() != 0:
         raise RuntimeError("device flag raised during the timed frames")
     ms_per_step = ms / args.steps
     frames_per_s = B * args.steps / (ms / 1e3)
 
+    driver = "stepwise" if args.stepwise else ("generic" if args.generic or B > 2 or g.weight_dtype != "bf16"
+                                               else "dataflow")
     nbytes = algorithmic_bytes(g)
-    achieved_gbs = nbytes / (ms_per_step / 1e3) / 1e9
+    achieved_gbs = nbytes / (launch_ms / 1e3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+                "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(wl.name) if driver == "dataflow" else None}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -165,8 +215,8 @@ def main():
                    "weights": g.weight_dtype, "embeddings": g.emb_format,
                    "predictor": f"dP={g.d_model} L={g.n_layers} heads={g.n_q_heads}/{g.n_kv_heads}x{g.head_dim} "
                                 f"F={g.d_ffn} V={g.vocab} dT={g.d_talker}",
-                   "driver": "stepwise" if args.stepwise else ("generic" if args.generic or B > 2 or g.weight_dtype != "bf16"
-                                                                else "dataflow"),
+                   "driver": driver,
+                   "ms_per_launch": round(launch_ms, 4),
                    "tokens_per_s": round(15 * frames_per_s, 1),
                    "algorithmic_bytes_per_step": nbytes,
                    "algorithmic_flops_per_step": algorithmic_flops(g, B)},
