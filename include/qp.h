@@ -158,8 +158,16 @@ qp_status qp_run_frames(qp_handle* h, int32_t B, const float* H,
 /* Execution strategy hints for qp_run_frames_ex `flags`. */
 #define QP_FLAG_STEPWISE 0x1u   /* one kernel per phase (no persistent kernel) */
 #define QP_FLAG_GENERIC 0x2u    /* the generic persistent kernel even where a
-                                   specialised one exists (B <= 2, bf16, the
-                                   1.7B predictor geometry)                   */
+                                   specialised one exists                      */
+#define QP_FLAG_TILED 0x4u      /* the batched matrix-core path (one kernel per
+                                   phase, projections on MFMA) for any B; only
+                                   for bf16 or Q8_0 weights with dT, dP, nq*hd
+                                   and F multiples of 256 and nqkv, V multiples
+                                   of 32 (else QP_ERR_INVALID_ARG); excludes
+                                   the other flags.
+   Without flags the library picks: B <= 2 with bf16 weights and the 1.7B
+   predictor geometry -> the dataflow kernel; otherwise, where the batched
+   path applies -> it; otherwise the generic persistent kernel.             */
 
 /* Same computation with test hooks (any hook may be NULL):
  *   force_tokens int32 [B, 15]  teacher forcing: the token fed back at step

@@ -33,6 +33,7 @@ QP_ERR_DEVICE_FLAG = -8
 
 QP_FLAG_STEPWISE = 0x1
 QP_FLAG_GENERIC = 0x2
+QP_FLAG_TILED = 0x4
 
 WEIGHT_DTYPES = {"f32": 0, "bf16": 1, "q8_0": 2}
 EMB_FORMATS = {"f32": 0, "bf16": 1, "ema": 2}
@@ -168,7 +169,7 @@ class Predictor:
         self.h = h
 
     def run(self, H, q0, tokens_out, embsum_out, force=None, logits_out=None, taps_out=None,
-            stepwise: bool = False, generic: bool = False, stream=None):
+            stepwise: bool = False, generic: bool = False, tiled: bool = False, stream=None):
         """Enqueue one frame on ``stream`` (default: torch's current stream)."""
         import torch
         B = H.shape[0]
@@ -188,7 +189,8 @@ class Predictor:
             assert tuple(taps_out.shape) == (N_CODEBOOKS, self.geom.n_layers, B, self.geom.d_model)
         if stream is None:
             stream = torch.cuda.current_stream(H.device).cuda_stream
-        flags = (QP_FLAG_STEPWISE if stepwise else 0) | (QP_FLAG_GENERIC if generic else 0)
+        flags = ((QP_FLAG_STEPWISE if stepwise else 0) | (QP_FLAG_GENERIC if generic else 0) |
+                 (QP_FLAG_TILED if tiled else 0))
         if force is None and logits_out is None and taps_out is None and flags == 0:
             st = self.lib.qp_run_frames(self.h, B, _dptr(H), _dptr(q0), _dptr(tokens_out),
                                         _dptr(embsum_out), stream)

@@ -1,6 +1,8 @@
 // Host side of the code-predictor library: the C ABI declared in qp.h,
-// create-time weight preparation, and the two frame drivers (one persistent
-// cooperative kernel per frame, or one kernel per phase).
+// create-time weight preparation, and the frame drivers: the dataflow kernel
+// (small batches of the 1.7B geometry), the batched matrix-core path (one
+// kernel per phase) and the generic path (one persistent cooperative kernel
+// per frame, or one kernel per phase).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -13,6 +15,7 @@
 #include "qp_common.h"
 #include "qp_phases.h"
 #include "qp_stream.h"
+#include "qp_tiled.h"
 
 using namespace qp;
 
@@ -174,6 +177,17 @@ struct qp_handle {
     bool stream_ok = false;
     qp::stream::Recs recs{};
     uint32_t seq = 0;
+    // batched matrix-core path
+    bool tiled_ok = false;
+    std::vector<LayerDev> layers_host;
+    qp::tiled::FMat t_proj{};
+    std::vector<qp::tiled::FMat> t_qkv, t_o, t_gate, t_up, t_down;
+    qp::tiled::FMat t_lm[kSteps]{};
+    unsigned long long* t_keys = nullptr;   // [max_batch][V/32]
+    float* t_part = nullptr;                // split-K partial tiles
+    size_t t_part_floats = 0;
+    unsigned* t_ctr = nullptr;              // split-K tile counters
+    size_t t_nctr = 0;
 };
 
 namespace {
@@ -245,27 +259,34 @@ struct Uploader {
         }
         return p;
     }
-    // Vertically stack matrices [N_i][K] of one storage type into one device
-    // matrix; Q8_0 rows are split into int8 codes and fp32 scales.
-    Mat stack(const std::vector<const void*>& parts, const std::vector<int>& rows, int K, int wt) {
-        Mat out{nullptr, nullptr};
+    // A matrix on the host in row-major storage: f32 / bf16 elements, or the
+    // Q8_0 rows split into int8 codes [N][K] and fp32 block scales [N][K/32].
+    struct HostMat {
+        std::vector<uint8_t> w;
+        std::vector<float> scale;
         size_t N = 0;
-        for (int r : rows) N += static_cast<size_t>(r);
+        int K = 0, wt = 0;
+    };
+    // Vertically stack matrices [N_i][K] of one storage type.
+    static HostMat build(const std::vector<const void*>& parts, const std::vector<int>& rows, int K, int wt) {
+        HostMat hm;
+        hm.K = K;
+        hm.wt = wt;
+        for (int r : rows) hm.N += static_cast<size_t>(r);
         if (wt == WT_F32 || wt == WT_BF16) {
             const size_t esz = wt == WT_F32 ? 4 : 2;
-            std::vector<uint8_t> buf(N * K * esz);
+            hm.w.resize(hm.N * K * esz);
             size_t off = 0;
             for (size_t i = 0; i < parts.size(); ++i) {
                 const size_t nb = static_cast<size_t>(rows[i]) * K * esz;
-                std::memcpy(buf.data() + off, parts[i], nb);
+                std::memcpy(hm.w.data() + off, parts[i], nb);
                 off += nb;
             }
-            out.w = upload(buf.data(), buf.size());
-            return out;
+            return hm;
         }
         const int nb = K / 32;
-        std::vector<int8_t> codes(N * K);
-        std::vector<float> scales(N * nb);
+        hm.w.resize(hm.N * K);
+        hm.scale.resize(hm.N * nb);
         size_t row = 0;
         for (size_t i = 0; i < parts.size(); ++i) {
             const uint8_t* src = static_cast<const uint8_t*>(parts[i]);
@@ -273,14 +294,44 @@ struct Uploader {
                 const uint8_t* rp = src + static_cast<size_t>(r) * nb * 34;
                 for (int bk = 0; bk < nb; ++bk) {
                     const uint8_t* blk = rp + static_cast<size_t>(bk) * 34;
-                    scales[row * nb + bk] = half_to_float(static_cast<uint16_t>(blk[0] | (blk[1] << 8)));
-                    std::memcpy(&codes[row * K + static_cast<size_t>(bk) * 32], blk + 2, 32);
+                    hm.scale[row * nb + bk] = half_to_float(static_cast<uint16_t>(blk[0] | (blk[1] << 8)));
+                    std::memcpy(&hm.w[row * K + static_cast<size_t>(bk) * 32], blk + 2, 32);
                 }
             }
         }
-        out.w = upload(codes.data(), codes.size());
-        out.scale = static_cast<const float*>(upload(scales.data(), scales.size() * 4));
+        return hm;
+    }
+    Mat rowmajor(const HostMat& hm) {
+        Mat out{nullptr, nullptr};
+        out.w = upload(hm.w.data(), hm.w.size());
+        if (hm.wt == WT_Q8) out.scale = static_cast<const float*>(upload(hm.scale.data(), hm.scale.size() * 4));
         return out;
+    }
+    // MFMA fragment order: fragment (n/16, k/32) holds, for lane
+    // l = (n % 16) + 16 * ((k % 32) / 8), the 8 elements k .. k+7 of row n.
+    qp::tiled::FMat fragments(const HostMat& hm) {
+        qp::tiled::FMat out{nullptr, nullptr};
+        const size_t N = hm.N, K = static_cast<size_t>(hm.K), KB = K / 32;
+        const size_t esz = hm.wt == WT_BF16 ? 2 : 1;
+        std::vector<uint8_t> f(hm.w.size());
+        for (size_t nb = 0; nb < N / 16; ++nb)
+            for (size_t kb = 0; kb < KB; ++kb)
+                for (size_t lane = 0; lane < 64; ++lane) {
+                    const size_t n = nb * 16 + (lane & 15), k = kb * 32 + (lane >> 4) * 8;
+                    std::memcpy(&f[((nb * KB + kb) * 64 + lane) * 8 * esz], &hm.w[(n * K + k) * esz], 8 * esz);
+                }
+        out.w = upload(f.data(), f.size());
+        if (hm.wt == WT_Q8) {
+            std::vector<float> sc(hm.scale.size());
+            for (size_t nb = 0; nb < N / 16; ++nb)
+                for (size_t kb = 0; kb < KB; ++kb)
+                    for (size_t r = 0; r < 16; ++r) sc[(nb * KB + kb) * 16 + r] = hm.scale[(nb * 16 + r) * KB + kb];
+            out.scale = static_cast<const float*>(upload(sc.data(), sc.size() * 4));
+        }
+        return out;
+    }
+    Mat stack(const std::vector<const void*>& parts, const std::vector<int>& rows, int K, int wt) {
+        return rowmajor(build(parts, rows, K, wt));
     }
     Mat one(const void* p, int N, int K, int wt) { return stack({p}, {N}, K, wt); }
 };
@@ -352,10 +403,148 @@ void free_all(qp_handle* h) {
 
 namespace {
 
+// --- batched matrix-core path ---------------------------------------------
+
+template <int WT, int SRC, int EPI>
+void tiled_gemm(const qp_handle* h, qp::tiled::GemmArgs g, hipStream_t stream) {
+    namespace T = qp::tiled;
+    const int gx = EPI == T::EPI_SWIGLU ? g.N / 16 : g.N / 32;
+    const int RT = g.M <= 16 ? 1 : (g.M <= 32 ? 2 : 4);
+    const int gy = (g.M + 16 * RT - 1) / (16 * RT);
+    // products with few output tiles also split K over workgroups
+    int KS = 1;
+    if (SRC != T::SRC_F32_NORM && EPI != T::EPI_SWIGLU && EPI != T::EPI_ARGMAX) {
+        while (KS < T::kMaxKS && gx * gy * KS < 256 && g.K % (256 * KS * 2) == 0 &&
+               static_cast<size_t>(KS * 2) * gx * gy * RT * T::kCT * 256 <= h->t_part_floats &&
+               static_cast<size_t>(gx) * gy <= h->t_nctr)
+            KS *= 2;
+    }
+    g.KS = KS;
+    g.part = h->t_part;
+    g.ctr = h->t_ctr;
+    const dim3 grid(gx, gy, KS), block(T::kThreadsT);
+    switch (RT) {
+        case 1: hipLaunchKernelGGL((T::k_gemm<WT, 1, SRC, EPI>), grid, block, 0, stream, g); break;
+        case 2: hipLaunchKernelGGL((T::k_gemm<WT, 2, SRC, EPI>), grid, block, 0, stream, g); break;
+        default: hipLaunchKernelGGL((T::k_gemm<WT, 4, SRC, EPI>), grid, block, 0, stream, g); break;
+    }
+}
+
 template <int WT>
-qp_status launch_frame(qp_handle* h, const RunArgs& a, hipStream_t stream, bool stepwise, bool generic) {
+qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
+    namespace T = qp::tiled;
     qp_status st = QP_OK;
     const Model& m = h->m;
+    const int B = a.B, qd = m.nq * m.hd;
+    const int nb = B < 1024 ? B : 1024;
+    hipLaunchKernelGGL(T::k_start, dim3(nb), dim3(T::kThreadsT), 0, stream, m, a);
+    T::GemmArgs g{};
+    g.eps = m.eps;
+    // x[position 0] = W_p . H + b_p
+    g.a = a.H;
+    g.lda = m.dT;
+    g.M = B;
+    g.N = m.dP;
+    g.K = m.dT;
+    g.w0 = h->t_proj;
+    g.out = m.x;
+    g.ldo = m.dP;
+    g.bias = m.proj_b;
+    tiled_gemm<WT, T::SRC_F32, T::EPI_BIAS>(h, g, stream);
+    for (int s = 1; s <= kSteps; ++s) {
+        const int M = s == 1 ? 2 * B : B;
+        for (int l = 0; l < m.L; ++l) {
+            const LayerDev& L = h->layers_host[l];
+            g = T::GemmArgs{};
+            g.eps = m.eps;
+            g.M = M;
+            // q, k, v = W_qkv . RMSNorm(x)
+            g.a = m.x;
+            g.lda = m.dP;
+            g.gain = L.attn_norm;
+            g.N = m.nqkv;
+            g.K = m.dP;
+            g.w0 = h->t_qkv[l];
+            g.out = m.qkv;
+            g.ldo = m.nqkv;
+            tiled_gemm<WT, T::SRC_F32_NORM, T::EPI_SCALE>(h, g, stream);
+            // attention
+            uint16_t* ao = reinterpret_cast<uint16_t*>(m.ao);
+            const dim3 ag(B * m.nkv);
+            switch (m.hd) {
+                case 64: hipLaunchKernelGGL(T::k_attn<64>, ag, dim3(T::kThreadsT), 0, stream, m, B, s, l, ao); break;
+                case 128: hipLaunchKernelGGL(T::k_attn<128>, ag, dim3(T::kThreadsT), 0, stream, m, B, s, l, ao); break;
+                default: hipLaunchKernelGGL(T::k_attn<256>, ag, dim3(T::kThreadsT), 0, stream, m, B, s, l, ao); break;
+            }
+            // x += W_o . attention
+            g.a = ao;
+            g.lda = qd;
+            g.gain = nullptr;
+            g.N = m.dP;
+            g.K = qd;
+            g.w0 = h->t_o[l];
+            g.out = m.x;
+            g.ldo = m.dP;
+            tiled_gemm<WT, T::SRC_BF16, T::EPI_RESID>(h, g, stream);
+            // h = silu(W_g . RMSNorm(x)) * (W_u . RMSNorm(x)), bf16
+            g.a = m.x;
+            g.lda = m.dP;
+            g.gain = L.ffn_norm;
+            g.N = m.F;
+            g.K = m.dP;
+            g.w0 = h->t_gate[l];
+            g.w1 = h->t_up[l];
+            g.out = nullptr;
+            g.outb = reinterpret_cast<uint16_t*>(m.hb);
+            tiled_gemm<WT, T::SRC_F32_NORM, T::EPI_SWIGLU>(h, g, stream);
+            // x += W_d . h (and the residual tap)
+            g.a = m.hb;
+            g.lda = m.F;
+            g.gain = nullptr;
+            g.N = m.dP;
+            g.K = m.F;
+            g.w0 = h->t_down[l];
+            g.w1 = T::FMat{};
+            g.outb = nullptr;
+            g.out = m.x;
+            g.ldo = m.dP;
+            g.taps = a.taps;
+            g.tap_s = s;
+            g.tap_l = l;
+            g.tap_L = m.L;
+            g.tap_B = B;
+            tiled_gemm<WT, T::SRC_BF16, T::EPI_RESID>(h, g, stream);
+        }
+        // lm_head[s-1] . RMSNorm(x at position s) -> per-tile argmax keys
+        g = T::GemmArgs{};
+        g.eps = m.eps;
+        g.a = m.x + (s == 1 ? static_cast<size_t>(B) * m.dP : 0);
+        g.lda = m.dP;
+        g.gain = m.out_norm;
+        g.M = B;
+        g.N = m.V;
+        g.K = m.dP;
+        g.w0 = h->t_lm[s - 1];
+        g.keys = h->t_keys;
+        if (a.logits_out) {
+            g.logits = a.logits_out + static_cast<size_t>(s - 1) * m.V;
+            g.logit_ld = static_cast<size_t>(kSteps) * m.V;
+        }
+        tiled_gemm<WT, T::SRC_F32_NORM, T::EPI_ARGMAX>(h, g, stream);
+        hipLaunchKernelGGL(T::k_next, dim3(nb), dim3(T::kThreadsT), 0, stream, m, a, s,
+                           static_cast<const unsigned long long*>(h->t_keys), m.V / 32);
+    }
+    if (!check_hip(hipGetLastError(), "batched path kernel launch", &st)) return st;
+    return QP_OK;
+}
+
+template <int WT>
+qp_status launch_frame(qp_handle* h, const RunArgs& a, hipStream_t stream, bool stepwise, bool generic, bool tiled) {
+    qp_status st = QP_OK;
+    const Model& m = h->m;
+    if constexpr (WT == WT_BF16 || WT == WT_Q8) {
+        if (tiled || (!stepwise && !generic && h->tiled_ok && a.B > 2)) return launch_tiled<WT>(h, a, stream);
+    }
     if constexpr (WT == WT_BF16) {
         if (!stepwise && !generic && h->stream_ok && a.B <= 2) {
             RunArgs ra = a;
@@ -469,7 +658,16 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
 
     Uploader up{h};
     const int wt = m.wt;
-    m.proj = up.one(w->proj_w, m.dP, m.dT, wt);
+    // batched matrix-core path: bf16 or Q8_0 weights whose widths tile into
+    // 32 x 256 blocks (every K split four ways into whole 32-wide blocks,
+    // two at a time; every N a whole number of 32-column tiles)
+    h->tiled_ok = (wt == WT_BF16 || wt == WT_Q8) && m.dT % 256 == 0 && m.dP % 256 == 0 &&
+                  (m.nq * m.hd) % 256 == 0 && m.F % 256 == 0 && m.nqkv % 32 == 0 && m.V % 32 == 0;
+    {
+        const Uploader::HostMat hm = Uploader::build({w->proj_w}, {m.dP}, m.dT, wt);
+        m.proj = up.rowmajor(hm);
+        if (h->tiled_ok) h->t_proj = up.fragments(hm);
+    }
     m.proj_b = static_cast<const float*>(up.upload(w->proj_b, sizeof(float) * m.dP));
     const size_t tab = static_cast<size_t>(m.V) * m.dT;
     if (g->emb_format == QP_EMB_EMA) {
@@ -502,11 +700,23 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
     for (int l = 0; l < m.L && up.st == QP_OK; ++l) {
         const qp_layer_weights& lw = w->layers[l];
         LayerDev& d = layers[l];
-        d.qkv = up.stack({lw.wq, lw.wk, lw.wv}, {qd, kd, kd}, m.dP, wt);
-        d.o = up.one(lw.wo, m.dP, qd, wt);
-        d.gate = up.one(lw.w_gate, m.F, m.dP, wt);
-        d.up = up.one(lw.w_up, m.F, m.dP, wt);
-        d.down = up.one(lw.w_down, m.dP, m.F, wt);
+        const Uploader::HostMat hq = Uploader::build({lw.wq, lw.wk, lw.wv}, {qd, kd, kd}, m.dP, wt);
+        const Uploader::HostMat ho = Uploader::build({lw.wo}, {m.dP}, qd, wt);
+        const Uploader::HostMat hg = Uploader::build({lw.w_gate}, {m.F}, m.dP, wt);
+        const Uploader::HostMat hu = Uploader::build({lw.w_up}, {m.F}, m.dP, wt);
+        const Uploader::HostMat hd = Uploader::build({lw.w_down}, {m.dP}, m.F, wt);
+        d.qkv = up.rowmajor(hq);
+        d.o = up.rowmajor(ho);
+        d.gate = up.rowmajor(hg);
+        d.up = up.rowmajor(hu);
+        d.down = up.rowmajor(hd);
+        if (h->tiled_ok) {
+            h->t_qkv.push_back(up.fragments(hq));
+            h->t_o.push_back(up.fragments(ho));
+            h->t_gate.push_back(up.fragments(hg));
+            h->t_up.push_back(up.fragments(hu));
+            h->t_down.push_back(up.fragments(hd));
+        }
         d.attn_norm = static_cast<const float*>(up.upload(lw.attn_norm, sizeof(float) * m.dP));
         d.q_norm = static_cast<const float*>(up.upload(lw.q_norm, sizeof(float) * m.hd));
         d.k_norm = static_cast<const float*>(up.upload(lw.k_norm, sizeof(float) * m.hd));
@@ -514,7 +724,12 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
     }
     m.layers = static_cast<const LayerDev*>(up.upload(layers.data(), sizeof(LayerDev) * (layers.empty() ? 1 : layers.size())));
     m.out_norm = static_cast<const float*>(up.upload(w->out_norm, sizeof(float) * m.dP));
-    for (int k = 0; k < kSteps; ++k) m.lm[k] = up.one(w->lm_head[k], m.V, m.dP, wt);
+    for (int k = 0; k < kSteps && up.st == QP_OK; ++k) {
+        const Uploader::HostMat hl = Uploader::build({w->lm_head[k]}, {m.V}, m.dP, wt);
+        m.lm[k] = up.rowmajor(hl);
+        if (h->tiled_ok) h->t_lm[k] = up.fragments(hl);
+    }
+    h->layers_host = layers;
 
     // RoPE table, fp64 then rounded: angle(p, i) = p * base^(-2i/hd)
     const int half = m.hd / 2;
@@ -542,6 +757,17 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
     m.bar = static_cast<unsigned long long*>(up.alloc(4096));
     float* ptab = static_cast<float*>(up.alloc(static_cast<size_t>(kSteps) * m.V * m.dP * 4));
     m.ptab = ptab;
+    if (h->tiled_ok) {
+        // argmax keys of the lm_head tiles; split-K partial tiles and counters
+        // for the products with N = dP (split K only when M <= 2 * max_batch
+        // rows leave fewer than 256 tiles)
+        h->t_keys = static_cast<unsigned long long*>(up.alloc(static_cast<size_t>(m.max_batch) * (m.V / 32) * 8));
+        const size_t row_tiles = (rows + 15) / 16 + 3;
+        h->t_part_floats = static_cast<size_t>(qp::tiled::kMaxKS) * (m.dP / 32) * row_tiles * 2 * 256;
+        h->t_part = static_cast<float*>(up.alloc(h->t_part_floats * 4));
+        h->t_nctr = static_cast<size_t>(m.dP / 32) * row_tiles;
+        h->t_ctr = static_cast<unsigned*>(up.alloc(h->t_nctr * 4));
+    }
 
     // records of the dataflow kernel (1.7B geometry, bf16 weights, B <= 2)
     {
@@ -574,7 +800,8 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
     }
     if (!check_hip(hipMemset(m.amax, 0, static_cast<size_t>(m.max_batch) * 8), "hipMemset", &st) ||
         !check_hip(hipMemset(m.err, 0, 256), "hipMemset", &st) ||
-        !check_hip(hipMemset(m.bar, 0, 4096), "hipMemset", &st)) {
+        !check_hip(hipMemset(m.bar, 0, 4096), "hipMemset", &st) ||
+        (h->tiled_ok && !check_hip(hipMemset(h->t_ctr, 0, h->t_nctr * 4), "hipMemset", &st))) {
         free_all(h);
         delete h;
         return st;
@@ -597,7 +824,13 @@ qp_status qp_run_frames_ex(qp_handle* h, int32_t B, const float* H, const int32_
     if (!h) return fail(QP_ERR_INVALID_ARG, "handle is NULL");
     if (B < 0 || B > h->m.max_batch)
         return fail(QP_ERR_BATCH, "B=" + std::to_string(B) + " outside [0, " + std::to_string(h->m.max_batch) + "]");
-    if (flags & ~(QP_FLAG_STEPWISE | QP_FLAG_GENERIC)) return fail(QP_ERR_INVALID_ARG, "unknown flag bits");
+    if (flags & ~(QP_FLAG_STEPWISE | QP_FLAG_GENERIC | QP_FLAG_TILED))
+        return fail(QP_ERR_INVALID_ARG, "unknown flag bits");
+    const bool tiled = (flags & QP_FLAG_TILED) != 0;
+    if (tiled && (flags & (QP_FLAG_STEPWISE | QP_FLAG_GENERIC)))
+        return fail(QP_ERR_INVALID_ARG, "QP_FLAG_TILED excludes the other driver flags");
+    if (tiled && !h->tiled_ok)
+        return fail(QP_ERR_INVALID_ARG, "the batched matrix-core path does not support this geometry or weight dtype");
     if (B == 0) return QP_OK;
     if (!H || !q0 || !tokens_out || !embsum_out) return fail(QP_ERR_INVALID_ARG, "NULL input or output pointer");
     DeviceGuard guard(h->device);
@@ -614,9 +847,9 @@ qp_status qp_run_frames_ex(qp_handle* h, int32_t B, const float* H, const int32_
     const bool stepwise = (flags & QP_FLAG_STEPWISE) != 0;
     const bool generic = (flags & QP_FLAG_GENERIC) != 0;
     switch (h->m.wt) {
-        case WT_F32: return launch_frame<WT_F32>(h, a, s, stepwise, generic);
-        case WT_BF16: return launch_frame<WT_BF16>(h, a, s, stepwise, generic);
-        default: return launch_frame<WT_Q8>(h, a, s, stepwise, generic);
+        case WT_F32: return launch_frame<WT_F32>(h, a, s, stepwise, generic, false);
+        case WT_BF16: return launch_frame<WT_BF16>(h, a, s, stepwise, generic, tiled);
+        default: return launch_frame<WT_Q8>(h, a, s, stepwise, generic, tiled);
     }
 }
 

@@ -96,6 +96,24 @@ WORKLOADS: Dict[str, Workload] = {
         batch=64, frames=64, weight_seed=1005, input_seed=2005,
         description="1.7B-shaped predictor, Q8_0 linears + EMA codebooks, "
                     "B=64 x 64 frames"),
+    # small parity cases for the bf16 / Q8_0 paths (the tiny geometry with the
+    # 1.7B configurations' storage formats)
+    "tiny_bf16": Workload(
+        "tiny_bf16",
+        Geometry(d_talker=512, d_model=256, n_layers=2, n_q_heads=4,
+                 n_kv_heads=2, head_dim=64, d_ffn=768, vocab=256,
+                 rms_eps=1e-6, rope_base=1e4, weight_dtype="bf16",
+                 emb_format="bf16"),
+        batch=20, frames=4, weight_seed=1101, input_seed=2101,
+        description="tiny predictor, bf16 weights and tables, B=20 x 4 frames"),
+    "tiny_q8ema": Workload(
+        "tiny_q8ema",
+        Geometry(d_talker=512, d_model=256, n_layers=2, n_q_heads=4,
+                 n_kv_heads=2, head_dim=64, d_ffn=768, vocab=256,
+                 rms_eps=1e-6, rope_base=1e4, weight_dtype="q8_0",
+                 emb_format="ema"),
+        batch=20, frames=4, weight_seed=1102, input_seed=2102,
+        description="tiny predictor, Q8_0 linears + EMA codebooks, B=20 x 4 frames"),
 }
 
 

@@ -39,12 +39,12 @@ def workload(name):
         wl = synth.WORKLOADS[name]
         W = synth.make_weights(wl.geom, wl.weight_seed)
         model = O.OracleModel(W, wl.geom)
-        pred = bd.Predictor(W, wl.geom, max_batch=max(wl.batch, 8))
+        pred = bd.Predictor(W, wl.geom, max_batch=max(wl.batch, 40))
         _cache[name] = (wl, W, model, pred)
     return _cache[name]
 
 
-def gpu_frame(pred, H, q0, force=None, logits=True, taps=False, stepwise=False, generic=False):
+def gpu_frame(pred, H, q0, force=None, logits=True, taps=False, stepwise=False, generic=False, tiled=False):
     dev = _dev()
     g = pred.geom
     B = H.shape[0]
@@ -56,7 +56,8 @@ def gpu_frame(pred, H, q0, force=None, logits=True, taps=False, stepwise=False, 
     lg = torch.full((B, 15, g.vocab), float("nan"), dtype=torch.float32, device=dev) if logits else None
     tp = (torch.full((16, g.n_layers, B, g.d_model), float("nan"), dtype=torch.float32, device=dev)
           if taps else None)
-    pred.run(Ht, qt, tok, emb, force=ft, logits_out=lg, taps_out=tp, stepwise=stepwise, generic=generic)
+    pred.run(Ht, qt, tok, emb, force=ft, logits_out=lg, taps_out=tp, stepwise=stepwise, generic=generic,
+             tiled=tiled)
     torch.cuda.synchronize()
     assert pred.get_error() == 0
     out = {"tokens": tok.cpu().numpy(), "embsum": emb.cpu().numpy()}
@@ -67,13 +68,13 @@ def gpu_frame(pred, H, q0, force=None, logits=True, taps=False, stepwise=False, 
     return out
 
 
-def check_against_oracle(name, model, pred, H, q0, rows, stepwise=False):
+def check_against_oracle(name, model, pred, H, q0, rows, stepwise=False, tiled=False):
     """Teacher-forced comparison of the sampled ``rows`` of one frame."""
     tol = TOL[model.g.weight_dtype]
     ref = O.run_frames(model, H[rows], q0[rows])
     force = np.zeros((H.shape[0], 15), dtype=np.int32)
     force[rows] = ref["tokens"]
-    got = gpu_frame(pred, H, q0, force=force, stepwise=stepwise)
+    got = gpu_frame(pred, H, q0, force=force, stepwise=stepwise, tiled=tiled)
     lg_err = np.abs(got["logits"][rows] - ref["logits"]).max()
     em_err = np.abs(got["embsum"][rows] - ref["embsum"]).max()
     sure = ref["margin"] > MARGIN
@@ -166,6 +167,14 @@ def test_edge_cases_and_flags():
     fixed[1] = 0
     ref = gpu_frame(pred, H[0], fixed)
     np.testing.assert_array_equal(tok.cpu().numpy(), ref["tokens"])
+    # the batched matrix-core path takes bf16 / Q8_0 weights only, alone
+    with pytest.raises(bd.QpError) as ei:
+        gpu_frame(pred, H[0], q0[0], tiled=True)
+    assert ei.value.status == bd.QP_ERR_INVALID_ARG
+    _, _, _, pb = workload("tiny_bf16")
+    with pytest.raises(bd.QpError) as ei:
+        gpu_frame(pb, H[0], q0[0], tiled=True, generic=True)
+    assert ei.value.status == bd.QP_ERR_INVALID_ARG
 
 
 # ----------------------------------------------------------------------------
@@ -214,3 +223,56 @@ def test_dataflow_kernel_taps_and_repeat():
     again = gpu_frame(pred, H[0], q0[0], force=ref["tokens"].astype(np.int32), taps=True)
     for key in ("tokens", "logits", "embsum", "taps"):
         np.testing.assert_array_equal(again[key], got[key])
+
+
+# ----------------------------------------------------------------------------
+# the batched matrix-core path (bf16 / Q8_0 weights, any B)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny_bf16", "tiny_q8ema"])
+def test_tiled_tiny_all_frames(name):
+    wl, W, model, pred = workload(name)
+    H, q0 = synth.make_inputs(wl.geom, wl.batch, wl.frames, wl.input_seed)
+    rows = np.arange(wl.batch)
+    for f in range(wl.frames):
+        check_against_oracle(name, model, pred, H[f], q0[f], rows, tiled=True)
+
+
+@pytest.mark.parametrize("B", [1, 2, 3, 16, 17, 37])
+def test_tiled_batch_sizes(B):
+    """Row tiles of 16/32/64 with ragged tails, split-K on and off."""
+    wl, W, model, pred = workload("tiny_bf16")
+    H, q0 = synth.make_inputs(wl.geom, B, 1, 3100 + B)
+    check_against_oracle(f"tiled B={B}", model, pred, H[0], q0[0], np.arange(B), tiled=True)
+
+
+def test_tiled_taps_composition_and_repeat():
+    wl, W, model, pred = workload("tiny_q8ema")
+    H, q0 = synth.make_inputs(wl.geom, 12, 1, 3333)
+    ref = O.run_frames(model, H[0], q0[0], want_taps=True)
+    force = ref["tokens"].astype(np.int32)
+    got = gpu_frame(pred, H[0], q0[0], force=force, taps=True, tiled=True)
+    err = np.abs(got["taps"] - ref["taps"]).max()
+    print(f"[tiled taps] max-abs {err:.3g}")
+    assert err <= TOL["q8_0"]
+    again = gpu_frame(pred, H[0], q0[0], force=force, taps=True, tiled=True)
+    for key in ("tokens", "logits", "embsum", "taps"):
+        np.testing.assert_array_equal(again[key], got[key])
+    # a permutation of the same batch (same tiling) reproduces each row bitwise
+    perm = np.random.default_rng(5).permutation(12)
+    sub = gpu_frame(pred, H[0][perm], q0[0][perm], force=force[perm], tiled=True)
+    for key in ("tokens", "logits", "embsum"):
+        np.testing.assert_array_equal(sub[key], got[key][perm])
+
+
+def test_tiled_against_dataflow_b2():
+    wl, W, model, pred = workload("b16")
+    H, q0 = synth.make_inputs(wl.geom, 2, 1, 5151)
+    ref = O.run_frames(model, H[0], q0[0])
+    force = ref["tokens"].astype(np.int32)
+    a = gpu_frame(pred, H[0], q0[0], force=force)
+    b = gpu_frame(pred, H[0], q0[0], force=force, tiled=True)
+    lg = np.abs(a["logits"] - b["logits"]).max()
+    print(f"[tiled vs dataflow B=2] logits max-abs {lg:.3g}")
+    assert lg <= TOL["bf16"]
+    assert np.abs(a["embsum"] - b["embsum"]).max() <= TOL["bf16"]
