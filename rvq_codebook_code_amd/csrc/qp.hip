@@ -188,6 +188,8 @@ struct qp_handle {
     size_t t_part_floats = 0;
     unsigned* t_ctr = nullptr;              // split-K tile counters
     size_t t_nctr = 0;
+    uint16_t* t_xg = nullptr;               // [2*max_batch][dP] bf16(g_next * x)
+    float* t_ss = nullptr;                  // [2*max_batch][dP/32] tile sums of x^2
 };
 
 namespace {
@@ -411,16 +413,24 @@ void tiled_gemm(const qp_handle* h, qp::tiled::GemmArgs g, hipStream_t stream) {
     const int gx = EPI == T::EPI_SWIGLU ? g.N / 16 : g.N / 32;
     const int RT = g.M <= 16 ? 1 : (g.M <= 32 ? 2 : 4);
     const int gy = (g.M + 16 * RT - 1) / (16 * RT);
-    // products with few output tiles also split K over workgroups
+    // Products with few output tiles (the N = dP ones) and more than one row
+    // tile also split K over workgroups: the smallest split (into whole pairs
+    // of 32-wide blocks per wave, at most 4) that fills 256 workgroups.  With
+    // a single row tile the ordered fixup costs more than it saves.
+    const int tiles = gx * gy;
     int KS = 1;
-    if (SRC != T::SRC_F32_NORM && EPI != T::EPI_SWIGLU && EPI != T::EPI_ARGMAX) {
-        while (KS < T::kMaxKS && gx * gy * KS < 256 && g.K % (256 * KS * 2) == 0 &&
-               static_cast<size_t>(KS * 2) * gx * gy * RT * T::kCT * 256 <= h->t_part_floats &&
-               static_cast<size_t>(gx) * gy <= h->t_nctr)
-            KS *= 2;
+    if ((EPI == T::EPI_RESID || EPI == T::EPI_BIAS) && RT > 1 && tiles < 256 &&
+        static_cast<size_t>(tiles) <= h->t_nctr) {
+        for (int c = 2; c <= T::kMaxKS; ++c) {
+            if ((g.K / 256) % c != 0) continue;
+            if (static_cast<size_t>(c) * tiles * RT * T::kCT * 256 > h->t_part_floats) break;
+            KS = c;
+            if (c * tiles >= 256) break;
+        }
     }
     g.KS = KS;
     g.part = h->t_part;
+    g.part_bytes = static_cast<uint32_t>(h->t_part_floats * 4);
     g.ctr = h->t_ctr;
     const dim3 grid(gx, gy, KS), block(T::kThreadsT);
     switch (RT) {
@@ -435,9 +445,11 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
     namespace T = qp::tiled;
     qp_status st = QP_OK;
     const Model& m = h->m;
-    const int B = a.B, qd = m.nq * m.hd;
+    const int B = a.B, qd = m.nq * m.hd, nss = m.dP / 32;
     const int nb = B < 1024 ? B : 1024;
-    hipLaunchKernelGGL(T::k_start, dim3(nb), dim3(T::kThreadsT), 0, stream, m, a);
+    // the gain of the first reader of a position's input row
+    const float* gain0 = m.L > 0 ? h->layers_host[0].attn_norm : m.out_norm;
+    hipLaunchKernelGGL(T::k_start, dim3(nb), dim3(T::kThreadsT), 0, stream, m, a, gain0, h->t_xg, h->t_ss);
     T::GemmArgs g{};
     g.eps = m.eps;
     // x[position 0] = W_p . H + b_p
@@ -450,64 +462,81 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
     g.out = m.x;
     g.ldo = m.dP;
     g.bias = m.proj_b;
+    g.xg = h->t_xg;
+    g.g_next = gain0;
+    g.ss_out = h->t_ss;
     tiled_gemm<WT, T::SRC_F32, T::EPI_BIAS>(h, g, stream);
+    uint16_t* ao = reinterpret_cast<uint16_t*>(m.ao);
+    uint16_t* hb = reinterpret_cast<uint16_t*>(m.hb);
     for (int s = 1; s <= kSteps; ++s) {
         const int M = s == 1 ? 2 * B : B;
         for (int l = 0; l < m.L; ++l) {
             const LayerDev& L = h->layers_host[l];
+            const float* g_after = l + 1 < m.L ? h->layers_host[l + 1].attn_norm : m.out_norm;
+            // q, k, v = W_qkv . RMSNorm(x)
             g = T::GemmArgs{};
             g.eps = m.eps;
             g.M = M;
-            // q, k, v = W_qkv . RMSNorm(x)
-            g.a = m.x;
+            g.a = h->t_xg;
             g.lda = m.dP;
-            g.gain = L.attn_norm;
+            g.ss_in = h->t_ss;
+            g.nss = nss;
             g.N = m.nqkv;
             g.K = m.dP;
             g.w0 = h->t_qkv[l];
             g.out = m.qkv;
             g.ldo = m.nqkv;
-            tiled_gemm<WT, T::SRC_F32_NORM, T::EPI_SCALE>(h, g, stream);
+            tiled_gemm<WT, T::SRC_BF16_NORM, T::EPI_SCALE>(h, g, stream);
             // attention
-            uint16_t* ao = reinterpret_cast<uint16_t*>(m.ao);
             const dim3 ag(B * m.nkv);
             switch (m.hd) {
                 case 64: hipLaunchKernelGGL(T::k_attn<64>, ag, dim3(T::kThreadsT), 0, stream, m, B, s, l, ao); break;
                 case 128: hipLaunchKernelGGL(T::k_attn<128>, ag, dim3(T::kThreadsT), 0, stream, m, B, s, l, ao); break;
                 default: hipLaunchKernelGGL(T::k_attn<256>, ag, dim3(T::kThreadsT), 0, stream, m, B, s, l, ao); break;
             }
-            // x += W_o . attention
+            // x += W_o . attention; publishes bf16(ffn_norm * x)
+            g = T::GemmArgs{};
+            g.eps = m.eps;
+            g.M = M;
             g.a = ao;
             g.lda = qd;
-            g.gain = nullptr;
             g.N = m.dP;
             g.K = qd;
             g.w0 = h->t_o[l];
             g.out = m.x;
             g.ldo = m.dP;
+            g.xg = h->t_xg;
+            g.g_next = L.ffn_norm;
+            g.ss_out = h->t_ss;
             tiled_gemm<WT, T::SRC_BF16, T::EPI_RESID>(h, g, stream);
             // h = silu(W_g . RMSNorm(x)) * (W_u . RMSNorm(x)), bf16
-            g.a = m.x;
+            g = T::GemmArgs{};
+            g.eps = m.eps;
+            g.M = M;
+            g.a = h->t_xg;
             g.lda = m.dP;
-            g.gain = L.ffn_norm;
+            g.ss_in = h->t_ss;
+            g.nss = nss;
             g.N = m.F;
             g.K = m.dP;
             g.w0 = h->t_gate[l];
             g.w1 = h->t_up[l];
-            g.out = nullptr;
-            g.outb = reinterpret_cast<uint16_t*>(m.hb);
-            tiled_gemm<WT, T::SRC_F32_NORM, T::EPI_SWIGLU>(h, g, stream);
-            // x += W_d . h (and the residual tap)
-            g.a = m.hb;
+            g.outb = hb;
+            tiled_gemm<WT, T::SRC_BF16_NORM, T::EPI_SWIGLU>(h, g, stream);
+            // x += W_d . h (and the residual tap); publishes the next reader's operand
+            g = T::GemmArgs{};
+            g.eps = m.eps;
+            g.M = M;
+            g.a = hb;
             g.lda = m.F;
-            g.gain = nullptr;
             g.N = m.dP;
             g.K = m.F;
             g.w0 = h->t_down[l];
-            g.w1 = T::FMat{};
-            g.outb = nullptr;
             g.out = m.x;
             g.ldo = m.dP;
+            g.xg = h->t_xg;
+            g.g_next = g_after;
+            g.ss_out = h->t_ss;
             g.taps = a.taps;
             g.tap_s = s;
             g.tap_l = l;
@@ -516,11 +545,13 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
             tiled_gemm<WT, T::SRC_BF16, T::EPI_RESID>(h, g, stream);
         }
         // lm_head[s-1] . RMSNorm(x at position s) -> per-tile argmax keys
+        const size_t row0 = s == 1 ? static_cast<size_t>(B) : 0;
         g = T::GemmArgs{};
         g.eps = m.eps;
-        g.a = m.x + (s == 1 ? static_cast<size_t>(B) * m.dP : 0);
+        g.a = h->t_xg + row0 * m.dP;
         g.lda = m.dP;
-        g.gain = m.out_norm;
+        g.ss_in = h->t_ss + row0 * nss;
+        g.nss = nss;
         g.M = B;
         g.N = m.V;
         g.K = m.dP;
@@ -530,9 +561,9 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
             g.logits = a.logits_out + static_cast<size_t>(s - 1) * m.V;
             g.logit_ld = static_cast<size_t>(kSteps) * m.V;
         }
-        tiled_gemm<WT, T::SRC_F32_NORM, T::EPI_ARGMAX>(h, g, stream);
+        tiled_gemm<WT, T::SRC_BF16_NORM, T::EPI_ARGMAX>(h, g, stream);
         hipLaunchKernelGGL(T::k_next, dim3(nb), dim3(T::kThreadsT), 0, stream, m, a, s,
-                           static_cast<const unsigned long long*>(h->t_keys), m.V / 32);
+                           static_cast<const unsigned long long*>(h->t_keys), m.V / 32, gain0, h->t_xg, h->t_ss);
     }
     if (!check_hip(hipGetLastError(), "batched path kernel launch", &st)) return st;
     return QP_OK;
@@ -661,7 +692,7 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
     // batched matrix-core path: bf16 or Q8_0 weights whose widths tile into
     // 32 x 256 blocks (every K split four ways into whole 32-wide blocks,
     // two at a time; every N a whole number of 32-column tiles)
-    h->tiled_ok = (wt == WT_BF16 || wt == WT_Q8) && m.dT % 256 == 0 && m.dP % 256 == 0 &&
+    h->tiled_ok = (wt == WT_BF16 || wt == WT_Q8) && m.dT % 256 == 0 && m.dP % 256 == 0 && m.dP <= 4096 &&
                   (m.nq * m.hd) % 256 == 0 && m.F % 256 == 0 && m.nqkv % 32 == 0 && m.V % 32 == 0;
     {
         const Uploader::HostMat hm = Uploader::build({w->proj_w}, {m.dP}, m.dT, wt);
@@ -762,11 +793,14 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
         // for the products with N = dP (split K only when M <= 2 * max_batch
         // rows leave fewer than 256 tiles)
         h->t_keys = static_cast<unsigned long long*>(up.alloc(static_cast<size_t>(m.max_batch) * (m.V / 32) * 8));
-        const size_t row_tiles = (rows + 15) / 16 + 3;
-        h->t_part_floats = static_cast<size_t>(qp::tiled::kMaxKS) * (m.dP / 32) * row_tiles * 2 * 256;
+        // K is split only while tiles * KS < 2 * 256, so 512 partial tiles
+        // of up to 4 row fragments x 2 column fragments suffice
+        h->t_part_floats = 512ull * 4 * 2 * 256;
         h->t_part = static_cast<float*>(up.alloc(h->t_part_floats * 4));
-        h->t_nctr = static_cast<size_t>(m.dP / 32) * row_tiles;
+        h->t_nctr = 256;  // split K only applies below 256 tiles
         h->t_ctr = static_cast<unsigned*>(up.alloc(h->t_nctr * 4));
+        h->t_xg = static_cast<uint16_t*>(up.alloc(rows * m.dP * 2));
+        h->t_ss = static_cast<float*>(up.alloc(rows * (m.dP / 32) * 4));
     }
 
     // records of the dataflow kernel (1.7B geometry, bf16 weights, B <= 2)

@@ -17,8 +17,12 @@
 //    weight load is one contiguous 1 KiB (or 512 B) read.
 //  * Activations enter as bf16.  RMSNorm is applied as
 //      W . (g * x / rms(x)) = (W . bf16(g * x)) / rms(x)
-//    with rms taken from the fp32 rows while they are loaded, so the gain
-//    rides on the activation operand and the row scale on the output.
+//    Whoever writes a residual-stream row also writes bf16(g * x) with the
+//    gain of the row's next reader (ffn_norm after the output projection,
+//    the next layer's attn_norm or out_norm after the MLP) and the row's sums
+//    of x^2 over 32-column tiles; the reader's epilogue adds those sums up
+//    (in tile order) for the row scale.  The operand is then a plain bf16
+//    load, and the gain rides on it while the row scale rides on the output.
 //  * Q8_0 codes are integers in [-128, 127], exact in bf16; one MFMA covers
 //    exactly one 32-wide quantisation block, whose f16 scale (stored as fp32)
 //    multiplies the block's partial sum before accumulation.  The weights
@@ -35,6 +39,8 @@
 #include "qp_common.h"
 #include "qp_phases.h"
 
+#include <type_traits>
+
 namespace qp {
 namespace tiled {
 
@@ -44,7 +50,6 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreadsT = 256;
 constexpr int kCT = 2;        // output fragments (16 columns each) per workgroup
-constexpr int kU = 2;         // k-blocks per load batch
 constexpr int kMaxKS = 4;     // largest split of K across workgroups
 
 // A weight matrix [N][K] in fragment order (see the file comment).
@@ -53,26 +58,36 @@ struct FMat {
     const float* scale;   // Q8_0: [N/16][K/32][16]; bf16: null
 };
 
-enum Src : int { SRC_F32 = 0, SRC_F32_NORM = 1, SRC_BF16 = 2 };
+enum Src : int { SRC_F32 = 0, SRC_BF16 = 1, SRC_BF16_NORM = 2 };
 enum Epi : int { EPI_BIAS = 0, EPI_SCALE = 1, EPI_RESID = 2, EPI_SWIGLU = 3, EPI_ARGMAX = 4 };
 
 struct GemmArgs {
-    const void* a;          // A operand rows [M][lda] (fp32 or bf16 elements)
+    const void* a;          // A operand rows [M][lda]: fp32 (SRC_F32) or bf16
     int lda;
-    const float* gain;      // [K] RMSNorm gain (SRC_F32_NORM)
-    float eps;
     int M, N, K, KS;        // N = output columns (for SwiGLU: F)
     FMat w0, w1;            // w1: the up matrix of SwiGLU
-    float* out;             // fp32 output rows [M][ldo] (BIAS, SCALE, RESID)
+    // RMSNorm of the A rows (SRC_BF16_NORM): the rows are already g * x in
+    // bf16; rms(x) comes from nss partial sums of squares per row
+    const float* ss_in;     // [M][nss]
+    int nss;
+    float eps;
+    // epilogue outputs
+    float* out;             // fp32 rows [M][ldo] (BIAS, SCALE, RESID)
     int ldo;
-    uint16_t* outb;         // bf16 output rows [M][N] (SWIGLU)
+    uint16_t* outb;         // bf16 rows [M][N] (SWIGLU)
     const float* bias;      // [N] (BIAS)
+    // BIAS / RESID also publish the next consumer's operand and row sums:
+    // xg = bf16(g_next * x) [M][ldo], ss_out[m][tile] = sum over the tile's 32 columns of x^2
+    uint16_t* xg;
+    const float* g_next;
+    float* ss_out;
     unsigned long long* keys;  // [M][gridDim.x] per-tile argmax keys (ARGMAX)
     float* logits;          // row m's logits at logits + m * logit_ld (ARGMAX, optional)
     size_t logit_ld;
     float* taps;            // residual taps [16][L][B][dP] (RESID of the down projection, optional)
     int tap_s, tap_l, tap_L, tap_B;
     float* part;            // split-K partial tiles
+    uint32_t part_bytes;
     unsigned* ctr;          // split-K arrival counters, one per tile, left at 0
 };
 
@@ -100,15 +115,25 @@ __device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
     return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
+// sum over the 16 lanes of a row group (lanes with equal lane / 16), fixed order
+__device__ __forceinline__ float sum16(float v) {
+    v += __shfl_xor(v, 1, 64);
+    v += __shfl_xor(v, 2, 64);
+    v += __shfl_xor(v, 4, 64);
+    v += __shfl_xor(v, 8, 64);
+    return v;
+}
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kDevScope = 16;   // buffer cache policy: device-coherent (sc1)
+
 // ---------------------------------------------------------------------------
 // [M x K] . [K x N] with a fused prologue (SRC) and epilogue (EPI).
 // grid = (N / 32 (SwiGLU: N / 16), ceil(M / (16 RT)), KS), 256 threads.
 // ---------------------------------------------------------------------------
 template <int WT, int RT, int SRC, int EPI>
 __global__ __launch_bounds__(kThreadsT) void k_gemm(GemmArgs g) {
-    constexpr bool NORM = SRC == SRC_F32_NORM;
     __shared__ f32x4_t red[4][RT][kCT][64];
-    __shared__ float ssr[4][RT][16];
     __shared__ int last_s;
 
     const int lane = threadIdx.x & 63;
@@ -138,25 +163,40 @@ __global__ __launch_bounds__(kThreadsT) void k_gemm(GemmArgs g) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) rok[rt] = m0 + 16 * rt + arow < g.M;
 
-    f32x4_t acc[RT][kCT];
-    float ss[RT];
+    // RMSNorm row scales of the row tiles this wave finishes, fetched before
+    // the products: lane l sums a quarter of row (l % 16)'s tile sums, the
+    // quarters are then combined across the lane groups (fixed order)
+    float rss[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        ss[rt] = 0.f;
-#pragma unroll
-        for (int c = 0; c < kCT; ++c) acc[rt][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        rss[rt] = 0.f;
+        if constexpr (SRC == SRC_BF16_NORM) {
+            if ((rt & 3) == wave && rok[rt]) {
+                const int q = g.nss >> 2;
+                const float* sr = g.ss_in + static_cast<size_t>(m0 + 16 * rt + arow) * g.nss + (lane >> 4) * q;
+                for (int t = 0; t < q; t += 2) {   // q = nss / 4 is even (dP % 256 == 0)
+                    const float2 v = *reinterpret_cast<const float2*>(sr + t);
+                    rss[rt] += v.x + v.y;
+                }
+            }
+        }
     }
 
-    for (int kb = kb0; kb < kb0 + kbw; kb += kU) {
-        // ---- loads of kU k-blocks ----
-        uint4 av[kU][RT];
-        float4 af[kU][RT][2];
-        uint4 wv[kU][kCT];
-        uint2 wq[kU][kCT];
-        float ws[kU][kCT];
-        float4 gv[kU][2];
+    f32x4_t acc[RT][kCT];
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int c = 0; c < kCT; ++c) acc[rt][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // one batch of UU k-blocks: every load first, then the products
+    auto batch = [&](int kb, auto uu) {
+        constexpr int UU = decltype(uu)::value;
+        uint4 av[UU][RT];
+        uint4 wv[UU][kCT];
+        uint2 wq[UU][kCT];
+        float ws[UU][kCT];
+#pragma unroll
+        for (int u = 0; u < UU; ++u) {
             const int k = (kb + u) * 32 + akoff;
 #pragma unroll
             for (int c = 0; c < kCT; ++c) {
@@ -167,55 +207,26 @@ __global__ __launch_bounds__(kThreadsT) void k_gemm(GemmArgs g) {
                     wv[u][c] = *reinterpret_cast<const uint4*>(wp[c] + (static_cast<size_t>(kb + u) * 64 + lane) * 16);
                 }
             }
-            if constexpr (SRC == SRC_BF16) {
 #pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    const uint16_t* src = static_cast<const uint16_t*>(g.a) +
-                                          static_cast<size_t>(m0 + 16 * rt + arow) * g.lda + k;
-                    av[u][rt] = rok[rt] ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
-                }
-            } else {
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    const float* src = static_cast<const float*>(g.a) +
-                                       static_cast<size_t>(m0 + 16 * rt + arow) * g.lda + k;
+            for (int rt = 0; rt < RT; ++rt) {
+                const size_t row = static_cast<size_t>(m0 + 16 * rt + arow);
+                if constexpr (SRC == SRC_F32) {
+                    const float* src = static_cast<const float*>(g.a) + row * g.lda + k;
+                    float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
                     if (rok[rt]) {
-                        af[u][rt][0] = *reinterpret_cast<const float4*>(src);
-                        af[u][rt][1] = *reinterpret_cast<const float4*>(src + 4);
-                    } else {
-                        af[u][rt][0] = make_float4(0.f, 0.f, 0.f, 0.f);
-                        af[u][rt][1] = af[u][rt][0];
+                        x0 = *reinterpret_cast<const float4*>(src);
+                        x1 = *reinterpret_cast<const float4*>(src + 4);
                     }
-                }
-                if constexpr (NORM) {
-                    gv[u][0] = *reinterpret_cast<const float4*>(g.gain + k);
-                    gv[u][1] = *reinterpret_cast<const float4*>(g.gain + k + 4);
+                    av[u][rt] = make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w),
+                                           pack_bf16x2(x1.x, x1.y), pack_bf16x2(x1.z, x1.w));
+                } else {
+                    const uint16_t* src = static_cast<const uint16_t*>(g.a) + row * g.lda + k;
+                    av[u][rt] = rok[rt] ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
                 }
             }
         }
-        // ---- products ----
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            uint4 a8[RT];
-            if constexpr (SRC == SRC_BF16) {
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt) a8[rt] = av[u][rt];
-            } else {
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    const float4 x0 = af[u][rt][0], x1 = af[u][rt][1];
-                    if constexpr (NORM) {
-                        ss[rt] += x0.x * x0.x + x0.y * x0.y + x0.z * x0.z + x0.w * x0.w +
-                                  x1.x * x1.x + x1.y * x1.y + x1.z * x1.z + x1.w * x1.w;
-                        const float4 g0 = gv[u][0], g1 = gv[u][1];
-                        a8[rt] = make_uint4(pack_bf16x2(g0.x * x0.x, g0.y * x0.y), pack_bf16x2(g0.z * x0.z, g0.w * x0.w),
-                                            pack_bf16x2(g1.x * x1.x, g1.y * x1.y), pack_bf16x2(g1.z * x1.z, g1.w * x1.w));
-                    } else {
-                        a8[rt] = make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w),
-                                            pack_bf16x2(x1.x, x1.y), pack_bf16x2(x1.z, x1.w));
-                    }
-                }
-            }
+        for (int u = 0; u < UU; ++u) {
 #pragma unroll
             for (int c = 0; c < kCT; ++c) {
                 uint4 w8;
@@ -228,7 +239,7 @@ __global__ __launch_bounds__(kThreadsT) void k_gemm(GemmArgs g) {
                 const bf16x8_t wb = __builtin_bit_cast(bf16x8_t, w8);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
-                    const bf16x8_t ab = __builtin_bit_cast(bf16x8_t, a8[rt]);
+                    const bf16x8_t ab = __builtin_bit_cast(bf16x8_t, av[u][rt]);
                     if constexpr (WT == WT_Q8) {
                         const f32x4_t p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, wb, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
                         const float sc = ws[u][c];
@@ -240,20 +251,20 @@ __global__ __launch_bounds__(kThreadsT) void k_gemm(GemmArgs g) {
                 }
             }
         }
+    };
+    int kb = kb0;
+    const int kb1 = kb0 + kbw;
+    if constexpr (RT == 1) {
+        for (; kb + 8 <= kb1; kb += 8) batch(kb, std::integral_constant<int, 8>{});
     }
+    for (; kb + 4 <= kb1; kb += 4) batch(kb, std::integral_constant<int, 4>{});
+    for (; kb < kb1; kb += 2) batch(kb, std::integral_constant<int, 2>{});
 
     // ---- reduce the four waves' K ranges, in wave order ----
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int c = 0; c < kCT; ++c) red[wave][rt][c][lane] = acc[rt][c];
-        if constexpr (NORM) {
-            float v = ss[rt];
-            v += __shfl_xor(v, 16, 64);
-            v += __shfl_xor(v, 32, 64);
-            if (lane < 16) ssr[wave][rt][lane] = v;
-        }
-    }
     __syncthreads();
 
     // wave w finishes row tiles w, w+4, ...
@@ -272,19 +283,22 @@ __global__ __launch_bounds__(kThreadsT) void k_gemm(GemmArgs g) {
     }
 
     if (g.KS > 1) {
-        // split K across workgroups: publish this partial tile, the last
-        // arriver sums all of them in kz order
+        // split K across workgroups: publish this partial tile with
+        // device-coherent stores; the last arriver sums all of them in kz order
         const size_t tile = static_cast<size_t>(by) * gridDim.x + bx;
         const size_t tiles = static_cast<size_t>(gridDim.x) * gridDim.y;
+        const auto pr = __builtin_amdgcn_make_buffer_rsrc(g.part, static_cast<short>(0), static_cast<int>(g.part_bytes),
+                                                          0x00020000);
+        auto poff = [&](int z, int rt, int c) {
+            return static_cast<uint32_t>(((((static_cast<size_t>(z) * tiles + tile) * RT + rt) * kCT + c) * 64 + lane) * 16);
+        };
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             if ((rt & 3) != wave) continue;
 #pragma unroll
-            for (int c = 0; c < kCT; ++c) {
-                float* dst = g.part + ((((static_cast<size_t>(kz) * tiles + tile) * RT + rt) * kCT + c) * 64 + lane) * 4;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) st_act(dst + i, tot[rt][c][i]);
-            }
+            for (int c = 0; c < kCT; ++c)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, tot[rt][c]), pr, poff(kz, rt, c), 0u,
+                                                       kDevScope);
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -302,10 +316,8 @@ __global__ __launch_bounds__(kThreadsT) void k_gemm(GemmArgs g) {
 #pragma unroll
             for (int c = 0; c < kCT; ++c) {
                 f32x4_t t = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                for (int z = 0; z < g.KS; ++z) {
-                    const float* src = g.part + ((((static_cast<size_t>(z) * tiles + tile) * RT + rt) * kCT + c) * 64 + lane) * 4;
-                    t = f32x4_t{t[0] + ld_act(src), t[1] + ld_act(src + 1), t[2] + ld_act(src + 2), t[3] + ld_act(src + 3)};
-                }
+                for (int z = 0; z < g.KS; ++z)
+                    t += __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(pr, poff(z, rt, c), 0u, kDevScope));
                 tot[rt][c] = t;
             }
         }
@@ -316,11 +328,13 @@ __global__ __launch_bounds__(kThreadsT) void k_gemm(GemmArgs g) {
     for (int rt = 0; rt < RT; ++rt) {
         if ((rt & 3) != wave) continue;
         float rinv[4] = {1.f, 1.f, 1.f, 1.f};
-        if constexpr (NORM) {
+        if constexpr (SRC == SRC_BF16_NORM) {
+            float t = rss[rt];
+            t += __shfl_xor(t, 16, 64);
+            t += __shfl_xor(t, 32, 64);   // every lane: the sum for row lane % 16
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = 4 * (lane >> 4) + i;
-                const float sst = ((ssr[0][rt][r] + ssr[1][rt][r]) + ssr[2][rt][r]) + ssr[3][rt][r];
+                const float sst = __shfl(t, 4 * (lane >> 4) + i, 64);
                 rinv[i] = 1.0f / sqrtf(sst / static_cast<float>(g.K) + g.eps);
             }
         }
@@ -353,31 +367,88 @@ __global__ __launch_bounds__(kThreadsT) void k_gemm(GemmArgs g) {
                 const float gt = tot[rt][0][i] * rinv[i], ut = tot[rt][1][i] * rinv[i];
                 g.outb[static_cast<size_t>(m) * g.N + n] = to_bf16((gt / (1.0f + expf(-gt))) * ut);
             }
-        } else {
+        } else if constexpr (EPI == EPI_SCALE) {
 #pragma unroll
             for (int c = 0; c < kCT; ++c) {
                 const int n = nb[c] * 16 + (lane & 15);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int m = m0 + 16 * rt + 4 * (lane >> 4) + i;
+                    if (m < g.M) g.out[static_cast<size_t>(m) * g.ldo + n] = tot[rt][c][i] * rinv[i];
+                }
+            }
+        } else {
+            // residual stream rows: x (fp32), xg = bf16(g_next * x), and the
+            // sum of x^2 over this workgroup's 32 columns
+            float sq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < kCT; ++c) {
+                const int n = nb[c] * 16 + (lane & 15);
+                const float gn = g.g_next[n];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int m = m0 + 16 * rt + 4 * (lane >> 4) + i;
                     if (m >= g.M) continue;
                     float* o = g.out + static_cast<size_t>(m) * g.ldo + n;
-                    const float v = tot[rt][c][i];
+                    float nv;
                     if constexpr (EPI == EPI_BIAS) {
-                        *o = v + g.bias[n];
-                    } else if constexpr (EPI == EPI_SCALE) {
-                        *o = v * rinv[i];
+                        nv = tot[rt][c][i] + g.bias[n];
                     } else {
-                        const float nv = *o + v;
-                        *o = nv;
+                        nv = *o + tot[rt][c][i];
                         if (g.taps) {
                             const int B = g.tap_B;
                             const int pos = row_pos(g.tap_s, B, m), b = row_req(g.tap_s, B, m);
                             g.taps[((static_cast<size_t>(pos) * g.tap_L + g.tap_l) * B + b) * g.ldo + n] = nv;
                         }
                     }
+                    *o = nv;
+                    g.xg[static_cast<size_t>(m) * g.ldo + n] = to_bf16(gn * nv);
+                    sq[i] = fmaf(nv, nv, sq[i]);
                 }
             }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float t = sum16(sq[i]);
+                const int m = m0 + 16 * rt + 4 * (lane >> 4) + i;
+                if ((lane & 15) == 0 && m < g.M) g.ss_out[static_cast<size_t>(m) * (g.ldo / 32) + bx] = t;
+            }
+        }
+    }
+}
+
+// One residual-stream row written whole (position inputs gathered from P_j):
+// x, xg = bf16(g * x) and the per-32-column sums of x^2.  Thread j owns
+// columns j, j + 256, ...; every load is issued before any arithmetic, and a
+// tile's sum is reduced over the 32 threads that own it.
+constexpr int kMaxRowPerThread = 16;   // dP <= 4096
+__device__ __forceinline__ void put_row(const Model& m, const float* src, int row, const float* gain, uint16_t* xg,
+                                        float* ss) {
+    const int j = threadIdx.x;
+    const int n_per = m.dP / kThreadsT;   // dP % 256 == 0
+    float v[kMaxRowPerThread], gv[kMaxRowPerThread];
+#pragma unroll
+    for (int i = 0; i < kMaxRowPerThread; ++i) {
+        if (i < n_per) {
+            v[i] = src[j + kThreadsT * i];
+            gv[i] = gain[j + kThreadsT * i];
+        }
+    }
+    float* xr = m.x + static_cast<size_t>(row) * m.dP;
+    uint16_t* gr = xg + static_cast<size_t>(row) * m.dP;
+    float* sr = ss + static_cast<size_t>(row) * (m.dP / 32);
+#pragma unroll
+    for (int i = 0; i < kMaxRowPerThread; ++i) {
+        if (i < n_per) {
+            const int n = j + kThreadsT * i;
+            xr[n] = v[i];
+            gr[n] = to_bf16(gv[i] * v[i]);
+            float q = v[i] * v[i];
+            q += __shfl_xor(q, 1, 64);
+            q += __shfl_xor(q, 2, 64);
+            q += __shfl_xor(q, 4, 64);
+            q += __shfl_xor(q, 8, 64);
+            q += __shfl_xor(q, 16, 64);
+            if ((j & 31) == 0) sr[n >> 5] = q;
         }
     }
 }
@@ -484,7 +555,7 @@ __global__ __launch_bounds__(kThreadsT) void k_attn(Model m, int B, int s, int l
 
 // Frame start, per request: check q0, x[pos 1] = P_0[q0], embsum = E_0[q0].
 // (x[pos 0] = W_p . H + b_p is a product of its own.)
-__global__ __launch_bounds__(kThreadsT) void k_start(Model m, RunArgs a) {
+__global__ __launch_bounds__(kThreadsT) void k_start(Model m, RunArgs a, const float* gain0, uint16_t* xg, float* ss) {
     __shared__ int tok_s;
     const int B = a.B;
     for (int b = blockIdx.x; b < B; b += gridDim.x) {
@@ -499,9 +570,7 @@ __global__ __launch_bounds__(kThreadsT) void k_start(Model m, RunArgs a) {
         }
         __syncthreads();
         const int q = tok_s;
-        const float* prow = m.ptab + static_cast<size_t>(q) * m.dP;
-        float* xr = m.x + static_cast<size_t>(B + b) * m.dP;
-        for (int k = threadIdx.x; k < m.dP; k += kThreadsT) xr[k] = prow[k];
+        put_row(m, m.ptab + static_cast<size_t>(q) * m.dP, B + b, gain0, xg, ss);
         float* es = a.embsum + static_cast<size_t>(b) * m.dT;
         for (int k = threadIdx.x; k < m.dT; k += kThreadsT) es[k] = emb_elem(m, 0, q, k);
     }
@@ -511,7 +580,7 @@ __global__ __launch_bounds__(kThreadsT) void k_start(Model m, RunArgs a) {
 // token (forced or own) adds E_s[t] to embsum and, before the last step,
 // sets the next position's input row P_s[t].
 __global__ __launch_bounds__(kThreadsT) void k_next(Model m, RunArgs a, int s, const unsigned long long* keys,
-                                                    int nkt) {
+                                                    int nkt, const float* gain0, uint16_t* xg, float* ss) {
     __shared__ unsigned long long red[kThreadsT / 64];
     __shared__ int fed_s;
     const int B = a.B;
@@ -540,11 +609,7 @@ __global__ __launch_bounds__(kThreadsT) void k_next(Model m, RunArgs a, int s, c
         const int t = fed_s;
         float* es = a.embsum + static_cast<size_t>(b) * m.dT;
         for (int k2 = threadIdx.x; k2 < m.dT; k2 += kThreadsT) es[k2] += emb_elem(m, s, t, k2);
-        if (s < kSteps) {
-            const float* prow = m.ptab + (static_cast<size_t>(s) * m.V + t) * m.dP;
-            float* xr = m.x + static_cast<size_t>(b) * m.dP;
-            for (int k2 = threadIdx.x; k2 < m.dP; k2 += kThreadsT) xr[k2] = prow[k2];
-        }
+        if (s < kSteps) put_row(m, m.ptab + (static_cast<size_t>(s) * m.V + t) * m.dP, b, gain0, xg, ss);
     }
 }
 
