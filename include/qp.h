@@ -162,7 +162,7 @@ qp_status qp_run_frames(qp_handle* h, int32_t B, const float* H,
 #define QP_FLAG_TILED 0x4u      /* the batched matrix-core path (one kernel per
                                    phase, projections on MFMA) for any B; only
                                    for bf16 or Q8_0 weights with dT, dP, nq*hd
-                                   and F multiples of 256, dP <= 4096, and nqkv, V multiples
+                                   and F multiples of 256, dP and dT <= 4096, nqkv and V multiples
                                    of 32 (else QP_ERR_INVALID_ARG); excludes
                                    the other flags.
    Without flags the library picks: B <= 2 with bf16 weights and the 1.7B

@@ -183,13 +183,13 @@ struct qp_handle {
     qp::tiled::FMat t_proj{};
     std::vector<qp::tiled::FMat> t_qkv, t_o, t_gate, t_up, t_down;
     qp::tiled::FMat t_lm[kSteps]{};
-    unsigned long long* t_keys = nullptr;   // [max_batch][V/32]
+    unsigned long long* t_keys = nullptr;   // [max_batch][V/16] per-tile argmax keys
     float* t_part = nullptr;                // split-K partial tiles
     size_t t_part_floats = 0;
     unsigned* t_ctr = nullptr;              // split-K tile counters
     size_t t_nctr = 0;
     uint16_t* t_xg = nullptr;               // [2*max_batch][dP] bf16(g_next * x)
-    float* t_ss = nullptr;                  // [2*max_batch][dP/32] tile sums of x^2
+    float* t_ss = nullptr;                  // [2*max_batch][dP/16] 16-column sums of x^2
 };
 
 namespace {
@@ -407,11 +407,15 @@ namespace {
 
 // --- batched matrix-core path ---------------------------------------------
 
+// Launches one product; returns the number of column tiles (gridDim.x).
 template <int WT, int SRC, int EPI>
-void tiled_gemm(const qp_handle* h, qp::tiled::GemmArgs g, hipStream_t stream) {
+int tiled_gemm(const qp_handle* h, qp::tiled::GemmArgs g, hipStream_t stream) {
     namespace T = qp::tiled;
-    const int gx = EPI == T::EPI_SWIGLU ? g.N / 16 : g.N / 32;
     const int RT = g.M <= 16 ? 1 : (g.M <= 32 ? 2 : 4);
+    // one row tile: one 16-column fragment per workgroup (twice the
+    // workgroups streaming weights); SwiGLU always pairs gate and up
+    const int CT = (RT == 1 && EPI != T::EPI_SWIGLU) ? 1 : 2;
+    const int gx = EPI == T::EPI_SWIGLU ? g.N / 16 : g.N / (16 * CT);
     const int gy = (g.M + 16 * RT - 1) / (16 * RT);
     // Products with few output tiles (the N = dP ones) and more than one row
     // tile also split K over workgroups: the smallest split (into whole pairs
@@ -423,7 +427,7 @@ void tiled_gemm(const qp_handle* h, qp::tiled::GemmArgs g, hipStream_t stream) {
         static_cast<size_t>(tiles) <= h->t_nctr) {
         for (int c = 2; c <= T::kMaxKS; ++c) {
             if ((g.K / 256) % c != 0) continue;
-            if (static_cast<size_t>(c) * tiles * RT * T::kCT * 256 > h->t_part_floats) break;
+            if (static_cast<size_t>(c) * tiles * RT * CT * 256 > h->t_part_floats) break;
             KS = c;
             if (c * tiles >= 256) break;
         }
@@ -432,12 +436,22 @@ void tiled_gemm(const qp_handle* h, qp::tiled::GemmArgs g, hipStream_t stream) {
     g.part = h->t_part;
     g.part_bytes = static_cast<uint32_t>(h->t_part_floats * 4);
     g.ctr = h->t_ctr;
-    const dim3 grid(gx, gy, KS), block(T::kThreadsT);
-    switch (RT) {
-        case 1: hipLaunchKernelGGL((T::k_gemm<WT, 1, SRC, EPI>), grid, block, 0, stream, g); break;
-        case 2: hipLaunchKernelGGL((T::k_gemm<WT, 2, SRC, EPI>), grid, block, 0, stream, g); break;
-        default: hipLaunchKernelGGL((T::k_gemm<WT, 4, SRC, EPI>), grid, block, 0, stream, g); break;
+    const dim3 grid(gx, gy, KS);
+    if (RT == 1) {
+        // little work per output: 8 waves per workgroup keep twice the weight
+        // bytes in flight where K splits into 16 pairs of blocks
+        const bool w8 = (g.K / 32) % 16 == 0;
+        constexpr int C1 = EPI == T::EPI_SWIGLU ? 2 : 1;
+        if (w8)
+            hipLaunchKernelGGL((T::k_gemm<WT, 1, SRC, EPI, 8, C1>), grid, dim3(512), 0, stream, g);
+        else
+            hipLaunchKernelGGL((T::k_gemm<WT, 1, SRC, EPI, 4, C1>), grid, dim3(256), 0, stream, g);
+    } else if (RT == 2) {
+        hipLaunchKernelGGL((T::k_gemm<WT, 2, SRC, EPI, 4, 2>), grid, dim3(256), 0, stream, g);
+    } else {
+        hipLaunchKernelGGL((T::k_gemm<WT, 4, SRC, EPI, 4, 2>), grid, dim3(256), 0, stream, g);
     }
+    return gx;
 }
 
 template <int WT>
@@ -445,11 +459,42 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
     namespace T = qp::tiled;
     qp_status st = QP_OK;
     const Model& m = h->m;
-    const int B = a.B, qd = m.nq * m.hd, nss = m.dP / 32;
+    const int B = a.B, qd = m.nq * m.hd, nss = m.dP / 16;
     const int nb = B < 1024 ? B : 1024;
     // the gain of the first reader of a position's input row
     const float* gain0 = m.L > 0 ? h->layers_host[0].attn_norm : m.out_norm;
-    hipLaunchKernelGGL(T::k_start, dim3(nb), dim3(T::kThreadsT), 0, stream, m, a, gain0, h->t_xg, h->t_ss);
+    T::TokArgs ta{};
+    ta.B = B;
+    ta.dT = m.dT;
+    ta.dP = m.dP;
+    ta.V = m.V;
+    ta.emb_bf16 = m.emb_bf16;
+    ta.q0 = a.q0;
+    ta.force = a.force;
+    ta.tok_out = a.tok_out;
+    ta.embsum = a.embsum;
+    ta.keys = h->t_keys;
+    ta.x = m.x;
+    ta.xg = h->t_xg;
+    ta.ss = h->t_ss;
+    ta.gain0 = gain0;
+    ta.err = m.err;
+    ta.emb = m.emb[0];
+    ta.ptab = m.ptab;
+    hipLaunchKernelGGL(T::k_start, dim3(nb), dim3(T::kThreadsT), 0, stream, ta);
+    T::AttnArgs aa{};
+    aa.B = B;
+    aa.nq = m.nq;
+    aa.nkv = m.nkv;
+    aa.nqkv = m.nqkv;
+    aa.max_batch = m.max_batch;
+    aa.eps = m.eps;
+    aa.attn_scale = m.attn_scale;
+    aa.qkv = m.qkv;
+    aa.kc = m.kc;
+    aa.vc = m.vc;
+    aa.rope_cos = m.rope_cos;
+    aa.rope_sin = m.rope_sin;
     T::GemmArgs g{};
     g.eps = m.eps;
     // x[position 0] = W_p . H + b_p
@@ -488,11 +533,16 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
             g.ldo = m.nqkv;
             tiled_gemm<WT, T::SRC_BF16_NORM, T::EPI_SCALE>(h, g, stream);
             // attention
+            aa.s = s;
+            aa.l = l;
+            aa.k_norm = L.k_norm;
+            aa.q_norm = L.q_norm;
+            aa.ao = ao;
             const dim3 ag(B * m.nkv);
             switch (m.hd) {
-                case 64: hipLaunchKernelGGL(T::k_attn<64>, ag, dim3(T::kThreadsT), 0, stream, m, B, s, l, ao); break;
-                case 128: hipLaunchKernelGGL(T::k_attn<128>, ag, dim3(T::kThreadsT), 0, stream, m, B, s, l, ao); break;
-                default: hipLaunchKernelGGL(T::k_attn<256>, ag, dim3(T::kThreadsT), 0, stream, m, B, s, l, ao); break;
+                case 64: hipLaunchKernelGGL(T::k_attn<64>, ag, dim3(T::kThreadsT), 0, stream, aa); break;
+                case 128: hipLaunchKernelGGL(T::k_attn<128>, ag, dim3(T::kThreadsT), 0, stream, aa); break;
+                default: hipLaunchKernelGGL(T::k_attn<256>, ag, dim3(T::kThreadsT), 0, stream, aa); break;
             }
             // x += W_o . attention; publishes bf16(ffn_norm * x)
             g = T::GemmArgs{};
@@ -561,9 +611,11 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
             g.logits = a.logits_out + static_cast<size_t>(s - 1) * m.V;
             g.logit_ld = static_cast<size_t>(kSteps) * m.V;
         }
-        tiled_gemm<WT, T::SRC_BF16_NORM, T::EPI_ARGMAX>(h, g, stream);
-        hipLaunchKernelGGL(T::k_next, dim3(nb), dim3(T::kThreadsT), 0, stream, m, a, s,
-                           static_cast<const unsigned long long*>(h->t_keys), m.V / 32, gain0, h->t_xg, h->t_ss);
+        ta.nkt = tiled_gemm<WT, T::SRC_BF16_NORM, T::EPI_ARGMAX>(h, g, stream);
+        ta.s = s;
+        ta.emb = m.emb[s];
+        ta.ptab = s < kSteps ? m.ptab + static_cast<size_t>(s) * m.V * m.dP : nullptr;
+        hipLaunchKernelGGL(T::k_next, dim3(nb), dim3(T::kThreadsT), 0, stream, ta);
     }
     if (!check_hip(hipGetLastError(), "batched path kernel launch", &st)) return st;
     return QP_OK;
@@ -692,7 +744,7 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
     // batched matrix-core path: bf16 or Q8_0 weights whose widths tile into
     // 32 x 256 blocks (every K split four ways into whole 32-wide blocks,
     // two at a time; every N a whole number of 32-column tiles)
-    h->tiled_ok = (wt == WT_BF16 || wt == WT_Q8) && m.dT % 256 == 0 && m.dP % 256 == 0 && m.dP <= 4096 &&
+    h->tiled_ok = (wt == WT_BF16 || wt == WT_Q8) && m.dT % 256 == 0 && m.dP % 256 == 0 && m.dP <= 4096 && m.dT <= 4096 &&
                   (m.nq * m.hd) % 256 == 0 && m.F % 256 == 0 && m.nqkv % 32 == 0 && m.V % 32 == 0;
     {
         const Uploader::HostMat hm = Uploader::build({w->proj_w}, {m.dP}, m.dT, wt);
@@ -792,7 +844,7 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
         // argmax keys of the lm_head tiles; split-K partial tiles and counters
         // for the products with N = dP (split K only when M <= 2 * max_batch
         // rows leave fewer than 256 tiles)
-        h->t_keys = static_cast<unsigned long long*>(up.alloc(static_cast<size_t>(m.max_batch) * (m.V / 32) * 8));
+        h->t_keys = static_cast<unsigned long long*>(up.alloc(static_cast<size_t>(m.max_batch) * (m.V / 16) * 8));
         // K is split only while tiles * KS < 2 * 256, so 512 partial tiles
         // of up to 4 row fragments x 2 column fragments suffice
         h->t_part_floats = 512ull * 4 * 2 * 256;
@@ -800,7 +852,7 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
         h->t_nctr = 256;  // split K only applies below 256 tiles
         h->t_ctr = static_cast<unsigned*>(up.alloc(h->t_nctr * 4));
         h->t_xg = static_cast<uint16_t*>(up.alloc(rows * m.dP * 2));
-        h->t_ss = static_cast<float*>(up.alloc(rows * (m.dP / 32) * 4));
+        h->t_ss = static_cast<float*>(up.alloc(rows * (m.dP / 16) * 4));
     }
 
     // records of the dataflow kernel (1.7B geometry, bf16 weights, B <= 2)

@@ -49,7 +49,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreadsT = 256;
-constexpr int kCT = 2;        // output fragments (16 columns each) per workgroup
+constexpr int kMaxCT = 2;     // output fragments (16 columns each) per workgroup
 constexpr int kMaxKS = 4;     // largest split of K across workgroups
 
 // A weight matrix [N][K] in fragment order (see the file comment).
@@ -68,7 +68,7 @@ struct GemmArgs {
     FMat w0, w1;            // w1: the up matrix of SwiGLU
     // RMSNorm of the A rows (SRC_BF16_NORM): the rows are already g * x in
     // bf16; rms(x) comes from nss partial sums of squares per row
-    const float* ss_in;     // [M][nss]
+    const float* ss_in;     // [M][nss], nss = K / 16
     int nss;
     float eps;
     // epilogue outputs
@@ -77,7 +77,8 @@ struct GemmArgs {
     uint16_t* outb;         // bf16 rows [M][N] (SWIGLU)
     const float* bias;      // [N] (BIAS)
     // BIAS / RESID also publish the next consumer's operand and row sums:
-    // xg = bf16(g_next * x) [M][ldo], ss_out[m][tile] = sum over the tile's 32 columns of x^2
+    // xg = bf16(g_next * x) [M][ldo], ss_out[m][f] = sum over the 16 columns
+    // of fragment f of x^2
     uint16_t* xg;
     const float* g_next;
     float* ss_out;
@@ -89,6 +90,38 @@ struct GemmArgs {
     float* part;            // split-K partial tiles
     uint32_t part_bytes;
     unsigned* ctr;          // split-K arrival counters, one per tile, left at 0
+};
+
+// Arguments of the token-step kernels, resolved on the host per launch and
+// kept small: a kernel reads them in one batch at its start instead of a
+// chain of dependent loads through a large structure.
+struct TokArgs {
+    int B, s, dT, dP, V, emb_bf16, nkt;
+    const void* emb;                  // E_j of this launch's codebook (fp32 or bf16 [V][dT])
+    const float* ptab;                // P_j [V][dP] of the next position's input; null at the last step
+    const int* q0;                    // [B] (frame start)
+    const int* force;                 // [B][15] or null
+    int* tok_out;                     // [B][15]
+    float* embsum;                    // [B][dT]
+    const unsigned long long* keys;   // [B][nkt] lm_head tile keys
+    float* x;                         // residual rows [2B][dP]
+    uint16_t* xg;                     // bf16(gain0 * x) rows
+    float* ss;                        // 16-column sums of x^2 [2B][dP/16]
+    const float* gain0;               // attn_norm of layer 0 (out_norm without layers)
+    unsigned* err;
+};
+
+struct AttnArgs {
+    int B, s, nq, nkv, nqkv, max_batch, l;
+    float eps, attn_scale;
+    const float* qkv;                 // [M][nqkv] step rows
+    float* kc;                        // KV cache [L][max_batch][16][nkv][hd]
+    float* vc;
+    const float* k_norm;              // layer l's per-head gains [hd]
+    const float* q_norm;
+    const float* rope_cos;            // [16][hd/2]
+    const float* rope_sin;
+    uint16_t* ao;                     // [M][nq*hd] bf16 output
 };
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -129,11 +162,14 @@ constexpr int kDevScope = 16;   // buffer cache policy: device-coherent (sc1)
 
 // ---------------------------------------------------------------------------
 // [M x K] . [K x N] with a fused prologue (SRC) and epilogue (EPI).
-// grid = (N / 32 (SwiGLU: N / 16), ceil(M / (16 RT)), KS), 256 threads.
+// grid = (N / (16 CT) (SwiGLU: N / 16), ceil(M / (16 RT)), KS), 64 * NW
+// threads (NW waves split the workgroup's K range); CT output fragments of
+// 16 columns per workgroup.
 // ---------------------------------------------------------------------------
-template <int WT, int RT, int SRC, int EPI>
-__global__ __launch_bounds__(kThreadsT) void k_gemm(GemmArgs g) {
-    __shared__ f32x4_t red[4][RT][kCT][64];
+template <int WT, int RT, int SRC, int EPI, int NW, int CT>
+__global__ __launch_bounds__(64 * NW) void k_gemm(GemmArgs g) {
+    static_assert(EPI != EPI_SWIGLU || CT == 2, "SwiGLU pairs a gate and an up fragment");
+    __shared__ f32x4_t red[NW][RT][CT][64];
     __shared__ int last_s;
 
     const int lane = threadIdx.x & 63;
@@ -141,17 +177,17 @@ __global__ __launch_bounds__(kThreadsT) void k_gemm(GemmArgs g) {
     const int bx = blockIdx.x, by = blockIdx.y, kz = blockIdx.z;
     const int m0 = by * 16 * RT;
     const int KB = g.K >> 5;
-    const int kbw = KB / (4 * g.KS);             // k-blocks per wave (even)
-    const int kb0 = (kz * 4 + wave) * kbw;
+    const int kbw = KB / (NW * g.KS);            // k-blocks per wave (even)
+    const int kb0 = (kz * NW + wave) * kbw;
 
     // output fragments of this workgroup
-    int nb[kCT];
-    const uint8_t* wp[kCT];
-    const float* sp[kCT];
+    int nb[CT];
+    const uint8_t* wp[CT];
+    const float* sp[CT];
 #pragma unroll
-    for (int c = 0; c < kCT; ++c) {
+    for (int c = 0; c < CT; ++c) {
         const FMat& W = (EPI == EPI_SWIGLU && c == 1) ? g.w1 : g.w0;
-        nb[c] = (EPI == EPI_SWIGLU) ? bx : bx * kCT + c;
+        nb[c] = (EPI == EPI_SWIGLU) ? bx : bx * CT + c;
         const size_t frag0 = static_cast<size_t>(nb[c]) * KB;
         wp[c] = static_cast<const uint8_t*>(W.w) + frag0 * 64 * (WT == WT_Q8 ? 8 : 16);
         sp[c] = (WT == WT_Q8) ? W.scale + frag0 * 16 : nullptr;
@@ -171,7 +207,7 @@ __global__ __launch_bounds__(kThreadsT) void k_gemm(GemmArgs g) {
     for (int rt = 0; rt < RT; ++rt) {
         rss[rt] = 0.f;
         if constexpr (SRC == SRC_BF16_NORM) {
-            if ((rt & 3) == wave && rok[rt]) {
+            if (rt % NW == wave && rok[rt]) {
                 const int q = g.nss >> 2;
                 const float* sr = g.ss_in + static_cast<size_t>(m0 + 16 * rt + arow) * g.nss + (lane >> 4) * q;
                 for (int t = 0; t < q; t += 2) {   // q = nss / 4 is even (dP % 256 == 0)
@@ -182,24 +218,45 @@ __global__ __launch_bounds__(kThreadsT) void k_gemm(GemmArgs g) {
         }
     }
 
-    f32x4_t acc[RT][kCT];
+    // residual-stream epilogues: the old x tile, the next reader's gain and
+    // the bias are fetched before the products
+    float xo[RT][CT][4], gnx[CT], bia[CT];
+    if constexpr (EPI == EPI_RESID || EPI == EPI_BIAS) {
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+            const int n = nb[c] * 16 + (lane & 15);
+            gnx[c] = g.g_next[n];
+            bia[c] = (EPI == EPI_BIAS) ? g.bias[n] : 0.f;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int m = m0 + 16 * rt + 4 * (lane >> 4) + i;
+                    xo[rt][c][i] = (EPI == EPI_RESID && rt % NW == wave && m < g.M)
+                                       ? g.out[static_cast<size_t>(m) * g.ldo + n] : 0.f;
+                }
+            }
+        }
+    }
+
+    f32x4_t acc[RT][CT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int c = 0; c < kCT; ++c) acc[rt][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < CT; ++c) acc[rt][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     // one batch of UU k-blocks: every load first, then the products
     auto batch = [&](int kb, auto uu) {
         constexpr int UU = decltype(uu)::value;
         uint4 av[UU][RT];
-        uint4 wv[UU][kCT];
-        uint2 wq[UU][kCT];
-        float ws[UU][kCT];
+        uint4 wv[UU][CT];
+        uint2 wq[UU][CT];
+        float ws[UU][CT];
 #pragma unroll
         for (int u = 0; u < UU; ++u) {
             const int k = (kb + u) * 32 + akoff;
 #pragma unroll
-            for (int c = 0; c < kCT; ++c) {
+            for (int c = 0; c < CT; ++c) {
                 if constexpr (WT == WT_Q8) {
                     wq[u][c] = *reinterpret_cast<const uint2*>(wp[c] + (static_cast<size_t>(kb + u) * 64 + lane) * 8);
                     ws[u][c] = sp[c][(kb + u) * 16 + (lane & 15)];
@@ -228,7 +285,7 @@ __global__ __launch_bounds__(kThreadsT) void k_gemm(GemmArgs g) {
 #pragma unroll
         for (int u = 0; u < UU; ++u) {
 #pragma unroll
-            for (int c = 0; c < kCT; ++c) {
+            for (int c = 0; c < CT; ++c) {
                 uint4 w8;
                 if constexpr (WT == WT_Q8) {
                     w8 = make_uint4(q8pair(wq[u][c].x, 0), q8pair(wq[u][c].x, 16), q8pair(wq[u][c].y, 0),
@@ -264,20 +321,19 @@ __global__ __launch_bounds__(kThreadsT) void k_gemm(GemmArgs g) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int c = 0; c < kCT; ++c) red[wave][rt][c][lane] = acc[rt][c];
+        for (int c = 0; c < CT; ++c) red[wave][rt][c][lane] = acc[rt][c];
     __syncthreads();
 
-    // wave w finishes row tiles w, w+4, ...
-    f32x4_t tot[RT][kCT];
+    // wave w finishes row tiles w, w + NW, ...
+    f32x4_t tot[RT][CT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        if ((rt & 3) != wave) continue;
+        if (rt % NW != wave) continue;
 #pragma unroll
-        for (int c = 0; c < kCT; ++c) {
+        for (int c = 0; c < CT; ++c) {
             f32x4_t t = red[0][rt][c][lane];
-            t += red[1][rt][c][lane];
-            t += red[2][rt][c][lane];
-            t += red[3][rt][c][lane];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) t += red[w][rt][c][lane];
             tot[rt][c] = t;
         }
     }
@@ -290,13 +346,13 @@ __global__ __launch_bounds__(kThreadsT) void k_gemm(GemmArgs g) {
         const auto pr = __builtin_amdgcn_make_buffer_rsrc(g.part, static_cast<short>(0), static_cast<int>(g.part_bytes),
                                                           0x00020000);
         auto poff = [&](int z, int rt, int c) {
-            return static_cast<uint32_t>(((((static_cast<size_t>(z) * tiles + tile) * RT + rt) * kCT + c) * 64 + lane) * 16);
+            return static_cast<uint32_t>(((((static_cast<size_t>(z) * tiles + tile) * RT + rt) * CT + c) * 64 + lane) * 16);
         };
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            if ((rt & 3) != wave) continue;
+            if (rt % NW != wave) continue;
 #pragma unroll
-            for (int c = 0; c < kCT; ++c)
+            for (int c = 0; c < CT; ++c)
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, tot[rt][c]), pr, poff(kz, rt, c), 0u,
                                                        kDevScope);
         }
@@ -312,9 +368,9 @@ __global__ __launch_bounds__(kThreadsT) void k_gemm(GemmArgs g) {
         if (!last_s) return;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            if ((rt & 3) != wave) continue;
+            if (rt % NW != wave) continue;
 #pragma unroll
-            for (int c = 0; c < kCT; ++c) {
+            for (int c = 0; c < CT; ++c) {
                 f32x4_t t = f32x4_t{0.f, 0.f, 0.f, 0.f};
                 for (int z = 0; z < g.KS; ++z)
                     t += __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(pr, poff(z, rt, c), 0u, kDevScope));
@@ -326,7 +382,7 @@ __global__ __launch_bounds__(kThreadsT) void k_gemm(GemmArgs g) {
     // ---- epilogue: lane holds rows 4*(lane/16)+i, column lane%16 of each fragment ----
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        if ((rt & 3) != wave) continue;
+        if (rt % NW != wave) continue;
         float rinv[4] = {1.f, 1.f, 1.f, 1.f};
         if constexpr (SRC == SRC_BF16_NORM) {
             float t = rss[rt];
@@ -341,7 +397,7 @@ __global__ __launch_bounds__(kThreadsT) void k_gemm(GemmArgs g) {
         if constexpr (EPI == EPI_ARGMAX) {
             uint64_t key[4] = {0, 0, 0, 0};
 #pragma unroll
-            for (int c = 0; c < kCT; ++c) {
+            for (int c = 0; c < CT; ++c) {
                 const int n = nb[c] * 16 + (lane & 15);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -369,7 +425,7 @@ __global__ __launch_bounds__(kThreadsT) void k_gemm(GemmArgs g) {
             }
         } else if constexpr (EPI == EPI_SCALE) {
 #pragma unroll
-            for (int c = 0; c < kCT; ++c) {
+            for (int c = 0; c < CT; ++c) {
                 const int n = nb[c] * 16 + (lane & 15);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -379,12 +435,12 @@ __global__ __launch_bounds__(kThreadsT) void k_gemm(GemmArgs g) {
             }
         } else {
             // residual stream rows: x (fp32), xg = bf16(g_next * x), and the
-            // sum of x^2 over this workgroup's 32 columns
-            float sq[4] = {0.f, 0.f, 0.f, 0.f};
+            // sum of x^2 over each 16-column fragment
 #pragma unroll
-            for (int c = 0; c < kCT; ++c) {
+            for (int c = 0; c < CT; ++c) {
+                float sq[4] = {0.f, 0.f, 0.f, 0.f};
                 const int n = nb[c] * 16 + (lane & 15);
-                const float gn = g.g_next[n];
+                const float gn = gnx[c];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int m = m0 + 16 * rt + 4 * (lane >> 4) + i;
@@ -392,9 +448,9 @@ __global__ __launch_bounds__(kThreadsT) void k_gemm(GemmArgs g) {
                     float* o = g.out + static_cast<size_t>(m) * g.ldo + n;
                     float nv;
                     if constexpr (EPI == EPI_BIAS) {
-                        nv = tot[rt][c][i] + g.bias[n];
+                        nv = tot[rt][c][i] + bia[c];
                     } else {
-                        nv = *o + tot[rt][c][i];
+                        nv = xo[rt][c][i] + tot[rt][c][i];
                         if (g.taps) {
                             const int B = g.tap_B;
                             const int pos = row_pos(g.tap_s, B, m), b = row_req(g.tap_s, B, m);
@@ -403,42 +459,36 @@ __global__ __launch_bounds__(kThreadsT) void k_gemm(GemmArgs g) {
                     }
                     *o = nv;
                     g.xg[static_cast<size_t>(m) * g.ldo + n] = to_bf16(gn * nv);
-                    sq[i] = fmaf(nv, nv, sq[i]);
+                    sq[i] = nv * nv;
                 }
-            }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float t = sum16(sq[i]);
-                const int m = m0 + 16 * rt + 4 * (lane >> 4) + i;
-                if ((lane & 15) == 0 && m < g.M) g.ss_out[static_cast<size_t>(m) * (g.ldo / 32) + bx] = t;
+                for (int i = 0; i < 4; ++i) {
+                    const float t = sum16(sq[i]);
+                    const int m = m0 + 16 * rt + 4 * (lane >> 4) + i;
+                    if ((lane & 15) == 0 && m < g.M) g.ss_out[static_cast<size_t>(m) * (g.ldo / 16) + nb[c]] = t;
+                }
             }
         }
     }
 }
 
-// One residual-stream row written whole (position inputs gathered from P_j):
-// x, xg = bf16(g * x) and the per-32-column sums of x^2.  Thread j owns
-// columns j, j + 256, ...; every load is issued before any arithmetic, and a
-// tile's sum is reduced over the 32 threads that own it.
-constexpr int kMaxRowPerThread = 16;   // dP <= 4096
-__device__ __forceinline__ void put_row(const Model& m, const float* src, int row, const float* gain, uint16_t* xg,
-                                        float* ss) {
-    const int j = threadIdx.x;
-    const int n_per = m.dP / kThreadsT;   // dP % 256 == 0
-    float v[kMaxRowPerThread], gv[kMaxRowPerThread];
+// Row helpers of the token steps.  Thread j owns elements j, j + 256, ...
+// (dT and dP are multiples of 256 and at most 4096); callers issue every
+// load before any store so that one memory round trip covers a row.
+constexpr int kMaxPer = 16;
+
+// x, xg = bf16(g * x) and the per-16-column sums of x^2 of residual-stream
+// row `row` from values v (with gains gv) already in registers; a
+// fragment's sum is reduced over the 16 threads that own it.
+__device__ __forceinline__ void store_row(const TokArgs& ta, int row, const float (&v)[kMaxPer],
+                                          const float (&gv)[kMaxPer]) {
+    const int j = threadIdx.x, np = ta.dP / kThreadsT;
+    float* xr = ta.x + static_cast<size_t>(row) * ta.dP;
+    uint16_t* gr = ta.xg + static_cast<size_t>(row) * ta.dP;
+    float* sr = ta.ss + static_cast<size_t>(row) * (ta.dP / 16);
 #pragma unroll
-    for (int i = 0; i < kMaxRowPerThread; ++i) {
-        if (i < n_per) {
-            v[i] = src[j + kThreadsT * i];
-            gv[i] = gain[j + kThreadsT * i];
-        }
-    }
-    float* xr = m.x + static_cast<size_t>(row) * m.dP;
-    uint16_t* gr = xg + static_cast<size_t>(row) * m.dP;
-    float* sr = ss + static_cast<size_t>(row) * (m.dP / 32);
-#pragma unroll
-    for (int i = 0; i < kMaxRowPerThread; ++i) {
-        if (i < n_per) {
+    for (int i = 0; i < kMaxPer; ++i) {
+        if (i < np) {
             const int n = j + kThreadsT * i;
             xr[n] = v[i];
             gr[n] = to_bf16(gv[i] * v[i]);
@@ -447,8 +497,63 @@ __device__ __forceinline__ void put_row(const Model& m, const float* src, int ro
             q += __shfl_xor(q, 2, 64);
             q += __shfl_xor(q, 4, 64);
             q += __shfl_xor(q, 8, 64);
-            q += __shfl_xor(q, 16, 64);
-            if ((j & 31) == 0) sr[n >> 5] = q;
+            if ((j & 15) == 0) sr[n >> 4] = q;
+        }
+    }
+}
+
+__device__ __forceinline__ void load_vec(const float* src, int n_per, float (&v)[kMaxPer]) {
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i)
+        if (i < n_per) v[i] = src[threadIdx.x + kThreadsT * i];
+}
+
+__device__ __forceinline__ void load_emb(const TokArgs& ta, int t, float (&e)[kMaxPer]) {
+    const int ne = ta.dT / kThreadsT;
+    const size_t row = static_cast<size_t>(t) * ta.dT;
+    if (ta.emb_bf16) {
+        const uint16_t* E = static_cast<const uint16_t*>(ta.emb) + row;
+#pragma unroll
+        for (int i = 0; i < kMaxPer; ++i)
+            if (i < ne) e[i] = __uint_as_float(static_cast<uint32_t>(E[threadIdx.x + kThreadsT * i]) << 16);
+    } else {
+        const float* E = static_cast<const float*>(ta.emb) + row;
+#pragma unroll
+        for (int i = 0; i < kMaxPer; ++i)
+            if (i < ne) e[i] = E[threadIdx.x + kThreadsT * i];
+    }
+}
+
+// Per-head RMSNorm then rotate-half RoPE of a head vector held by one wave
+// (element lane + 64 j in v[j]); the pair of element i is element i + hd/2.
+template <int HD>
+__device__ __forceinline__ void norm_rope_regs(const float (&v)[HD / 64], const float* gain, float eps, int pos,
+                                               const float* rcos, const float* rsin, float (&out)[HD / 64]) {
+    constexpr int J = HD / 64;
+    const int lane = threadIdx.x & 63;
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) ss += v[j] * v[j];
+    ss = wave_sum(ss);
+    const float rinv = 1.0f / sqrtf(ss / static_cast<float>(HD) + eps);
+    float w[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) w[j] = gain[lane + 64 * j] * (v[j] * rinv);
+    const float* cp = rcos + pos * (HD / 2);
+    const float* sp = rsin + pos * (HD / 2);
+    if constexpr (J == 1) {
+        const float partner = __shfl_xor(w[0], 32, 64);
+        const int i = lane & 31;
+        const float c = cp[i], sn = sp[i];
+        out[0] = (lane < 32) ? (w[0] * c - partner * sn) : (w[0] * c + partner * sn);
+    } else {
+        constexpr int H2 = J / 2;
+#pragma unroll
+        for (int j = 0; j < H2; ++j) {
+            const int i = lane + 64 * j;
+            const float c = cp[i], sn = sp[i];
+            out[j] = w[j] * c - w[j + H2] * sn;
+            out[j + H2] = w[j + H2] * c + w[j] * sn;
         }
     }
 }
@@ -458,59 +563,111 @@ __device__ __forceinline__ void put_row(const Model& m, const float* src, int ro
 // position of the step is handled in order (the prefill's position 1 sees
 // position 0).  Keys and values of earlier positions come from the fp32 KV
 // cache; the new position's key gets its per-head RMSNorm and RoPE here and
-// is appended to the cache.  Scores for all <= 16 keys are formed at once:
-// key t on lanes 4t..4t+3, each lane a quarter of the head.
+// is appended to the cache.  All global reads (history, the step's q/k/v
+// rows) are issued before the first barrier.  Scores for all <= 16 keys are
+// formed at once: key t on lanes 4t..4t+3, each lane a quarter of the head.
 // Output: bf16 rows [M][nq*hd], the operand of the output projection.
 // ---------------------------------------------------------------------------
 template <int HD>
-__global__ __launch_bounds__(kThreadsT) void k_attn(Model m, int B, int s, int l, uint16_t* ao) {
+__global__ __launch_bounds__(kThreadsT) void k_attn(AttnArgs m) {
     constexpr int J = HD / 64;        // elements per lane in the lane + 64 j layout
     constexpr int SL = HD / 4;        // slice of the head per lane in the score
+    constexpr int HPT = kPositions * HD / kThreadsT;   // history elements per thread (max)
     __shared__ float Ks[kPositions][HD];
     __shared__ float Vs[kPositions][HD];
     __shared__ float qs[4][HD];
     __shared__ float es[4][kPositions];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int B = m.B, s = m.s, l = m.l;
     const int nkv = m.nkv, grp = m.nq / m.nkv;
     const int b = blockIdx.x / nkv, g = blockIdx.x % nkv;
-    const LayerDev& L = m.layers[l];
     const int npos = (s == 1) ? 2 : 1;
     const int pf = (s == 1) ? 0 : s;
     const size_t kvb = ((static_cast<size_t>(l) * m.max_batch + b) * kPositions) * nkv * HD;
-    for (int idx = threadIdx.x; idx < pf * HD; idx += kThreadsT) {
-        const int t = idx / HD, d = idx - t * HD;
-        const size_t off = kvb + (static_cast<size_t>(t) * nkv + g) * HD + d;
-        Ks[t][d] = m.kc[off];
-        Vs[t][d] = m.vc[off];
+
+    // ---- every global read first ----
+    float hk[HPT], hv[HPT];
+#pragma unroll
+    for (int i = 0; i < HPT; ++i) {
+        const int idx = threadIdx.x + kThreadsT * i;
+        hk[i] = hv[i] = 0.f;
+        if (idx < pf * HD) {
+            const int t = idx / HD, d = idx - t * HD;
+            const size_t off = kvb + (static_cast<size_t>(t) * nkv + g) * HD + d;
+            hk[i] = m.kc[off];
+            hv[i] = m.vc[off];
+        }
     }
+    // wave 0: the step's key rows, wave 1: value rows, wave w: query head
+    // g * grp + w (later heads of a large group are read when used)
+    float pin[2][J];
+#pragma unroll
+    for (int pi = 0; pi < 2; ++pi) {
+        const int r = (s == 1) ? pi * B + b : b;
+        const float* row = m.qkv + static_cast<size_t>(r) * m.nqkv;
+        const int col = wave == 0 ? (m.nq + g) * HD : (wave == 1 ? (m.nq + nkv + g) * HD : 0);
+#pragma unroll
+        for (int j = 0; j < J; ++j) pin[pi][j] = 0.f;
+        if (pi < npos && wave < 2) {
+#pragma unroll
+            for (int j = 0; j < J; ++j) pin[pi][j] = row[col + lane + 64 * j];
+        }
+    }
+    float qin[2][J];
+#pragma unroll
+    for (int pi = 0; pi < 2; ++pi) {
+        const int r = (s == 1) ? pi * B + b : b;
+        const float* row = m.qkv + static_cast<size_t>(r) * m.nqkv;
+#pragma unroll
+        for (int j = 0; j < J; ++j) qin[pi][j] = 0.f;
+        if (pi < npos && wave < grp) {
+#pragma unroll
+            for (int j = 0; j < J; ++j) qin[pi][j] = row[(g * grp + wave) * HD + lane + 64 * j];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < HPT; ++i) {
+        const int idx = threadIdx.x + kThreadsT * i;
+        if (idx < pf * HD) {
+            const int t = idx / HD, d = idx - t * HD;
+            Ks[t][d] = hk[i];
+            Vs[t][d] = hv[i];
+        }
+    }
+
     for (int pi = 0; pi < npos; ++pi) {
         const int p = pf + pi;
         const int r = (s == 1) ? pi * B + b : b;
-        const float* row = m.qkv + static_cast<size_t>(r) * m.nqkv;
         const size_t off = kvb + (static_cast<size_t>(p) * nkv + g) * HD;
         if (wave == 0) {
-            float kr[4];
-            norm_rope_wave(row + (m.nq + g) * HD, L.k_norm, HD, m.eps, p, m.rope_cos, m.rope_sin, kr);
+            float kr[J];
+            norm_rope_regs<HD>(pin[pi], m.k_norm, m.eps, p, m.rope_cos, m.rope_sin, kr);
 #pragma unroll
             for (int j = 0; j < J; ++j) {
                 Ks[p][lane + 64 * j] = kr[j];
                 m.kc[off + lane + 64 * j] = kr[j];
             }
         } else if (wave == 1) {
-            const float* vr = row + (m.nq + nkv + g) * HD;
 #pragma unroll
             for (int j = 0; j < J; ++j) {
-                const float v = vr[lane + 64 * j];
-                Vs[p][lane + 64 * j] = v;
-                m.vc[off + lane + 64 * j] = v;
+                Vs[p][lane + 64 * j] = pin[pi][j];
+                m.vc[off + lane + 64 * j] = pin[pi][j];
             }
         }
         __syncthreads();
         for (int i = wave; i < grp; i += 4) {
             const int h = g * grp + i;
-            float q[4];
-            norm_rope_wave(row + h * HD, L.q_norm, HD, m.eps, p, m.rope_cos, m.rope_sin, q);
+            float qv[J], q[J];
+            if (i == wave) {
+#pragma unroll
+                for (int j = 0; j < J; ++j) qv[j] = qin[pi][j];
+            } else {
+                const float* row = m.qkv + static_cast<size_t>(r) * m.nqkv + h * HD;
+#pragma unroll
+                for (int j = 0; j < J; ++j) qv[j] = row[lane + 64 * j];
+            }
+            norm_rope_regs<HD>(qv, m.q_norm, m.eps, p, m.rope_cos, m.rope_sin, q);
 #pragma unroll
             for (int j = 0; j < J; ++j) qs[wave][lane + 64 * j] = q[j];
             const int kt = lane >> 2, k0 = (lane & 3) * SL;
@@ -518,12 +675,12 @@ __global__ __launch_bounds__(kThreadsT) void k_attn(Model m, int B, int s, int l
             if (kt <= p) {
 #pragma unroll
                 for (int d = 0; d < SL; d += 4) {
-                    const float4 qv = *reinterpret_cast<const float4*>(&qs[wave][k0 + d]);
-                    const float4 kv = *reinterpret_cast<const float4*>(&Ks[kt][k0 + d]);
-                    sc = fmaf(qv.x, kv.x, sc);
-                    sc = fmaf(qv.y, kv.y, sc);
-                    sc = fmaf(qv.z, kv.z, sc);
-                    sc = fmaf(qv.w, kv.w, sc);
+                    const float4 qq = *reinterpret_cast<const float4*>(&qs[wave][k0 + d]);
+                    const float4 kk = *reinterpret_cast<const float4*>(&Ks[kt][k0 + d]);
+                    sc = fmaf(qq.x, kk.x, sc);
+                    sc = fmaf(qq.y, kk.y, sc);
+                    sc = fmaf(qq.z, kk.z, sc);
+                    sc = fmaf(qq.w, kk.w, sc);
                 }
             }
             sc += dpp_or_zero<0xB1, 0xF>(sc);
@@ -545,7 +702,7 @@ __global__ __launch_bounds__(kThreadsT) void k_attn(Model m, int B, int s, int l
 #pragma unroll
                 for (int j = 0; j < J; ++j) o[j] = fmaf(w, Vs[tt][lane + 64 * j], o[j]);
             }
-            uint16_t* orow = ao + static_cast<size_t>(r) * (m.nq * HD) + h * HD;
+            uint16_t* orow = m.ao + static_cast<size_t>(r) * (m.nq * HD) + h * HD;
 #pragma unroll
             for (int j = 0; j < J; ++j) orow[lane + 64 * j] = to_bf16(o[j] / den);
         }
@@ -555,41 +712,51 @@ __global__ __launch_bounds__(kThreadsT) void k_attn(Model m, int B, int s, int l
 
 // Frame start, per request: check q0, x[pos 1] = P_0[q0], embsum = E_0[q0].
 // (x[pos 0] = W_p . H + b_p is a product of its own.)
-__global__ __launch_bounds__(kThreadsT) void k_start(Model m, RunArgs a, const float* gain0, uint16_t* xg, float* ss) {
+__global__ __launch_bounds__(kThreadsT) void k_start(TokArgs ta) {
     __shared__ int tok_s;
-    const int B = a.B;
+    const int B = ta.B, ne = ta.dT / kThreadsT, np = ta.dP / kThreadsT;
+    float gv[kMaxPer], v[kMaxPer], e[kMaxPer];
+    load_vec(ta.gain0, np, gv);
     for (int b = blockIdx.x; b < B; b += gridDim.x) {
         __syncthreads();
         if (threadIdx.x == 0) {
-            int q = a.q0[b];
-            if (q < 0 || q >= m.V) {
-                atomicOr(m.err, kErrBadQ0);
+            int q = ta.q0[b];
+            if (q < 0 || q >= ta.V) {
+                atomicOr(ta.err, kErrBadQ0);
                 q = 0;
             }
             tok_s = q;
         }
         __syncthreads();
-        const int q = tok_s;
-        put_row(m, m.ptab + static_cast<size_t>(q) * m.dP, B + b, gain0, xg, ss);
-        float* es = a.embsum + static_cast<size_t>(b) * m.dT;
-        for (int k = threadIdx.x; k < m.dT; k += kThreadsT) es[k] = emb_elem(m, 0, q, k);
+        const int q = __builtin_amdgcn_readfirstlane(tok_s);
+        load_vec(ta.ptab + static_cast<size_t>(q) * ta.dP, np, v);
+        load_emb(ta, q, e);
+        store_row(ta, B + b, v, gv);
+        float* es = ta.embsum + static_cast<size_t>(b) * ta.dT;
+#pragma unroll
+        for (int i = 0; i < kMaxPer; ++i)
+            if (i < ne) es[threadIdx.x + kThreadsT * i] = e[i];
     }
 }
 
 // Step s's token per request from the lm_head tiles' keys; the fed-back
 // token (forced or own) adds E_s[t] to embsum and, before the last step,
 // sets the next position's input row P_s[t].
-__global__ __launch_bounds__(kThreadsT) void k_next(Model m, RunArgs a, int s, const unsigned long long* keys,
-                                                    int nkt, const float* gain0, uint16_t* xg, float* ss) {
+__global__ __launch_bounds__(kThreadsT) void k_next(TokArgs ta) {
     __shared__ unsigned long long red[kThreadsT / 64];
     __shared__ int fed_s;
-    const int B = a.B;
+    const int B = ta.B, s = ta.s, nkt = ta.nkt;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int ne = ta.dT / kThreadsT, np = ta.dP / kThreadsT;
+    float gv[kMaxPer], o[kMaxPer], v[kMaxPer], e[kMaxPer];
+    if (ta.ptab) load_vec(ta.gain0, np, gv);
     for (int b = blockIdx.x; b < B; b += gridDim.x) {
+        float* es = ta.embsum + static_cast<size_t>(b) * ta.dT;
+        load_vec(es, ne, o);
         uint64_t k = 0;
-        for (int t = threadIdx.x; t < nkt; t += kThreadsT) k = umax64(k, keys[static_cast<size_t>(b) * nkt + t]);
+        for (int t = threadIdx.x; t < nkt; t += kThreadsT) k = umax64(k, ta.keys[static_cast<size_t>(b) * nkt + t]);
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) k = umax64(k, shfl_xor64(k, o));
+        for (int off = 1; off < 64; off <<= 1) k = umax64(k, shfl_xor64(k, off));
         __syncthreads();
         if (lane == 0) red[wave] = k;
         __syncthreads();
@@ -597,19 +764,22 @@ __global__ __launch_bounds__(kThreadsT) void k_next(Model m, RunArgs a, int s, c
             uint64_t kk = red[0];
             for (int w = 1; w < kThreadsT / 64; ++w) kk = umax64(kk, red[w]);
             const int tok = argmax_index(kk);
-            a.tok_out[b * kSteps + (s - 1)] = tok;
-            int fed = a.force ? a.force[b * kSteps + (s - 1)] : tok;
-            if (fed < 0 || fed >= m.V) {
-                atomicOr(m.err, a.force ? kErrBadForced : kErrBadQ0);
+            ta.tok_out[b * kSteps + (s - 1)] = tok;
+            int fed = ta.force ? ta.force[b * kSteps + (s - 1)] : tok;
+            if (fed < 0 || fed >= ta.V) {
+                atomicOr(ta.err, ta.force ? kErrBadForced : kErrBadQ0);
                 fed = 0;
             }
             fed_s = fed;
         }
         __syncthreads();
-        const int t = fed_s;
-        float* es = a.embsum + static_cast<size_t>(b) * m.dT;
-        for (int k2 = threadIdx.x; k2 < m.dT; k2 += kThreadsT) es[k2] += emb_elem(m, s, t, k2);
-        if (s < kSteps) put_row(m, m.ptab + (static_cast<size_t>(s) * m.V + t) * m.dP, b, gain0, xg, ss);
+        const int t = __builtin_amdgcn_readfirstlane(fed_s);
+        load_emb(ta, t, e);
+        if (ta.ptab) load_vec(ta.ptab + static_cast<size_t>(t) * ta.dP, np, v);
+#pragma unroll
+        for (int i = 0; i < kMaxPer; ++i)
+            if (i < ne) es[threadIdx.x + kThreadsT * i] = o[i] + e[i];
+        if (ta.ptab) store_row(ta, b, v, gv);
     }
 }
 
