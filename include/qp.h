@@ -150,7 +150,10 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device,
  *   embsum_out float [B, dT]   E_0[q0] + E_1[q1] + ... + E_15[q15], fp32,
  *                              summed in that order
  * Row b of the outputs depends only on (H[b], q0[b]).  An out-of-range q0 is
- * replaced by 0 and raises the sticky device flag (qp_get_error). */
+ * replaced by 0 and raises the sticky device flag (qp_get_error).
+ * On the batched matrix-core path the frame replays a graph captured once
+ * per batch size (the handle keeps the 4 most recent); the first call with
+ * a new B captures and instantiates it before enqueueing. */
 qp_status qp_run_frames(qp_handle* h, int32_t B, const float* H,
                         const int32_t* q0, int32_t* tokens_out,
                         float* embsum_out, void* stream);

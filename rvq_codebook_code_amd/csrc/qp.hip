@@ -5,6 +5,7 @@
 // per frame, or one kernel per phase).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -104,6 +105,13 @@ __global__ __launch_bounds__(kThreads) void k_phase(Model m, RunArgs a, int ph, 
     run_phase<WT>(m, a, ph, s, l, lds, blockIdx.x, gridDim.x);
 }
 
+// 32-bit word copy (staging of a frame's inputs and outputs)
+__global__ void k_copy32(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst, size_t n) {
+    for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
+         i += static_cast<size_t>(gridDim.x) * blockDim.x)
+        dst[i] = src[i];
+}
+
 // --- create-time kernels ----------------------------------------------------
 
 // EMA codebook: E[v][k] = S[v][k] / (u[v] + 1e-7), fp32 add then fp32 divide.
@@ -188,6 +196,21 @@ struct qp_handle {
     size_t t_part_floats = 0;
     unsigned* t_ctr = nullptr;              // split-K tile counters
     size_t t_nctr = 0;
+    // one frame of the batched path captured as a graph per batch size,
+    // reading and writing handle-owned staging buffers
+    struct FrameGraph {
+        int B = 0;
+        hipGraph_t graph = nullptr;
+        hipGraphExec_t exec = nullptr;
+    };
+    static constexpr int kGraphs = 4;
+    FrameGraph graphs[kGraphs];
+    int graph_next = 0;
+    hipStream_t cap_stream = nullptr;
+    float* st_H = nullptr;                  // [max_batch][dT]
+    int* st_q0 = nullptr;                   // [max_batch]
+    int* st_tok = nullptr;                  // [max_batch][15]
+    float* st_emb = nullptr;                // [max_batch][dT]
     uint16_t* t_xg = nullptr;               // [2*max_batch][dP] bf16(g_next * x)
     float* t_ss = nullptr;                  // [2*max_batch][dP/16] 16-column sums of x^2
 };
@@ -621,12 +644,78 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
     return QP_OK;
 }
 
+void copy32(const void* src, void* dst, size_t words, hipStream_t stream) {
+    const int blocks = static_cast<int>(std::min<size_t>((words + 255) / 256, 1024));
+    hipLaunchKernelGGL(k_copy32, dim3(blocks), dim3(256), 0, stream, static_cast<const uint32_t*>(src),
+                       static_cast<uint32_t*>(dst), words);
+}
+
+// The batched path without test hooks: inputs are staged into handle-owned
+// buffers, the frame (about 400 kernels) replays as one graph captured once
+// per batch size, and the outputs are copied back.  Nothing in the graph
+// clears memory with a memset node: the split-K counters are left at zero by
+// the kernels themselves.
+template <int WT>
+qp_status launch_tiled_graph(qp_handle* h, const RunArgs& a, hipStream_t stream) {
+    qp_status st = QP_OK;
+    const Model& m = h->m;
+    const int B = a.B;
+    copy32(a.H, h->st_H, static_cast<size_t>(B) * m.dT, stream);
+    copy32(a.q0, h->st_q0, static_cast<size_t>(B), stream);
+    qp_handle::FrameGraph* fg = nullptr;
+    for (auto& e : h->graphs)
+        if (e.exec && e.B == B) fg = &e;
+    if (!fg) {
+        if (!h->cap_stream &&
+            !check_hip(hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking), "hipStreamCreate", &st))
+            return st;
+        RunArgs sa = a;
+        sa.H = h->st_H;
+        sa.q0 = h->st_q0;
+        sa.tok_out = h->st_tok;
+        sa.embsum = h->st_emb;
+        fg = &h->graphs[h->graph_next];
+        h->graph_next = (h->graph_next + 1) % qp_handle::kGraphs;
+        if (fg->exec) {
+            (void)hipGraphExecDestroy(fg->exec);
+            (void)hipGraphDestroy(fg->graph);
+            *fg = qp_handle::FrameGraph{};
+        }
+        hipGraph_t graph = nullptr;
+        hipGraphExec_t exec = nullptr;
+        if (!check_hip(hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeRelaxed), "hipStreamBeginCapture", &st))
+            return st;
+        const qp_status lst = launch_tiled<WT>(h, sa, h->cap_stream);
+        const hipError_t ce = hipStreamEndCapture(h->cap_stream, &graph);
+        if (lst != QP_OK) {
+            if (graph) (void)hipGraphDestroy(graph);
+            return lst;
+        }
+        if (!check_hip(ce, "hipStreamEndCapture", &st)) return st;
+        if (!check_hip(hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0), "hipGraphInstantiate", &st)) {
+            (void)hipGraphDestroy(graph);
+            return st;
+        }
+        fg->B = B;
+        fg->graph = graph;
+        fg->exec = exec;
+    }
+    if (!check_hip(hipGraphLaunch(fg->exec, stream), "hipGraphLaunch", &st)) return st;
+    copy32(h->st_tok, a.tok_out, static_cast<size_t>(B) * kSteps, stream);
+    copy32(h->st_emb, a.embsum, static_cast<size_t>(B) * m.dT, stream);
+    if (!check_hip(hipGetLastError(), "staging copy launch", &st)) return st;
+    return QP_OK;
+}
+
 template <int WT>
 qp_status launch_frame(qp_handle* h, const RunArgs& a, hipStream_t stream, bool stepwise, bool generic, bool tiled) {
     qp_status st = QP_OK;
     const Model& m = h->m;
     if constexpr (WT == WT_BF16 || WT == WT_Q8) {
-        if (tiled || (!stepwise && !generic && h->tiled_ok && a.B > 2)) return launch_tiled<WT>(h, a, stream);
+        if (tiled || (!stepwise && !generic && h->tiled_ok && a.B > 2)) {
+            const bool hooks = a.force || a.logits_out || a.taps;
+            return hooks ? launch_tiled<WT>(h, a, stream) : launch_tiled_graph<WT>(h, a, stream);
+        }
     }
     if constexpr (WT == WT_BF16) {
         if (!stepwise && !generic && h->stream_ok && a.B <= 2) {
@@ -852,6 +941,10 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
         h->t_nctr = 256;  // split K only applies below 256 tiles
         h->t_ctr = static_cast<unsigned*>(up.alloc(h->t_nctr * 4));
         h->t_xg = static_cast<uint16_t*>(up.alloc(rows * m.dP * 2));
+        h->st_H = static_cast<float*>(up.alloc(static_cast<size_t>(m.max_batch) * m.dT * 4));
+        h->st_q0 = static_cast<int*>(up.alloc(static_cast<size_t>(m.max_batch) * 4));
+        h->st_tok = static_cast<int*>(up.alloc(static_cast<size_t>(m.max_batch) * kSteps * 4));
+        h->st_emb = static_cast<float*>(up.alloc(static_cast<size_t>(m.max_batch) * m.dT * 4));
         h->t_ss = static_cast<float*>(up.alloc(rows * (m.dP / 16) * 4));
     }
 
@@ -969,6 +1062,11 @@ void qp_destroy(qp_handle* h) {
     {
         DeviceGuard guard(h->device);
         (void)hipDeviceSynchronize();
+        for (auto& e : h->graphs) {
+            if (e.exec) (void)hipGraphExecDestroy(e.exec);
+            if (e.graph) (void)hipGraphDestroy(e.graph);
+        }
+        if (h->cap_stream) (void)hipStreamDestroy(h->cap_stream);
         free_all(h);
     }
     delete h;

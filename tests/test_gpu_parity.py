@@ -276,3 +276,25 @@ def test_tiled_against_dataflow_b2():
     print(f"[tiled vs dataflow B=2] logits max-abs {lg:.3g}")
     assert lg <= TOL["bf16"]
     assert np.abs(a["embsum"] - b["embsum"]).max() <= TOL["bf16"]
+
+
+def test_tiled_graph_replays_match_stream_path():
+    """Without test hooks the batched path replays a captured graph per batch
+    size; every replay, interleaved with eager work and with more batch sizes
+    than the graph cache holds, must equal the direct launch sequence."""
+    wl, W, model, pred = workload("tiny_q8ema")
+    dev = _dev()
+    g = wl.geom
+    sizes = [3, 17, 3, 37, 5, 9, 17, 3, 40]
+    for i, B in enumerate(sizes):
+        H, q0 = synth.make_inputs(g, B, 1, 6100 + i)
+        graph = gpu_frame(pred, H[0], q0[0], logits=False, tiled=True)
+        # eager work on the same stream between replays
+        junk = torch.randn(1 << 16, device=dev)
+        (junk * 2.0).sum().item()
+        direct = gpu_frame(pred, H[0], q0[0], logits=True, tiled=True)
+        np.testing.assert_array_equal(graph["tokens"], direct["tokens"])
+        np.testing.assert_array_equal(graph["embsum"], direct["embsum"])
+        again = gpu_frame(pred, H[0], q0[0], logits=False, tiled=True)
+        np.testing.assert_array_equal(again["tokens"], graph["tokens"])
+        np.testing.assert_array_equal(again["embsum"], graph["embsum"])
