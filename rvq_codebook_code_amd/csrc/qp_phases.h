@@ -32,6 +32,42 @@ __device__ __forceinline__ float wave_sum(float v) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// N independent wave sums, stage by stage, so that the DPP moves of one sum
+// fill the wait states of the others; same tree (and result) as wave_sum.
+template <int N>
+__device__ __forceinline__ void wave_sums(float (&v)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp_or_zero<0xB1, 0xF>(v[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp_or_zero<0x4E, 0xF>(v[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp_or_zero<0x141, 0xF>(v[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp_or_zero<0x140, 0xF>(v[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp_or_zero<0x142, 0xA>(v[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp_or_zero<0x143, 0xC>(v[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i]), 63));
+}
+
+// Maximum over the 64 lanes with DPP moves (lanes a move does not reach keep
+// their own value); broadcast from lane 63.
+template <unsigned CTRL, unsigned ROW_MASK>
+__device__ __forceinline__ float dpp_or_self(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp_or_self<0xB1, 0xF>(v));
+    v = fmaxf(v, dpp_or_self<0x4E, 0xF>(v));
+    v = fmaxf(v, dpp_or_self<0x141, 0xF>(v));
+    v = fmaxf(v, dpp_or_self<0x140, 0xF>(v));
+    v = fmaxf(v, dpp_or_self<0x142, 0xA>(v));
+    v = fmaxf(v, dpp_or_self<0x143, 0xC>(v));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 __device__ __forceinline__ float block_sum(float v) {
     __shared__ float red[kWaves];
     v = wave_sum(v);

@@ -494,12 +494,10 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                         for (int q = 0; q < 4; ++q) acc[q] = dot8(wQ[q * 2 + c], x8, acc[q]);
                     }
                     const float rinv = 1.0f / sqrtf(row_ss(par, r) / static_cast<float>(DP) + eps);
+                    wave_sums(acc);
                     float v = 0.f;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float t = wave_sum(acc[q]) * rinv;
-                        v = (lane == q) ? t : v;
-                    }
+                    for (int q = 0; q < 4; ++q) v = (lane == q) ? acc[q] * rinv : v;
                     if (lane < 4) st_rec(rc.QKV + static_cast<size_t>(r) * NQKV + 16 * wg + 4 * wave + lane, v, tag_of(ph));
                 }
                 ++ph;
@@ -547,10 +545,15 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                         const int r = (s == 1) ? pi * B + b : b;
                         const float* nd = hist + 4096 + pi * 512;
                         const float c0 = rope_s[0][p * (HD / 2) + lane], s0 = rope_s[1][p * (HD / 2) + lane];
+                        // key and this wave's query: per-head RMSNorm (both sums
+                        // at once), rotate-half RoPE (pair lane, lane + 64)
+                        const float k0 = nd[256 + lane], k1 = nd[256 + lane + 64];
+                        const float x0 = nd[wave * HD + lane], x1 = nd[wave * HD + lane + 64];
+                        float sq[2] = {k0 * k0 + k1 * k1, x0 * x0 + x1 * x1};
+                        wave_sums(sq);
                         float kv0, kv1;
-                        {   // key: per-head RMSNorm, rotate-half RoPE (pair lane, lane+64)
-                            const float k0 = nd[256 + lane], k1 = nd[256 + lane + 64];
-                            const float rv = 1.0f / sqrtf(wave_sum(k0 * k0 + k1 * k1) / static_cast<float>(HD) + eps);
+                        {
+                            const float rv = 1.0f / sqrtf(sq[0] / static_cast<float>(HD) + eps);
                             const float a0 = gk[lane] * (k0 * rv), a1 = gk[lane + 64] * (k1 * rv);
                             kv0 = a0 * c0 - a1 * s0;
                             kv1 = a1 * c0 + a0 * s0;
@@ -570,8 +573,7 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                         hist[2048 + p * HD + lane] = vv0;
                         hist[2048 + p * HD + lane + 64] = vv1;
                         {
-                            const float x0 = nd[wave * HD + lane], x1 = nd[wave * HD + lane + 64];
-                            const float rv = 1.0f / sqrtf(wave_sum(x0 * x0 + x1 * x1) / static_cast<float>(HD) + eps);
+                            const float rv = 1.0f / sqrtf(sq[1] / static_cast<float>(HD) + eps);
                             const float a0 = gq[lane] * (x0 * rv), a1 = gq[lane + 64] * (x1 * rv);
                             qb[lane] = a0 * c0 - a1 * s0;
                             qb[lane + 64] = a1 * c0 + a0 * s0;
@@ -592,18 +594,18 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                         sc += dpp_or_zero<0xB1, 0xF>(sc);   // lanes of a quad: one key
                         sc += dpp_or_zero<0x4E, 0xF>(sc);
                         sc = (kt <= p) ? sc * m.attn_scale : -__builtin_huge_valf();
-                        float mx = sc;
-#pragma unroll
-                        for (int off = 32; off >= 4; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+                        const float mx = wave_max(sc);
                         const float e = (kt <= p) ? expf(sc - mx) : 0.f;
                         const float den = wave_sum((lane & 3) == 0 ? e : 0.f);
-                        if ((lane & 3) == 0 && kt < kPositions) eb[kt] = e;
-                        // weighted values
+                        if ((lane & 3) == 0) eb[kt] = e;
+                        // weighted values (weights are 0 beyond p)
                         float o0 = 0.f, o1 = 0.f;
-                        for (int t = 0; t <= p; ++t) {
+#pragma unroll
+                        for (int t = 0; t < kPositions; ++t) {
+                            const int tt = t <= p ? t : p;
                             const float w = eb[t];
-                            o0 = fmaf(w, hist[2048 + t * HD + lane], o0);
-                            o1 = fmaf(w, hist[2048 + t * HD + lane + 64], o1);
+                            o0 = fmaf(w, hist[2048 + tt * HD + lane], o0);
+                            o1 = fmaf(w, hist[2048 + tt * HD + lane + 64], o1);
                         }
                         uint64_t* orow = rc.AO + static_cast<size_t>(r) * QD + h * HD;
                         st_rec(orow + lane, o0 / den, tag_of(ph));
@@ -664,11 +666,13 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                         }
                     }
                     const float rinv = 1.0f / sqrtf(row_ss(par, r) / static_cast<float>(DP) + eps);
+                    float gu[6] = {ag[0], ag[1], ag[2], au[0], au[1], au[2]};
+                    wave_sums(gu);
                     float v = 0.f;
 #pragma unroll
                     for (int q = 0; q < 3; ++q) {
-                        const float gv = wave_sum(ag[q]) * rinv;
-                        const float uv = wave_sum(au[q]) * rinv;
+                        const float gv = gu[q] * rinv;
+                        const float uv = gu[3 + q] * rinv;
                         const float hv = (gv / (1.0f + expf(-gv))) * uv;
                         v = (lane == q) ? hv : v;
                     }
@@ -735,8 +739,10 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                         acc1 = dot8(wL[2 + c], x8, acc1);
                     }
                     const float rinv = 1.0f / sqrtf(row_ss(par, b) / static_cast<float>(DP) + eps);
-                    const float l0 = wave_sum(acc0) * rinv;
-                    const float l1 = wave_sum(acc1) * rinv;
+                    float lg[2] = {acc0, acc1};
+                    wave_sums(lg);
+                    const float l0 = lg[0] * rinv;
+                    const float l1 = lg[1] * rinv;
                     if (a.logits_out && lane < 2)
                         a.logits_out[(static_cast<size_t>(b) * kSteps + (s - 1)) * V + v0 + lane] = lane ? l1 : l0;
                     const bool second = ordered_bits(l1) > ordered_bits(l0);
