@@ -298,3 +298,45 @@ def test_tiled_graph_replays_match_stream_path():
         again = gpu_frame(pred, H[0], q0[0], logits=False, tiled=True)
         np.testing.assert_array_equal(again["tokens"], graph["tokens"])
         np.testing.assert_array_equal(again["embsum"], graph["embsum"])
+
+
+@pytest.mark.parametrize("name,tiled", [("tiny_bf16", True), ("b16", False)], ids=["batched", "dataflow"])
+def test_flags_on_fast_paths(name, tiled):
+    """Out-of-range q0 (graph and direct launches) and forced tokens raise the
+    sticky flag, are read as token 0, and leave the next call clean."""
+    wl, W, model, pred = workload(name)
+    dev = _dev()
+    g = wl.geom
+    B = 3 if tiled else 2
+    H, q0 = synth.make_inputs(g, B, 1, 8800)
+    bad = q0[0].copy()
+    bad[B - 1] = -5
+    fixed = bad.copy()
+    fixed[B - 1] = 0
+    ref = gpu_frame(pred, H[0], fixed, logits=False, tiled=tiled)
+    Ht = torch.from_numpy(H[0]).to(dev)
+    tok = torch.zeros((B, 15), dtype=torch.int32, device=dev)
+    emb = torch.zeros((B, g.d_talker), device=dev)
+    for hooks in (False, True):
+        lg = torch.zeros((B, 15, g.vocab), device=dev) if hooks else None
+        pred.run(Ht, torch.from_numpy(bad).to(dev), tok, emb, logits_out=lg, tiled=tiled)
+        torch.cuda.synchronize()
+        assert pred.get_error() == 1
+        assert pred.get_error() == 0
+        np.testing.assert_array_equal(tok.cpu().numpy(), ref["tokens"])
+        np.testing.assert_array_equal(emb.cpu().numpy(), ref["embsum"])
+    force = np.zeros((B, 15), dtype=np.int32)
+    force[0, 4] = g.vocab
+    ft = torch.from_numpy(force).to(dev)
+    pred.run(Ht, torch.from_numpy(fixed).to(dev), tok, emb, force=ft, tiled=tiled)
+    torch.cuda.synchronize()
+    assert pred.get_error() == 2
+    assert pred.get_error() == 0
+
+
+def test_tiled_full_max_batch():
+    wl, W, model, pred = workload("tiny_bf16")
+    B = pred.max_batch
+    H, q0 = synth.make_inputs(wl.geom, B, 1, 9901)
+    rows = np.array([0, B // 2, B - 1])
+    check_against_oracle("tiled B=max", model, pred, H[0], q0[0], rows, tiled=True)
