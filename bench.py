@@ -31,7 +31,7 @@ METRIC = "code-predictor frames/sec (15 tokens each) at B=1/16/128; % HBM/MFMA r
 
 
 def bytes_per_weight(dtype: str) -> float:
-    return {"f32": 4.0, "bf16": 2.0, "q8_0": 34.0 / 32.0}[dtype]
+    return {"f32": 4.0, "bf16": 2.0, "q8_0": 34.0 / 32.0, "q4_0": 18.0 / 32.0}[dtype]
 
 
 def algorithmic_bytes(g: synth.Geometry) -> int:
@@ -98,7 +98,7 @@ def select_driver(g, B: int, args) -> str:
         return "dataflow"
     qd = g.n_q_heads * g.head_dim
     nqkv = (g.n_q_heads + 2 * g.n_kv_heads) * g.head_dim
-    if (g.weight_dtype in ("bf16", "q8_0") and g.d_talker % 256 == 0 and g.d_model % 256 == 0 and g.d_model <= 4096 and g.d_talker <= 4096 and
+    if (g.weight_dtype in ("bf16", "q8_0", "q4_0") and g.d_talker % 256 == 0 and g.d_model % 256 == 0 and g.d_model <= 4096 and g.d_talker <= 4096 and
             qd % 256 == 0 and g.d_ffn % 256 == 0 and nqkv % 32 == 0 and g.vocab % 32 == 0):
         return "tiled"
     return "generic"

@@ -66,10 +66,16 @@ typedef enum {
 typedef enum {
     QP_WEIGHT_F32 = 0,
     QP_WEIGHT_BF16 = 1,   /* uint16 bfloat16 bit patterns                     */
-    QP_WEIGHT_Q8_0 = 2    /* GGUF Q8_0: per row, in/32 blocks of 34 bytes =
+    QP_WEIGHT_Q8_0 = 2,   /* GGUF Q8_0: per row, in/32 blocks of 34 bytes =
                              little-endian f16 scale d, then 32 int8 codes q;
                              value = q * d (rightkit-qts README: Q8_0 through
                              gguf's quantizer)                                 */
+    QP_WEIGHT_Q4_0 = 3    /* GGUF Q4_0: per row, in/32 blocks of 18 bytes =
+                             little-endian f16 scale d, then 16 bytes, byte j
+                             holding the 4-bit code c of element j (low
+                             nibble) and of element j + 16 (high nibble);
+                             value = (c - 8) * d (forpes.ru RustTTS article,
+                             "Поддержка GGUF-квантизации": q4_0 GGUF files)  */
 } qp_weight_dtype;
 
 /* Storage of the 16 codebook tables [V, d_talker]. */
@@ -94,7 +100,8 @@ typedef struct {
     int32_t n_codebooks;  /* must be QP_N_CODEBOOKS                           */
     float rms_eps;        /* attention.layer_norm_rms_epsilon, > 0            */
     float rope_base;      /* rope.freq_base, > 1                              */
-    int32_t weight_dtype; /* qp_weight_dtype                                  */
+    int32_t weight_dtype; /* qp_weight_dtype (Q8_0, Q4_0: every input width a
+                             multiple of 32)                                 */
     int32_t emb_format;   /* qp_emb_format                                    */
     int32_t max_batch;    /* largest B a later qp_run_frames may pass, >= 1   */
 } qp_geometry;
@@ -164,7 +171,7 @@ qp_status qp_run_frames(qp_handle* h, int32_t B, const float* H,
                                    specialised one exists                      */
 #define QP_FLAG_TILED 0x4u      /* the batched matrix-core path (one kernel per
                                    phase, projections on MFMA) for any B; only
-                                   for bf16 or Q8_0 weights with dT, dP, nq*hd
+                                   for bf16, Q8_0 or Q4_0 weights with dT, dP, nq*hd
                                    and F multiples of 256, dP and dT <= 4096, nqkv and V multiples
                                    of 32 (else QP_ERR_INVALID_ARG); excludes
                                    the other flags.

@@ -34,6 +34,11 @@ descriptions of the model and of the exported predictor):
   "Проблема 1: Формат codebook'ов").
 * Q8_0 rows are blocks of 32 along the input dimension, an f16 scale then 32
   int8 codes, value = code * scale (the README's Q8_0 export through gguf).
+* Q4_0 (the RustTTS article loads q4_0 GGUF files, "Поддержка
+  GGUF-квантизации"; the block layout is read as GGUF's): blocks of 32 along
+  the input dimension, an f16 scale then 16 bytes of 4-bit codes (element j
+  in the low nibble of byte j, element j + 16 in the high nibble), value =
+  (code - 8) * scale.
 
 Readings taken where the pages are silent (each listed with its reason in the
 design notes): prefill is [H, E_0[q0]] at positions 0 and 1; positions restart
@@ -72,6 +77,20 @@ def dequant_q8_0(packed: np.ndarray, in_features: int) -> np.ndarray:
     return (q * d).reshape(out_f, in_features)
 
 
+def dequant_q4_0(packed: np.ndarray, in_features: int) -> np.ndarray:
+    """GGUF Q4_0: each 18-byte block is a little-endian f16 scale d followed
+    by 16 bytes; byte j carries the 4-bit code of element j (low nibble) and
+    of element j + 16 (high nibble), and a code c stands for (c - 8) * d.
+    Blocks run along the input dimension of a row-major [out, in] matrix."""
+    out_f = packed.shape[0]
+    nb = in_features // 32
+    blocks = packed.reshape(out_f, nb, 18)
+    d = blocks[..., 0:2].copy().view(np.float16).astype(np.float64)  # [out, nb, 1]
+    qs = blocks[..., 2:].astype(np.int64)                             # [out, nb, 16]
+    codes = np.concatenate([qs & 15, qs >> 4], axis=-1)               # elements 0..15, 16..31
+    return ((codes - 8).astype(np.float64) * d).reshape(out_f, in_features)
+
+
 def materialise_matrix(m: np.ndarray, dtype: str, in_features: int) -> np.ndarray:
     if dtype == "f32":
         return m.astype(np.float64)
@@ -79,6 +98,8 @@ def materialise_matrix(m: np.ndarray, dtype: str, in_features: int) -> np.ndarra
         return bf16_bits_to_f64(m)
     if dtype == "q8_0":
         return dequant_q8_0(m, in_features)
+    if dtype == "q4_0":
+        return dequant_q4_0(m, in_features)
     raise ValueError(dtype)
 
 

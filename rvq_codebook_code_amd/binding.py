@@ -35,7 +35,7 @@ QP_FLAG_STEPWISE = 0x1
 QP_FLAG_GENERIC = 0x2
 QP_FLAG_TILED = 0x4
 
-WEIGHT_DTYPES = {"f32": 0, "bf16": 1, "q8_0": 2}
+WEIGHT_DTYPES = {"f32": 0, "bf16": 1, "q8_0": 2, "q4_0": 3}
 EMB_FORMATS = {"f32": 0, "bf16": 1, "ema": 2}
 
 EXPORTED = ["qp_create", "qp_run_frames", "qp_run_frames_ex", "qp_get_error",

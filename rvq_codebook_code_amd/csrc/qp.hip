@@ -187,6 +187,7 @@ struct qp_handle {
     uint32_t seq = 0;
     // batched matrix-core path
     bool tiled_ok = false;
+    bool q4 = false;   // Q4_0 weights: 4-bit fragments on the batched path
     std::vector<LayerDev> layers_host;
     qp::tiled::FMat t_proj{};
     std::vector<qp::tiled::FMat> t_qkv, t_o, t_gate, t_up, t_down;
@@ -309,44 +310,68 @@ struct Uploader {
             }
             return hm;
         }
+        // Q8_0 / Q4_0: int8 codes (Q4_0: code - 8) and fp32 block scales
         const int nb = K / 32;
+        const size_t bbytes = wt == WT_Q4 ? 18 : 34;
         hm.w.resize(hm.N * K);
         hm.scale.resize(hm.N * nb);
         size_t row = 0;
         for (size_t i = 0; i < parts.size(); ++i) {
             const uint8_t* src = static_cast<const uint8_t*>(parts[i]);
             for (int r = 0; r < rows[i]; ++r, ++row) {
-                const uint8_t* rp = src + static_cast<size_t>(r) * nb * 34;
+                const uint8_t* rp = src + static_cast<size_t>(r) * nb * bbytes;
                 for (int bk = 0; bk < nb; ++bk) {
-                    const uint8_t* blk = rp + static_cast<size_t>(bk) * 34;
+                    const uint8_t* blk = rp + static_cast<size_t>(bk) * bbytes;
                     hm.scale[row * nb + bk] = half_to_float(static_cast<uint16_t>(blk[0] | (blk[1] << 8)));
-                    std::memcpy(&hm.w[row * K + static_cast<size_t>(bk) * 32], blk + 2, 32);
+                    int8_t* dst = reinterpret_cast<int8_t*>(&hm.w[row * K + static_cast<size_t>(bk) * 32]);
+                    if (wt == WT_Q4) {
+                        for (int j = 0; j < 16; ++j) {
+                            dst[j] = static_cast<int8_t>((blk[2 + j] & 15) - 8);
+                            dst[j + 16] = static_cast<int8_t>((blk[2 + j] >> 4) - 8);
+                        }
+                    } else {
+                        std::memcpy(dst, blk + 2, 32);
+                    }
                 }
             }
         }
         return hm;
     }
+    // Row-major device copy (Q4_0 as int8 codes with block scales, i.e. the
+    // Q8_0 layout)
     Mat rowmajor(const HostMat& hm) {
         Mat out{nullptr, nullptr};
         out.w = upload(hm.w.data(), hm.w.size());
-        if (hm.wt == WT_Q8) out.scale = static_cast<const float*>(upload(hm.scale.data(), hm.scale.size() * 4));
+        if (hm.wt == WT_Q8 || hm.wt == WT_Q4)
+            out.scale = static_cast<const float*>(upload(hm.scale.data(), hm.scale.size() * 4));
         return out;
     }
     // MFMA fragment order: fragment (n/16, k/32) holds, for lane
-    // l = (n % 16) + 16 * ((k % 32) / 8), the 8 elements k .. k+7 of row n.
+    // l = (n % 16) + 16 * ((k % 32) / 8), the 8 elements k .. k+7 of row n
+    // (bf16: 16 bytes; Q8_0: 8 int8 codes; Q4_0: 8 codes + 8 as nibbles of
+    // one 32-bit word, element k + i in bits 4i .. 4i+3).
     qp::tiled::FMat fragments(const HostMat& hm) {
         qp::tiled::FMat out{nullptr, nullptr};
         const size_t N = hm.N, K = static_cast<size_t>(hm.K), KB = K / 32;
         const size_t esz = hm.wt == WT_BF16 ? 2 : 1;
-        std::vector<uint8_t> f(hm.w.size());
+        const size_t chunk = hm.wt == WT_BF16 ? 16 : (hm.wt == WT_Q8 ? 8 : 4);
+        std::vector<uint8_t> f(N / 16 * KB * 64 * chunk);
         for (size_t nb = 0; nb < N / 16; ++nb)
             for (size_t kb = 0; kb < KB; ++kb)
                 for (size_t lane = 0; lane < 64; ++lane) {
                     const size_t n = nb * 16 + (lane & 15), k = kb * 32 + (lane >> 4) * 8;
-                    std::memcpy(&f[((nb * KB + kb) * 64 + lane) * 8 * esz], &hm.w[(n * K + k) * esz], 8 * esz);
+                    uint8_t* dst = &f[((nb * KB + kb) * 64 + lane) * chunk];
+                    if (hm.wt == WT_Q4) {
+                        uint32_t word = 0;
+                        for (int i = 0; i < 8; ++i)
+                            word |= static_cast<uint32_t>((static_cast<int8_t>(hm.w[n * K + k + i]) + 8) & 15) << (4 * i);
+                        std::memcpy(dst, &word, 4);
+                    } else {
+                        std::memcpy(dst, &hm.w[(n * K + k) * esz], 8 * esz);
+                    }
                 }
         out.w = upload(f.data(), f.size());
-        if (hm.wt == WT_Q8) {
+        if (hm.wt == WT_Q8 || hm.wt == WT_Q4) {
             std::vector<float> sc(hm.scale.size());
             for (size_t nb = 0; nb < N / 16; ++nb)
                 for (size_t kb = 0; kb < KB; ++kb)
@@ -382,13 +407,13 @@ qp_status validate_geometry(const qp_geometry* g) {
         return fail(QP_ERR_GEOMETRY, "rms_eps and rope_base must be positive");
     if (g->max_batch < 1 || g->max_batch > 65536)
         return fail(QP_ERR_GEOMETRY, "max_batch must be in [1, 65536]");
-    if (g->weight_dtype < QP_WEIGHT_F32 || g->weight_dtype > QP_WEIGHT_Q8_0)
+    if (g->weight_dtype < QP_WEIGHT_F32 || g->weight_dtype > QP_WEIGHT_Q4_0)
         return fail(QP_ERR_DTYPE, "unknown weight_dtype");
     if (g->emb_format < QP_EMB_F32 || g->emb_format > QP_EMB_EMA)
         return fail(QP_ERR_DTYPE, "unknown emb_format");
     const int qd = g->n_q_heads * g->head_dim;
     const int ins[4] = {g->d_talker, g->d_model, qd, g->d_ffn};
-    const int align = g->weight_dtype == QP_WEIGHT_Q8_0 ? 32 : 8;
+    const int align = (g->weight_dtype == QP_WEIGHT_Q8_0 || g->weight_dtype == QP_WEIGHT_Q4_0) ? 32 : 8;
     for (int k : ins) {
         if (k % align != 0)
             return fail(QP_ERR_SHAPE, "every input width (dT, dP, nq*hd, F) must be a multiple of " +
@@ -714,6 +739,8 @@ qp_status launch_frame(qp_handle* h, const RunArgs& a, hipStream_t stream, bool 
     if constexpr (WT == WT_BF16 || WT == WT_Q8) {
         if (tiled || (!stepwise && !generic && h->tiled_ok && a.B > 2)) {
             const bool hooks = a.force || a.logits_out || a.taps;
+            if (WT == WT_Q8 && h->q4)
+                return hooks ? launch_tiled<WT_Q4>(h, a, stream) : launch_tiled_graph<WT_Q4>(h, a, stream);
             return hooks ? launch_tiled<WT>(h, a, stream) : launch_tiled_graph<WT>(h, a, stream);
         }
     }
@@ -822,18 +849,20 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
     m.hd = g->head_dim;
     m.F = g->d_ffn;
     m.V = g->vocab;
-    m.wt = g->weight_dtype;
+    // Q4_0 weights run as int8 codes on every path but the batched one
+    h->q4 = g->weight_dtype == QP_WEIGHT_Q4_0;
+    m.wt = h->q4 ? WT_Q8 : g->weight_dtype;
     m.nqkv = (m.nq + 2 * m.nkv) * m.hd;
     m.max_batch = g->max_batch;
     m.eps = g->rms_eps;
     m.attn_scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(m.hd)));
 
     Uploader up{h};
-    const int wt = m.wt;
+    const int wt = h->q4 ? WT_Q4 : m.wt;   // storage format of the host weights
     // batched matrix-core path: bf16 or Q8_0 weights whose widths tile into
     // 32 x 256 blocks (every K split four ways into whole 32-wide blocks,
     // two at a time; every N a whole number of 32-column tiles)
-    h->tiled_ok = (wt == WT_BF16 || wt == WT_Q8) && m.dT % 256 == 0 && m.dP % 256 == 0 && m.dP <= 4096 && m.dT <= 4096 &&
+    h->tiled_ok = (wt == WT_BF16 || wt == WT_Q8 || wt == WT_Q4) && m.dT % 256 == 0 && m.dP % 256 == 0 && m.dP <= 4096 && m.dT <= 4096 &&
                   (m.nq * m.hd) % 256 == 0 && m.F % 256 == 0 && m.nqkv % 32 == 0 && m.V % 32 == 0;
     {
         const Uploader::HostMat hm = Uploader::build({w->proj_w}, {m.dP}, m.dT, wt);

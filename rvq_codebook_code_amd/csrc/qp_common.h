@@ -15,7 +15,9 @@ constexpr int kLdsFloats = 16384;        // 64 KiB workgroup scratch
 constexpr int kMaxHeadDim = 256;
 constexpr int kMaxRowsPerChunk = 4;
 
-enum WeightType : int { WT_F32 = 0, WT_BF16 = 1, WT_Q8 = 2 };
+// WT_Q4 only names the 4-bit fragment layout of the batched path; elsewhere
+// Q4_0 weights are held as int8 codes (code - 8) with WT_Q8's block scales.
+enum WeightType : int { WT_F32 = 0, WT_BF16 = 1, WT_Q8 = 2, WT_Q4 = 3 };
 
 // Device error flag bits (also documented in qp.h).
 constexpr unsigned kErrBadQ0 = 1u;

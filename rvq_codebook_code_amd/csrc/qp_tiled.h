@@ -23,10 +23,12 @@
 //    of x^2 over 32-column tiles; the reader's epilogue adds those sums up
 //    (in tile order) for the row scale.  The operand is then a plain bf16
 //    load, and the gain rides on it while the row scale rides on the output.
-//  * Q8_0 codes are integers in [-128, 127], exact in bf16; one MFMA covers
-//    exactly one 32-wide quantisation block, whose f16 scale (stored as fp32)
-//    multiplies the block's partial sum before accumulation.  The weights
-//    therefore enter the product exactly.
+//  * Q8_0 codes are integers in [-128, 127] and Q4_0 codes minus 8 are in
+//    [-8, 7], both exact in bf16; one MFMA covers exactly one 32-wide
+//    quantisation block, whose f16 scale (stored as fp32) multiplies the
+//    block's partial sum before accumulation.  The weights therefore enter
+//    the product exactly.  Q4_0 fragments hold a lane's 8 codes in one
+//    32-bit word (256 B per fragment).
 //  * A workgroup (4 waves) owns a tile of 16*RT rows x 32 output columns
 //    (2 fragments wide; for SwiGLU the gate and up fragments of the same 16
 //    columns).  The 4 waves split K and their partial tiles are summed through
@@ -54,8 +56,9 @@ constexpr int kMaxKS = 4;     // largest split of K across workgroups
 
 // A weight matrix [N][K] in fragment order (see the file comment).
 struct FMat {
-    const void* w;        // bf16: uint16 [N/16][K/32][64][8]; Q8_0: int8 [N/16][K/32][64][8]
-    const float* scale;   // Q8_0: [N/16][K/32][16]; bf16: null
+    const void* w;        // bf16: uint16 [N/16][K/32][64][8]; Q8_0: int8 [N/16][K/32][64][8];
+                          // Q4_0: uint32 [N/16][K/32][64], nibble i = code of element i
+    const float* scale;   // Q8_0, Q4_0: [N/16][K/32][16]; bf16: null
 };
 
 enum Src : int { SRC_F32 = 0, SRC_BF16 = 1, SRC_BF16_NORM = 2 };
@@ -133,6 +136,18 @@ __device__ __forceinline__ uint16_t to_bf16(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// 8 Q4_0 codes (nibble i of w, value code - 8) -> 8 bf16 (exact)
+__device__ __forceinline__ uint4 q4x8(uint32_t w) {
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float lo = static_cast<float>(static_cast<int>((w >> (8 * i)) & 15u) - 8);
+        const float hi = static_cast<float>(static_cast<int>((w >> (8 * i + 4)) & 15u) - 8);
+        o[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 // int8 code -> bf16 bits (exact: |q| <= 128 needs 8 significant bits)
 __device__ __forceinline__ uint32_t q8pair(uint32_t w, int sh) {
     const float lo = static_cast<float>(static_cast<int>(w << (24 - sh)) >> 24);
@@ -189,8 +204,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(GemmArgs g) {
         const FMat& W = (EPI == EPI_SWIGLU && c == 1) ? g.w1 : g.w0;
         nb[c] = (EPI == EPI_SWIGLU) ? bx : bx * CT + c;
         const size_t frag0 = static_cast<size_t>(nb[c]) * KB;
-        wp[c] = static_cast<const uint8_t*>(W.w) + frag0 * 64 * (WT == WT_Q8 ? 8 : 16);
-        sp[c] = (WT == WT_Q8) ? W.scale + frag0 * 16 : nullptr;
+        wp[c] = static_cast<const uint8_t*>(W.w) + frag0 * 64 * (WT == WT_Q8 ? 8 : (WT == WT_Q4 ? 4 : 16));
+        sp[c] = (WT == WT_Q8 || WT == WT_Q4) ? W.scale + frag0 * 16 : nullptr;
     }
 
     // this lane's A row (per row tile) and k offset inside a block
@@ -251,6 +266,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(GemmArgs g) {
         uint4 av[UU][RT];
         uint4 wv[UU][CT];
         uint2 wq[UU][CT];
+        uint32_t w4[UU][CT];
         float ws[UU][CT];
 #pragma unroll
         for (int u = 0; u < UU; ++u) {
@@ -259,6 +275,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(GemmArgs g) {
             for (int c = 0; c < CT; ++c) {
                 if constexpr (WT == WT_Q8) {
                     wq[u][c] = *reinterpret_cast<const uint2*>(wp[c] + (static_cast<size_t>(kb + u) * 64 + lane) * 8);
+                    ws[u][c] = sp[c][(kb + u) * 16 + (lane & 15)];
+                } else if constexpr (WT == WT_Q4) {
+                    w4[u][c] = *reinterpret_cast<const uint32_t*>(wp[c] + (static_cast<size_t>(kb + u) * 64 + lane) * 4);
                     ws[u][c] = sp[c][(kb + u) * 16 + (lane & 15)];
                 } else {
                     wv[u][c] = *reinterpret_cast<const uint4*>(wp[c] + (static_cast<size_t>(kb + u) * 64 + lane) * 16);
@@ -290,6 +309,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(GemmArgs g) {
                 if constexpr (WT == WT_Q8) {
                     w8 = make_uint4(q8pair(wq[u][c].x, 0), q8pair(wq[u][c].x, 16), q8pair(wq[u][c].y, 0),
                                     q8pair(wq[u][c].y, 16));
+                } else if constexpr (WT == WT_Q4) {
+                    w8 = q4x8(w4[u][c]);
                 } else {
                     w8 = wv[u][c];
                 }
@@ -297,7 +318,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(GemmArgs g) {
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
                     const bf16x8_t ab = __builtin_bit_cast(bf16x8_t, av[u][rt]);
-                    if constexpr (WT == WT_Q8) {
+                    if constexpr (WT == WT_Q8 || WT == WT_Q4) {
                         const f32x4_t p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, wb, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
                         const float sc = ws[u][c];
                         acc[rt][c] = f32x4_t{fmaf(sc, p[0], acc[rt][c][0]), fmaf(sc, p[1], acc[rt][c][1]),

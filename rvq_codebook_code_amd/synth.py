@@ -50,7 +50,7 @@ class Geometry:
     vocab: int          # V, per codebook
     rms_eps: float
     rope_base: float
-    weight_dtype: str   # 'f32' | 'bf16' | 'q8_0'   (every linear)
+    weight_dtype: str   # 'f32' | 'bf16' | 'q8_0' | 'q4_0'   (every linear)
     emb_format: str     # 'f32' | 'bf16' | 'ema'    (the 16 codebook tables)
     n_codebooks: int = N_CODEBOOKS
 
@@ -114,6 +114,19 @@ WORKLOADS: Dict[str, Workload] = {
                  emb_format="ema"),
         batch=20, frames=4, weight_seed=1102, input_seed=2102,
         description="tiny predictor, Q8_0 linears + EMA codebooks, B=20 x 4 frames"),
+    "tiny_q4": Workload(
+        "tiny_q4",
+        Geometry(d_talker=512, d_model=256, n_layers=2, n_q_heads=4,
+                 n_kv_heads=2, head_dim=64, d_ffn=768, vocab=256,
+                 rms_eps=1e-6, rope_base=1e4, weight_dtype="q4_0",
+                 emb_format="bf16"),
+        batch=20, frames=4, weight_seed=1103, input_seed=2103,
+        description="tiny predictor, Q4_0 linears, bf16 tables, B=20 x 4 frames"),
+    # Q4_0 weights on the 1.7B-shaped predictor (the first "next" row)
+    "q4_b16": Workload(
+        "q4_b16", Geometry(**_PRED_17B, weight_dtype="q4_0", emb_format="bf16"),
+        batch=16, frames=64, weight_seed=1006, input_seed=2006,
+        description="1.7B-shaped predictor, Q4_0 linears, bf16 tables, B=16 x 64 frames"),
 }
 
 
@@ -164,6 +177,36 @@ def pack_q8_0(x: np.ndarray) -> np.ndarray:
     return packed.reshape(out_f, nb * Q8_BLOCK_BYTES)
 
 
+Q4_BLOCK_BYTES = 18
+
+
+def pack_q4_0(x: np.ndarray) -> np.ndarray:
+    """Pack a row-major ``[out, in]`` fp32 matrix into GGUF-style Q4_0 rows.
+
+    Every row becomes ``in/32`` blocks of 18 bytes along ``in``: the f16
+    scale d = max|x|/7 (rounded to f16), then 16 bytes whose byte j holds the
+    4-bit code of element j in its low nibble and of element j + 16 in its
+    high nibble; a code is c = clamp(round-half-away(x/d), -8, 7) + 8, so the
+    value is (c - 8) * d (all codes 8 when d == 0).  Returns uint8
+    ``[out, in/32*18]``.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out_f, in_f = x.shape
+    assert in_f % Q8_BLOCK == 0, "Q4_0 needs in-features divisible by 32"
+    nb = in_f // Q8_BLOCK
+    blk = x.reshape(out_f, nb, Q8_BLOCK).astype(np.float64)
+    amax = np.abs(blk).max(axis=-1)
+    d16 = (amax / 7.0).astype(np.float16)
+    d = d16.astype(np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = np.where(d[..., None] > 0, blk / d[..., None], 0.0)
+    c = (np.clip(np.sign(t) * np.floor(np.abs(t) + 0.5), -8, 7) + 8).astype(np.uint8)
+    packed = np.empty((out_f, nb, Q4_BLOCK_BYTES), dtype=np.uint8)
+    packed[..., 0:2] = d16.view(np.uint8).reshape(out_f, nb, 2)
+    packed[..., 2:] = c[..., :16] | (c[..., 16:] << 4)
+    return packed.reshape(out_f, nb * Q4_BLOCK_BYTES)
+
+
 def _matrix(rng: np.random.Generator, out_f: int, in_f: int, dtype: str):
     w = (rng.standard_normal((out_f, in_f), dtype=np.float32) * np.float32(0.02))
     if dtype == "f32":
@@ -172,6 +215,8 @@ def _matrix(rng: np.random.Generator, out_f: int, in_f: int, dtype: str):
         return f32_to_bf16_bits(w)
     if dtype == "q8_0":
         return pack_q8_0(w)
+    if dtype == "q4_0":
+        return pack_q4_0(w)
     raise ValueError(dtype)
 
 

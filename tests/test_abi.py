@@ -73,8 +73,9 @@ def test_geometry_validation(lib, field, value, status):
     assert lib.qp_last_error()
 
 
-def test_q8_0_needs_32_aligned_widths(lib):
-    g = bd.make_geometry(synth.scaled_geometry(_tiny(), weight_dtype="q8_0", d_ffn=776), 4)
+@pytest.mark.parametrize("dtype", ["q8_0", "q4_0"])
+def test_block_formats_need_32_aligned_widths(lib, dtype):
+    g = bd.make_geometry(synth.scaled_geometry(_tiny(), weight_dtype=dtype, d_ffn=776), 4)
     h = C.c_void_p()
     assert lib.qp_create(C.byref(bd.QpWeights()), C.byref(g), 0, C.byref(h)) == bd.QP_ERR_SHAPE
 

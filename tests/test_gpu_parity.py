@@ -19,7 +19,7 @@ from rvq_codebook_code_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-4, "bf16": 3e-2, "q8_0": 3e-2}
+TOL = {"f32": 1e-4, "bf16": 3e-2, "q8_0": 3e-2, "q4_0": 3e-2}
 MARGIN = 0.05
 
 
@@ -229,7 +229,7 @@ def test_dataflow_kernel_taps_and_repeat():
 # the batched matrix-core path (bf16 / Q8_0 weights, any B)
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["tiny_bf16", "tiny_q8ema"])
+@pytest.mark.parametrize("name", ["tiny_bf16", "tiny_q8ema", "tiny_q4"])
 def test_tiled_tiny_all_frames(name):
     wl, W, model, pred = workload(name)
     H, q0 = synth.make_inputs(wl.geom, wl.batch, wl.frames, wl.input_seed)
@@ -340,3 +340,17 @@ def test_tiled_full_max_batch():
     H, q0 = synth.make_inputs(wl.geom, B, 1, 9901)
     rows = np.array([0, B // 2, B - 1])
     check_against_oracle("tiled B=max", model, pred, H[0], q0[0], rows, tiled=True)
+
+
+def test_q4_generic_path_and_full_size():
+    """Q4_0 on the generic path (int8 codes) against the oracle, the batched
+    path against it within tolerance, and the 1.7B-shaped Q4_0 workload on
+    sampled rows."""
+    wl, W, model, pred = workload("tiny_q4")
+    H, q0 = synth.make_inputs(wl.geom, 4, 1, 7300)
+    ref, got = check_against_oracle("tiny_q4 generic", model, pred, H[0], q0[0], np.arange(4))
+    tiled = gpu_frame(pred, H[0], q0[0], force=ref["tokens"].astype(np.int32), tiled=True)
+    assert np.abs(tiled["logits"] - got["logits"]).max() <= TOL["q4_0"]
+    wl, W, model, pred = workload("q4_b16")
+    H, q0 = synth.make_inputs(wl.geom, wl.batch, 2, wl.input_seed)
+    check_against_oracle("q4_b16", model, pred, H[1], q0[1], np.array([0, 9, 15]))

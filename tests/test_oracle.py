@@ -103,6 +103,35 @@ def test_q8_0_round_trip_error_bound():
     assert np.all(w[0, :32] == 0)
 
 
+def test_q4_0_dequant_hand_built_block():
+    """An 18-byte block: f16 scale 0.25, byte j = code(j) | code(j + 16) << 4
+    with code(j) = j for j < 16 and code(16 + j) = 15 - j; value (code - 8) * 0.25."""
+    lo = list(range(16))
+    hi = [15 - j for j in range(16)]
+    qs = bytes(l | (h << 4) for l, h in zip(lo, hi))
+    blk = struct.pack("<e", 0.25) + qs
+    blk2 = struct.pack("<e", -2.0) + bytes([0x88] * 16)           # every code 8 -> 0
+    packed = np.frombuffer(blk + blk2, dtype=np.uint8).reshape(1, 36)
+    w = O.dequant_q4_0(packed, 64)
+    np.testing.assert_array_equal(w[0, :16], 0.25 * (np.array(lo) - 8))
+    np.testing.assert_array_equal(w[0, 16:32], 0.25 * (np.array(hi) - 8))
+    np.testing.assert_array_equal(w[0, 32:], np.zeros(32))
+
+
+def test_q4_0_round_trip_error_bound():
+    rng = np.random.default_rng(13)
+    x = (rng.standard_normal((8, 96)) * 0.02).astype(np.float32)
+    x[0, :32] = 0.0                                  # all-zero block
+    packed = synth.pack_q4_0(x)
+    w = O.dequant_q4_0(packed, 96)
+    d = packed.reshape(8, 3, 18)[..., :2].copy().view(np.float16).astype(np.float64)
+    err = np.abs(x.astype(np.float64).reshape(8, 3, 32) - w.reshape(8, 3, 32))
+    # the largest magnitude maps to +-7 d (d rounded to f16, so allow its rounding)
+    assert np.all(err <= d / 2 + np.abs(x).reshape(8, 3, 32).max(-1, keepdims=True) * 2.0 ** -10 + 1e-12)
+    assert np.all(w[0, :32] == 0)
+    assert np.unique(np.round(w[1:] / np.repeat(d[1:, :, 0], 32, axis=-1).reshape(7, 96))).size > 8
+
+
 def test_ema_codebook_recovers_direction():
     """With embedding_sum = z * usage the EMA table equals z up to the
     1e-7 regulariser: E = z * u / (u + 1e-7)."""
