@@ -493,7 +493,7 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
 #pragma unroll
                         for (int q = 0; q < 4; ++q) acc[q] = dot8(wQ[q * 2 + c], x8, acc[q]);
                     }
-                    const float rinv = 1.0f / sqrtf(row_ss(par, r) / static_cast<float>(DP) + eps);
+                    const float rinv = __builtin_amdgcn_rsqf(row_ss(par, r) / static_cast<float>(DP) + eps);
                     wave_sums(acc);
                     float v = 0.f;
 #pragma unroll
@@ -544,21 +544,25 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                         const int p = pf + pi;
                         const int r = (s == 1) ? pi * B + b : b;
                         const float* nd = hist + 4096 + pi * 512;
+                        // every LDS operand of this position first, then one wait
                         const float c0 = rope_s[0][p * (HD / 2) + lane], s0 = rope_s[1][p * (HD / 2) + lane];
-                        // key and this wave's query: per-head RMSNorm (both sums
-                        // at once), rotate-half RoPE (pair lane, lane + 64)
                         const float k0 = nd[256 + lane], k1 = nd[256 + lane + 64];
                         const float x0 = nd[wave * HD + lane], x1 = nd[wave * HD + lane + 64];
+                        const float vv0 = nd[384 + lane], vv1 = nd[384 + lane + 64];
+                        const float gk0 = gk[lane], gk1 = gk[lane + 64], gq0 = gq[lane], gq1 = gq[lane + 64];
+                        // key and this wave's query: per-head RMSNorm (both sums
+                        // at once; hardware reciprocal square root), rotate-half
+                        // RoPE (pair lane, lane + 64)
                         float sq[2] = {k0 * k0 + k1 * k1, x0 * x0 + x1 * x1};
                         wave_sums(sq);
+                        const float rk = __builtin_amdgcn_rsqf(sq[0] / static_cast<float>(HD) + eps);
+                        const float rq = __builtin_amdgcn_rsqf(sq[1] / static_cast<float>(HD) + eps);
                         float kv0, kv1;
                         {
-                            const float rv = 1.0f / sqrtf(sq[0] / static_cast<float>(HD) + eps);
-                            const float a0 = gk[lane] * (k0 * rv), a1 = gk[lane + 64] * (k1 * rv);
+                            const float a0 = gk0 * (k0 * rk), a1 = gk1 * (k1 * rk);
                             kv0 = a0 * c0 - a1 * s0;
                             kv1 = a1 * c0 + a0 * s0;
                         }
-                        const float vv0 = nd[384 + lane], vv1 = nd[384 + lane + 64];
                         if (wave == 0) {
                             const size_t off = kvb + (static_cast<size_t>(p) * NKV + g) * HD;
                             st_act(m.kc + off + lane, kv0);
@@ -573,8 +577,7 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                         hist[2048 + p * HD + lane] = vv0;
                         hist[2048 + p * HD + lane + 64] = vv1;
                         {
-                            const float rv = 1.0f / sqrtf(sq[1] / static_cast<float>(HD) + eps);
-                            const float a0 = gq[lane] * (x0 * rv), a1 = gq[lane + 64] * (x1 * rv);
+                            const float a0 = gq0 * (x0 * rq), a1 = gq1 * (x1 * rq);
                             qb[lane] = a0 * c0 - a1 * s0;
                             qb[lane + 64] = a1 * c0 + a0 * s0;
                         }
@@ -595,26 +598,36 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                         sc += dpp_or_zero<0x4E, 0xF>(sc);
                         sc = (kt <= p) ? sc * m.attn_scale : -__builtin_huge_valf();
                         const float mx = wave_max(sc);
-                        const float e = (kt <= p) ? expf(sc - mx) : 0.f;
+                        const float e = (kt <= p) ? __expf(sc - mx) : 0.f;
                         const float den = wave_sum((lane & 3) == 0 ? e : 0.f);
                         if ((lane & 3) == 0) eb[kt] = e;
-                        // weighted values (weights are 0 beyond p)
-                        float o0 = 0.f, o1 = 0.f;
+                        // weighted values (weights are 0 beyond p; rows beyond p
+                        // are read as row p, so no stale LDS enters the sum); all
+                        // reads are issued before the first product
+                        float va[kPositions], vb[kPositions], ew[kPositions];
 #pragma unroll
                         for (int t = 0; t < kPositions; ++t) {
                             const int tt = t <= p ? t : p;
-                            const float w = eb[t];
-                            o0 = fmaf(w, hist[2048 + tt * HD + lane], o0);
-                            o1 = fmaf(w, hist[2048 + tt * HD + lane + 64], o1);
+                            ew[t] = eb[t];
+                            va[t] = hist[2048 + tt * HD + lane];
+                            vb[t] = hist[2048 + tt * HD + lane + 64];
+                        }
+                        float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+                        for (int t = 0; t < kPositions; ++t) {
+                            o0 = fmaf(ew[t], va[t], o0);
+                            o1 = fmaf(ew[t], vb[t], o1);
                         }
                         uint64_t* orow = rc.AO + static_cast<size_t>(r) * QD + h * HD;
-                        st_rec(orow + lane, o0 / den, tag_of(ph));
-                        st_rec(orow + lane + 64, o1 / den, tag_of(ph));
+                        const float rden = __builtin_amdgcn_rcpf(den);
+                        st_rec(orow + lane, o0 * rden, tag_of(ph));
+                        st_rec(orow + lane + 64, o1 * rden, tag_of(ph));
                     }
                 }
                 // next phase's weights, after this phase's stores have left
                 sched_fence();
                 load_wO(l);
+                if (!unit) load_wU(l);
                 sched_fence();
                 ++ph;
             }
@@ -642,7 +655,7 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                     if (lane == 0) st_rec(rc.X + static_cast<size_t>(r) * DP + n, nv, tag_of(ph));
                 }
                 sched_fence();
-                load_wU(l);
+                if (wg < B * NKV) load_wU(l);
                 sched_fence();
                 ++ph;
             }
@@ -665,7 +678,7 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                             au[q] = dot8(wU[6 + q * 2 + c], x8, au[q]);
                         }
                     }
-                    const float rinv = 1.0f / sqrtf(row_ss(par, r) / static_cast<float>(DP) + eps);
+                    const float rinv = __builtin_amdgcn_rsqf(row_ss(par, r) / static_cast<float>(DP) + eps);
                     float gu[6] = {ag[0], ag[1], ag[2], au[0], au[1], au[2]};
                     wave_sums(gu);
                     float v = 0.f;
@@ -673,7 +686,7 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                     for (int q = 0; q < 3; ++q) {
                         const float gv = gu[q] * rinv;
                         const float uv = gu[3 + q] * rinv;
-                        const float hv = (gv / (1.0f + expf(-gv))) * uv;
+                        const float hv = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
                         v = (lane == q) ? hv : v;
                     }
                     if (lane < 3) st_rec(rc.H + static_cast<size_t>(r) * F + 12 * wg + 3 * wave + lane, v, tag_of(ph));
@@ -738,7 +751,7 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                         acc0 = dot8(wL[c], x8, acc0);
                         acc1 = dot8(wL[2 + c], x8, acc1);
                     }
-                    const float rinv = 1.0f / sqrtf(row_ss(par, b) / static_cast<float>(DP) + eps);
+                    const float rinv = __builtin_amdgcn_rsqf(row_ss(par, b) / static_cast<float>(DP) + eps);
                     float lg[2] = {acc0, acc1};
                     wave_sums(lg);
                     const float l0 = lg[0] * rinv;
