@@ -243,17 +243,24 @@ def project(model: OracleModel, rows: np.ndarray) -> np.ndarray:
 
 def run_frames(model: OracleModel, H: np.ndarray, q0: np.ndarray,
                force: Optional[np.ndarray] = None,
-               want_taps: bool = False) -> Dict[str, np.ndarray]:
+               want_taps: bool = False,
+               sampling: Optional[tuple] = None,
+               uniforms: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
     """One frame for B independent requests.
 
     H: [B, dT]; q0: [B] in [0, V).  force: None or [B, 15] — under teacher
     forcing the token fed back at step k (k = 1..15) and summed into the
     embedding total is force[:, k-1]; tokens and logits remain the model's own.
+    sampling: None (greedy) or (temperature, top_k, top_p) with uniforms
+    [B, 15]; step k then draws its token with ``sampling.sample_token`` and
+    the uniform uniforms[:, k-1] in place of the argmax.
 
     Returns dict: tokens [B,15] int64, logits [B,15,V] float64,
-    margin [B,15] (top-2 logit gap), embsum [B,dT] float64, and with
+    margin [B,15] (top-2 logit gap), embsum [B,dT] float64, with sampling
+    also sample_margin [B,15] (the draw's relative margin), and with
     ``want_taps`` the per-(position, layer) outputs [16, L, B, dP].
     """
+    from oracle import sampling as S
     g = model.g
     H = np.asarray(H, dtype=np.float64)
     q0 = np.asarray(q0, dtype=np.int64)
@@ -266,6 +273,10 @@ def run_frames(model: OracleModel, H: np.ndarray, q0: np.ndarray,
     vcache = np.zeros_like(kcache)
     tokens = np.zeros((B, n_steps), dtype=np.int64)
     logits = np.zeros((B, n_steps, g.vocab))
+    smargin = np.full((B, n_steps), np.inf)
+    if sampling is not None:
+        uniforms = np.asarray(uniforms, dtype=np.float32)
+        assert uniforms.shape == (B, n_steps)
     taps = [] if want_taps else None
 
     # position 0: the projected frame hidden state
@@ -282,11 +293,18 @@ def run_frames(model: OracleModel, H: np.ndarray, q0: np.ndarray,
         lg = rms_norm(h, model.out_norm, g.rms_eps) @ model.lm_head[k - 1].T
         assert np.all(np.isfinite(lg))
         logits[:, k - 1] = lg
-        tokens[:, k - 1] = argmax_lowest(lg)
+        if sampling is None:
+            tokens[:, k - 1] = argmax_lowest(lg)
+        else:
+            T, K, P = sampling
+            for b in range(B):
+                tokens[b, k - 1], smargin[b, k - 1], _ = S.sample_token(lg[b], T, K, P, uniforms[b, k - 1])
         prev = tokens[:, k - 1] if force is None else np.asarray(force[:, k - 1], dtype=np.int64)
     embsum = embsum + model.emb[n_steps][prev]
     out = {"tokens": tokens, "logits": logits, "margin": top2_margin(logits),
            "embsum": embsum}
+    if sampling is not None:
+        out["sample_margin"] = smargin
     if want_taps:
         L = g.n_layers
         out["taps"] = np.stack(taps).reshape(n_pos, L, B, g.d_model)

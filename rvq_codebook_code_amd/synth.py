@@ -288,6 +288,13 @@ def make_inputs(geom: Geometry, batch: int, frames: int, seed: int):
     return H, q0
 
 
+def make_uniforms(batch: int, frames: int, seed: int):
+    """The caller's draws for sampled frames: ``[frames, batch, 15]`` fp32
+    uniform in [0, 1), one per request and step."""
+    rng = np.random.default_rng(seed)
+    return rng.random((frames, batch, 15), dtype=np.float32)
+
+
 def workload_data(name: str, frames: Optional[int] = None, batch: Optional[int] = None):
     """(workload, weights, H, q0) for a named workload; ``frames``/``batch``
     may shrink the input draw (the weights are always the full set)."""
