@@ -56,9 +56,9 @@ def algorithmic_flops(g: synth.Geometry, B: int) -> int:
     return 2 * B * (15 * per_step + g.d_model * g.d_talker)
 
 
-def cpu_baseline(wl, W, H, q0, budget_s: float):
+def cpu_baseline(wl, W, H, q0, budget_s: float, sampling=None, U=None):
     """The oracle as it stands, on the host, for about ``budget_s`` seconds of
-    frames of the same workload."""
+    frames of the same workload (sampled frames when ``sampling`` is given)."""
     from oracle import predictor as O
     try:
         from threadpoolctl import threadpool_info
@@ -70,15 +70,18 @@ def cpu_baseline(wl, W, H, q0, budget_s: float):
     n = 0
     t0 = time.perf_counter()
     while True:
-        O.run_frames(model, H[n % H.shape[0]], q0[n % H.shape[0]])
+        if sampling is None:
+            O.run_frames(model, H[n % H.shape[0]], q0[n % H.shape[0]])
+        else:
+            O.run_frames(model, H[n % H.shape[0]], q0[n % H.shape[0]], sampling=sampling, uniforms=U[n % H.shape[0]])
         n += 1
         el = time.perf_counter() - t0
         if el >= budget_s or n >= H.shape[0]:
             break
     return {"value": round(n * B / el, 3), "unit": "frames/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{n} frame(s) of {B} request(s) of the {wl.name} workload, fp64 NumPy, "
-                      f"{el:.1f} s"}
+            "sample": f"{n} frame(s) of {B} request(s) of the {wl.name} workload"
+                      f"{' (sampled)' if sampling else ''}, fp64 NumPy, {el:.1f} s"}
 
 
 COPY_BYTES = 1 << 30
@@ -89,6 +92,8 @@ _DATAFLOW_GEOMETRY = dict(d_talker=2048, d_model=1024, n_q_heads=16, n_kv_heads=
 
 def select_driver(g, B: int, args) -> str:
     """The driver the library picks for this call (same rule as the C side)."""
+    if getattr(args, "sample", None):
+        return "tiled"
     if args.stepwise:
         return "stepwise"
     if args.generic:
@@ -151,6 +156,8 @@ def main():
     ap.add_argument("--generic", action="store_true", help="the generic persistent kernel even where a specialised one exists")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sample", default=None, metavar="T,K,P",
+                    help="draw every token (temperature T, top-k K, top-p P) with seeded uniforms instead of the argmax")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (to scale HBM byte counters)")
     args = ap.parse_args()
@@ -181,9 +188,21 @@ def main():
     tok = torch.zeros((B, 15), dtype=torch.int32, device=dev)
     emb = torch.zeros((B, g.d_talker), dtype=torch.float32, device=dev)
     F = H.shape[0]
+    sampling = None
+    if args.sample:
+        t_, k_, p_ = args.sample.split(",")
+        sampling = (float(t_), int(k_), float(p_))
+        U = synth.make_uniforms(B, F, wl.input_seed + 7)
+        Ud = torch.from_numpy(U).to(dev)
+
+    def frame(i):
+        if sampling is None:
+            pred.run(Hd[i % F], qd[i % F], tok, emb, stepwise=args.stepwise, generic=args.generic)
+        else:
+            pred.run_sampled(Hd[i % F], qd[i % F], Ud[i % F], tok, emb, *sampling)
 
     for i in range(args.warmup):
-        pred.run(Hd[i % F], qd[i % F], tok, emb, stepwise=args.stepwise, generic=args.generic)
+        frame(i)
     torch.cuda.synchronize()
     if pred.get_error() != 0:
         raise RuntimeError("device flag raised during warm-up")
@@ -195,7 +214,7 @@ def main():
     torch.cuda.synchronize()
     for i in range(args.steps):
         ev[i][0].record(stream)
-        pred.run(Hd[i % F], qd[i % F], tok, emb, stepwise=args.stepwise, generic=args.generic)
+        frame(i)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     ms = ev[0][0].elapsed_time(ev[-1][1])
@@ -221,7 +240,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, W, H, q0, args.cpu_budget)
+        cpu = cpu_baseline(wl, W, H, q0, args.cpu_budget, sampling, U if sampling else None)
 
     # arithmetic type of the products: fp32 on the dataflow/generic paths,
     # bf16 operands with fp32 accumulation on the matrix cores
@@ -244,6 +263,9 @@ def main():
                    "predictor": f"dP={g.d_model} L={g.n_layers} heads={g.n_q_heads}/{g.n_kv_heads}x{g.head_dim} "
                                 f"F={g.d_ffn} V={g.vocab} dT={g.d_talker}",
                    "driver": driver,
+                   "sampling": (None if sampling is None else
+                                {"temperature": sampling[0], "top_k": sampling[1], "top_p": sampling[2],
+                                 "uniforms": "seeded, one per request and step"}),
                    "ms_per_launch": round(launch_ms, 4),
                    "tokens_per_s": round(15 * frames_per_s, 1),
                    "algorithmic_bytes_per_step": nbytes,

@@ -193,6 +193,57 @@ qp_status qp_run_frames_ex(qp_handle* h, int32_t B, const float* H,
                            const int32_t* force_tokens, float* logits_out,
                            float* taps_out, uint32_t flags);
 
+/* Caller-controlled sampling.  The pages leave sampling to the caller (the
+ * GGUF loaders do not read the generation config: rightkit-qts exporter
+ * README, "Qwen3-TTS 1.7B -> QTS GGUF", section "Usage") and describe the
+ * exported predictor loop as greedy.  A sampled step replaces the argmax by
+ * this draw from the step's fp32 logits z:
+ *   1. rank order: descending logit, lower vocabulary index first on ties;
+ *   2. weights w_r = exp((z_r - z_0) / temperature), z_0 the largest logit;
+ *   3. top-k: the first top_k ranks stay (0 = all);
+ *   4. top-p: of those, the shortest rank-order prefix whose weight reaches
+ *      top_p times their total stays (at least one token; 1 = all);
+ *   5. the token is the first kept rank whose inclusive cumulative weight
+ *      exceeds u times the kept total, u being the caller's uniform for that
+ *      request and step (clamped to [0, 1], NaN as 0), else the last kept rank.
+ * The weights are summed in fp32; only draws whose threshold lies within
+ * about 2e-6 of the total from a cumulative boundary can differ from exact
+ * arithmetic.
+ * top_k = 1 reproduces the argmax. */
+typedef struct {
+    float temperature;  /* finite, > 0                                  */
+    int32_t top_k;      /* >= 0; 0 keeps every token                    */
+    float top_p;        /* in (0, 1]; 1 keeps every token top-k kept     */
+} qp_sampling;
+
+/* One frame with every step's token drawn as above instead of the argmax.
+ * Same arguments as qp_run_frames_ex, plus:
+ *   sampling     host pointer, read before return (one setting for all rows)
+ *   uniforms     float [B, 15] device: the draw of step k for request b is
+ *                uniforms[b, k-1]
+ * tokens_out receives the drawn tokens; force_tokens (may be NULL) overrides
+ * the fed-back token as in qp_run_frames_ex, logits_out (may be NULL) receives
+ * the logits.  Runs on the batched matrix-core path (its weight and geometry
+ * conditions under QP_FLAG_TILED, and V <= 4096), else QP_ERR_INVALID_ARG;
+ * invalid parameters give QP_ERR_INVALID_ARG.  Without hooks the frame
+ * replays a captured graph, as qp_run_frames does. */
+qp_status qp_run_frames_sampled(qp_handle* h, int32_t B, const float* H,
+                                const int32_t* q0, const qp_sampling* sampling,
+                                const float* uniforms, int32_t* tokens_out,
+                                float* embsum_out, void* stream,
+                                const int32_t* force_tokens, float* logits_out);
+
+/* The draw alone, on caller-provided logits (no handle needed).  Device
+ * pointers: logits float [rows, row_stride] (the first V of each row are
+ * read), uniforms float with row r's uniform at uniforms[r * uniform_stride],
+ * tokens_out int32 [rows].  1 <= V <= 4096, row_stride >= V,
+ * uniform_stride >= 1, else QP_ERR_INVALID_ARG; rows = 0 is a no-op.
+ * Asynchronous on `stream` (a hipStream_t). */
+qp_status qp_sample_logits(const float* logits, int32_t rows, int32_t V,
+                           int64_t row_stride, const qp_sampling* sampling,
+                           const float* uniforms, int32_t uniform_stride,
+                           int32_t* tokens_out, void* stream);
+
 /* Synchronise the handle's device, then return and clear the sticky device
  * flag: QP_OK, or QP_ERR_DEVICE_FLAG when a kernel saw an out-of-range token
  * (q0 or a forced token) or a grid barrier timed out since the last call. */

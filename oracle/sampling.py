@@ -61,14 +61,11 @@ def clamp_uniform(u: float) -> float:
     return min(max(u, 0.0), 1.0)
 
 
-def sample_token(z: np.ndarray, temperature: float, top_k: int, top_p: float,
-                 u: float) -> Tuple[int, float, int]:
-    """One token from logits z (length V) under the steps of the module header.
-
-    Returns (token, margin, kept): the vocabulary index drawn; the smallest
-    relative distance, as a fraction of the relevant total, between a
-    threshold and a cumulative boundary; and the number of tokens kept after
-    top-k and top-p."""
+def explain(z: np.ndarray, temperature: float, top_k: int, top_p: float, u: float) -> dict:
+    """Every intermediate of one draw (module header, steps 1-5): the rank
+    order, the cumulative weights c1 of the top-k ranks and their total s1,
+    the kept count n2 after top-p, the kept total s2, the draw threshold
+    u * s2 and the drawn rank."""
     assert temperature > 0.0 and math.isfinite(temperature)
     assert 0.0 < top_p <= 1.0
     assert top_k >= 0
@@ -80,26 +77,39 @@ def sample_token(z: np.ndarray, temperature: float, top_k: int, top_p: float,
     n1 = V if (top_k == 0 or top_k >= V) else top_k
     c1 = np.cumsum(w[:n1])
     s1 = c1[-1]
-    margin = math.inf
+    cut = None
     if top_p >= 1.0:
         n2 = n1
     else:
-        thr = float(np.float32(top_p)) * s1
-        reach = np.nonzero(c1 >= thr)[0]
+        cut = float(np.float32(top_p)) * s1
+        reach = np.nonzero(c1 >= cut)[0]
         n2 = int(reach[0]) + 1 if reach.size else n1
-        margin = min(margin, float(np.min(np.abs(c1 - thr))) / s1)
-    c2 = c1[:n2]
-    s2 = c2[-1]
-    uu = clamp_uniform(u)
-    thr = uu * s2
-    above = np.nonzero(c2 > thr)[0]
-    r = int(above[0]) if above.size else n2 - 1
+    s2 = c1[n2 - 1]
+    thr = clamp_uniform(u) * s2
+    above = np.nonzero(c1[:n2] > thr)[0]
+    rank = int(above[0]) if above.size else n2 - 1
+    return {"order": order, "c1": c1, "s1": s1, "cut": cut, "n2": n2, "s2": s2, "thr": thr, "rank": rank}
+
+
+def sample_token(z: np.ndarray, temperature: float, top_k: int, top_p: float,
+                 u: float) -> Tuple[int, float, int]:
+    """One token from logits z (length V) under the steps of the module header.
+
+    Returns (token, margin, kept): the vocabulary index drawn; the smallest
+    relative distance, as a fraction of the relevant total, between a
+    threshold and a cumulative boundary; and the number of tokens kept after
+    top-k and top-p."""
+    e = explain(z, temperature, top_k, top_p, u)
+    c1, n2 = e["c1"], e["n2"]
+    margin = math.inf
+    if e["cut"] is not None:
+        margin = min(margin, float(np.min(np.abs(c1 - e["cut"]))) / e["s1"])
     # distance to the interior boundaries (the last one is s2 itself, which
     # only u = 1 reaches, and that draws the last kept rank either way)
-    inner = c2[:-1]
+    inner = c1[: n2 - 1]
     if inner.size:
-        margin = min(margin, float(np.min(np.abs(inner - thr))) / s2)
-    return int(order[r]), margin, n2
+        margin = min(margin, float(np.min(np.abs(inner - e["thr"]))) / e["s2"])
+    return int(e["order"][e["rank"]]), margin, n2
 
 
 def sample_rows(logits: np.ndarray, temperature: float, top_k: int, top_p: float,

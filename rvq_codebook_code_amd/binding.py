@@ -38,8 +38,8 @@ QP_FLAG_TILED = 0x4
 WEIGHT_DTYPES = {"f32": 0, "bf16": 1, "q8_0": 2, "q4_0": 3}
 EMB_FORMATS = {"f32": 0, "bf16": 1, "ema": 2}
 
-EXPORTED = ["qp_create", "qp_run_frames", "qp_run_frames_ex", "qp_get_error",
-            "qp_last_device_flags", "qp_destroy", "qp_status_string", "qp_last_error"]
+EXPORTED = ["qp_create", "qp_run_frames", "qp_run_frames_ex", "qp_run_frames_sampled", "qp_sample_logits",
+            "qp_get_error", "qp_last_device_flags", "qp_destroy", "qp_status_string", "qp_last_error"]
 
 
 class QpGeometry(C.Structure):
@@ -60,6 +60,10 @@ class QpWeights(C.Structure):
                 ("emb", C.c_void_p * N_CODEBOOKS), ("ema_sum", C.c_void_p * N_CODEBOOKS),
                 ("ema_usage", C.c_void_p * N_CODEBOOKS), ("layers", C.POINTER(QpLayerWeights)),
                 ("out_norm", C.c_void_p), ("lm_head", C.c_void_p * N_STEPS)]
+
+
+class QpSampling(C.Structure):
+    _fields_ = [("temperature", C.c_float), ("top_k", C.c_int32), ("top_p", C.c_float)]
 
 
 class QpError(RuntimeError):
@@ -86,6 +90,10 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     lib.qp_run_frames.restype = i32
     lib.qp_run_frames_ex.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, u32]
     lib.qp_run_frames_ex.restype = i32
+    lib.qp_run_frames_sampled.argtypes = [vp, i32, vp, vp, C.POINTER(QpSampling), vp, vp, vp, vp, vp, vp]
+    lib.qp_run_frames_sampled.restype = i32
+    lib.qp_sample_logits.argtypes = [vp, i32, i32, C.c_int64, C.POINTER(QpSampling), vp, i32, vp, vp]
+    lib.qp_sample_logits.restype = i32
     lib.qp_get_error.argtypes = [vp]
     lib.qp_get_error.restype = i32
     lib.qp_last_device_flags.argtypes = [vp]
@@ -200,6 +208,31 @@ class Predictor:
                                            _dptr(taps_out), flags)
         _check(self.lib, st, "qp_run_frames")
 
+    def run_sampled(self, H, q0, uniforms, tokens_out, embsum_out, temperature: float, top_k: int = 0,
+                    top_p: float = 1.0, force=None, logits_out=None, stream=None):
+        """Enqueue one frame whose tokens are drawn (temperature, top-k,
+        top-p) with the caller's uniforms [B, 15] instead of the argmax."""
+        import torch
+        B = H.shape[0]
+        for t in (H, q0, uniforms, tokens_out, embsum_out, force, logits_out):
+            if t is not None:
+                assert t.is_cuda and t.is_contiguous()
+        assert H.dtype == torch.float32 and q0.dtype == torch.int32 and uniforms.dtype == torch.float32
+        assert tuple(uniforms.shape) == (B, N_STEPS)
+        assert tuple(H.shape) == (B, self.geom.d_talker) and tuple(q0.shape) == (B,)
+        assert tuple(tokens_out.shape) == (B, N_STEPS) and tuple(embsum_out.shape) == (B, self.geom.d_talker)
+        if force is not None:
+            assert force.dtype == torch.int32 and tuple(force.shape) == (B, N_STEPS)
+        if logits_out is not None:
+            assert logits_out.dtype == torch.float32 and tuple(logits_out.shape) == (B, N_STEPS, self.geom.vocab)
+        if stream is None:
+            stream = torch.cuda.current_stream(H.device).cuda_stream
+        sp = QpSampling(temperature, top_k, top_p)
+        st = self.lib.qp_run_frames_sampled(self.h, B, _dptr(H), _dptr(q0), C.byref(sp), _dptr(uniforms),
+                                            _dptr(tokens_out), _dptr(embsum_out), stream, _dptr(force),
+                                            _dptr(logits_out))
+        _check(self.lib, st, "qp_run_frames_sampled")
+
     def get_error(self) -> int:
         """Synchronise; returns 0 or the raw device flag bits (and clears them)."""
         st = self.lib.qp_get_error(self.h)
@@ -220,3 +253,23 @@ class Predictor:
             self.close()
         except Exception:
             pass
+
+
+def sample_logits(logits, uniforms, tokens_out, temperature: float, top_k: int = 0, top_p: float = 1.0,
+                  stream=None):
+    """Draw one token per row of logits [rows, V] (device fp32) with
+    uniforms [rows] into tokens_out [rows] (int32), on the GPU."""
+    import torch
+    lib = load_library()
+    rows, V = logits.shape
+    for t in (logits, uniforms, tokens_out):
+        assert t.is_cuda
+    assert logits.dtype == torch.float32 and logits.stride(1) == 1
+    assert uniforms.dtype == torch.float32 and tuple(uniforms.shape) == (rows,) and uniforms.is_contiguous()
+    assert tokens_out.dtype == torch.int32 and tuple(tokens_out.shape) == (rows,) and tokens_out.is_contiguous()
+    if stream is None:
+        stream = torch.cuda.current_stream(logits.device).cuda_stream
+    sp = QpSampling(temperature, top_k, top_p)
+    st = lib.qp_sample_logits(_dptr(logits), rows, V, logits.stride(0), C.byref(sp), _dptr(uniforms), 1,
+                              _dptr(tokens_out), stream)
+    _check(lib, st, "qp_sample_logits")

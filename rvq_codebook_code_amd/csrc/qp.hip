@@ -17,6 +17,7 @@
 #include "qp_phases.h"
 #include "qp_stream.h"
 #include "qp_tiled.h"
+#include "qp_sample.h"
 
 using namespace qp;
 
@@ -201,6 +202,7 @@ struct qp_handle {
     // reading and writing handle-owned staging buffers
     struct FrameGraph {
         int B = 0;
+        bool sampled = false;
         hipGraph_t graph = nullptr;
         hipGraphExec_t exec = nullptr;
     };
@@ -214,6 +216,12 @@ struct qp_handle {
     float* st_emb = nullptr;                // [max_batch][dT]
     uint16_t* t_xg = nullptr;               // [2*max_batch][dP] bf16(g_next * x)
     float* t_ss = nullptr;                  // [2*max_batch][dP/16] 16-column sums of x^2
+    // sampled frames (batched path, V <= 4096)
+    bool sample_ok = false;
+    float* t_logits = nullptr;              // [max_batch][V] one step's logits
+    int* t_sampled = nullptr;               // [max_batch] one step's drawn tokens
+    float* st_u = nullptr;                  // [max_batch][15] staged uniforms
+    qp::sample::Params* st_samp = nullptr;  // the call's sampling parameters
 };
 
 namespace {
@@ -658,8 +666,18 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
         if (a.logits_out) {
             g.logits = a.logits_out + static_cast<size_t>(s - 1) * m.V;
             g.logit_ld = static_cast<size_t>(kSteps) * m.V;
+        } else if (a.uniforms) {
+            g.logits = h->t_logits;
+            g.logit_ld = m.V;
         }
         ta.nkt = tiled_gemm<WT, T::SRC_BF16_NORM, T::EPI_ARGMAX>(h, g, stream);
+        if (a.uniforms) {
+            // the step's token drawn from its logits with the caller's uniform
+            hipLaunchKernelGGL(qp::sample::sample_kernel(m.V), dim3(B), dim3(qp::sample::kThreadsSm), 0, stream, g.logits,
+                               static_cast<long long>(g.logit_ld), m.V, qp::sample::Params{}, h->st_samp,
+                               a.uniforms + (s - 1), kSteps, h->t_sampled);
+            ta.sampled = h->t_sampled;
+        }
         ta.s = s;
         ta.emb = m.emb[s];
         ta.ptab = s < kSteps ? m.ptab + static_cast<size_t>(s) * m.V * m.dP : nullptr;
@@ -685,11 +703,13 @@ qp_status launch_tiled_graph(qp_handle* h, const RunArgs& a, hipStream_t stream)
     qp_status st = QP_OK;
     const Model& m = h->m;
     const int B = a.B;
+    const bool sampled = a.uniforms != nullptr;
     copy32(a.H, h->st_H, static_cast<size_t>(B) * m.dT, stream);
     copy32(a.q0, h->st_q0, static_cast<size_t>(B), stream);
+    if (sampled) copy32(a.uniforms, h->st_u, static_cast<size_t>(B) * kSteps, stream);
     qp_handle::FrameGraph* fg = nullptr;
     for (auto& e : h->graphs)
-        if (e.exec && e.B == B) fg = &e;
+        if (e.exec && e.B == B && e.sampled == sampled) fg = &e;
     if (!fg) {
         if (!h->cap_stream &&
             !check_hip(hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking), "hipStreamCreate", &st))
@@ -699,6 +719,7 @@ qp_status launch_tiled_graph(qp_handle* h, const RunArgs& a, hipStream_t stream)
         sa.q0 = h->st_q0;
         sa.tok_out = h->st_tok;
         sa.embsum = h->st_emb;
+        if (sampled) sa.uniforms = h->st_u;
         fg = &h->graphs[h->graph_next];
         h->graph_next = (h->graph_next + 1) % qp_handle::kGraphs;
         if (fg->exec) {
@@ -722,6 +743,7 @@ qp_status launch_tiled_graph(qp_handle* h, const RunArgs& a, hipStream_t stream)
             return st;
         }
         fg->B = B;
+        fg->sampled = sampled;
         fg->graph = graph;
         fg->exec = exec;
     }
@@ -975,6 +997,13 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
         h->st_tok = static_cast<int*>(up.alloc(static_cast<size_t>(m.max_batch) * kSteps * 4));
         h->st_emb = static_cast<float*>(up.alloc(static_cast<size_t>(m.max_batch) * m.dT * 4));
         h->t_ss = static_cast<float*>(up.alloc(rows * (m.dP / 16) * 4));
+        h->sample_ok = m.V <= qp::sample::kMaxV;
+        if (h->sample_ok) {
+            h->t_logits = static_cast<float*>(up.alloc(static_cast<size_t>(m.max_batch) * m.V * 4));
+            h->t_sampled = static_cast<int*>(up.alloc(static_cast<size_t>(m.max_batch) * 4));
+            h->st_u = static_cast<float*>(up.alloc(static_cast<size_t>(m.max_batch) * kSteps * 4));
+            h->st_samp = static_cast<qp::sample::Params*>(up.alloc(256));
+        }
     }
 
     // records of the dataflow kernel (1.7B geometry, bf16 weights, B <= 2)
@@ -1064,6 +1093,83 @@ qp_status qp_run_frames_ex(qp_handle* h, int32_t B, const float* H, const int32_
 qp_status qp_run_frames(qp_handle* h, int32_t B, const float* H, const int32_t* q0, int32_t* tokens_out,
                         float* embsum_out, void* stream) {
     return qp_run_frames_ex(h, B, H, q0, tokens_out, embsum_out, stream, nullptr, nullptr, nullptr, 0u);
+}
+
+namespace {
+bool sampling_valid(const qp_sampling* sp, std::string* why) {
+    if (!sp) {
+        *why = "sampling parameters are NULL";
+        return false;
+    }
+    if (!(sp->temperature > 0.0f) || !std::isfinite(sp->temperature)) {
+        *why = "temperature must be finite and > 0";
+        return false;
+    }
+    if (sp->top_k < 0) {
+        *why = "top_k must be >= 0";
+        return false;
+    }
+    if (!(sp->top_p > 0.0f && sp->top_p <= 1.0f)) {
+        *why = "top_p must lie in (0, 1]";
+        return false;
+    }
+    return true;
+}
+}  // namespace
+
+qp_status qp_run_frames_sampled(qp_handle* h, int32_t B, const float* H, const int32_t* q0,
+                                const qp_sampling* sampling, const float* uniforms, int32_t* tokens_out,
+                                float* embsum_out, void* stream, const int32_t* force_tokens, float* logits_out) {
+    if (!h) return fail(QP_ERR_INVALID_ARG, "handle is NULL");
+    if (B < 0 || B > h->m.max_batch)
+        return fail(QP_ERR_BATCH, "B=" + std::to_string(B) + " outside [0, " + std::to_string(h->m.max_batch) + "]");
+    std::string why;
+    if (!sampling_valid(sampling, &why)) return fail(QP_ERR_INVALID_ARG, why);
+    if (!h->tiled_ok || !h->sample_ok)
+        return fail(QP_ERR_INVALID_ARG,
+                    "sampled frames run on the batched matrix-core path, which does not support this geometry, "
+                    "weight dtype or vocabulary size");
+    if (B == 0) return QP_OK;
+    if (!H || !q0 || !uniforms || !tokens_out || !embsum_out)
+        return fail(QP_ERR_INVALID_ARG, "NULL input or output pointer");
+    DeviceGuard guard(h->device);
+    RunArgs a{};
+    a.B = B;
+    a.H = H;
+    a.q0 = q0;
+    a.tok_out = tokens_out;
+    a.embsum = embsum_out;
+    a.force = force_tokens;
+    a.logits_out = logits_out;
+    a.uniforms = uniforms;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const qp::sample::Params p{sampling->temperature, sampling->top_k, sampling->top_p};
+    hipLaunchKernelGGL(qp::sample::k_set_params, dim3(1), dim3(64), 0, s, p, h->st_samp);
+    switch (h->m.wt) {
+        case WT_BF16: return launch_frame<WT_BF16>(h, a, s, false, false, true);
+        default: return launch_frame<WT_Q8>(h, a, s, false, false, true);
+    }
+}
+
+qp_status qp_sample_logits(const float* logits, int32_t rows, int32_t V, int64_t row_stride,
+                           const qp_sampling* sampling, const float* uniforms, int32_t uniform_stride,
+                           int32_t* tokens_out, void* stream) {
+    std::string why;
+    if (!sampling_valid(sampling, &why)) return fail(QP_ERR_INVALID_ARG, why);
+    if (rows < 0) return fail(QP_ERR_INVALID_ARG, "rows must be >= 0");
+    if (V < 1 || V > qp::sample::kMaxV)
+        return fail(QP_ERR_INVALID_ARG, "V must lie in [1, " + std::to_string(qp::sample::kMaxV) + "]");
+    if (row_stride < V) return fail(QP_ERR_INVALID_ARG, "row_stride must be >= V");
+    if (uniform_stride < 1) return fail(QP_ERR_INVALID_ARG, "uniform_stride must be >= 1");
+    if (rows == 0) return QP_OK;
+    if (!logits || !uniforms || !tokens_out) return fail(QP_ERR_INVALID_ARG, "NULL input or output pointer");
+    const qp::sample::Params p{sampling->temperature, sampling->top_k, sampling->top_p};
+    hipLaunchKernelGGL(qp::sample::sample_kernel(V), dim3(rows), dim3(qp::sample::kThreadsSm), 0,
+                       static_cast<hipStream_t>(stream), logits, static_cast<long long>(row_stride), V, p,
+                       static_cast<const qp::sample::Params*>(nullptr), uniforms, uniform_stride, tokens_out);
+    qp_status st = QP_OK;
+    if (!check_hip(hipGetLastError(), "sampling kernel launch", &st)) return st;
+    return QP_OK;
 }
 
 qp_status qp_get_error(qp_handle* h) {

@@ -78,6 +78,7 @@ struct RunArgs {
     const int* force;      // [B][15] or null
     float* logits_out;     // [B][15][V] or null
     float* taps;           // [16][L][B][dP] or null
+    const float* uniforms; // [B][15] caller's draws for sampled frames, or null (greedy)
     unsigned long long bar_base;  // grid barriers completed by earlier launches
     uint32_t seq0;                // record epochs used by earlier launches
 };

@@ -107,6 +107,7 @@ struct TokArgs {
     int* tok_out;                     // [B][15]
     float* embsum;                    // [B][dT]
     const unsigned long long* keys;   // [B][nkt] lm_head tile keys
+    const int* sampled;               // [B] drawn tokens of this step (sampled frames), or null
     float* x;                         // residual rows [2B][dP]
     uint16_t* xg;                     // bf16(gain0 * x) rows
     float* ss;                        // 16-column sums of x^2 [2B][dP/16]
@@ -775,7 +776,8 @@ __global__ __launch_bounds__(kThreadsT) void k_next(TokArgs ta) {
         float* es = ta.embsum + static_cast<size_t>(b) * ta.dT;
         load_vec(es, ne, o);
         uint64_t k = 0;
-        for (int t = threadIdx.x; t < nkt; t += kThreadsT) k = umax64(k, ta.keys[static_cast<size_t>(b) * nkt + t]);
+        if (!ta.sampled)
+            for (int t = threadIdx.x; t < nkt; t += kThreadsT) k = umax64(k, ta.keys[static_cast<size_t>(b) * nkt + t]);
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) k = umax64(k, shfl_xor64(k, off));
         __syncthreads();
@@ -784,7 +786,7 @@ __global__ __launch_bounds__(kThreadsT) void k_next(TokArgs ta) {
         if (threadIdx.x == 0) {
             uint64_t kk = red[0];
             for (int w = 1; w < kThreadsT / 64; ++w) kk = umax64(kk, red[w]);
-            const int tok = argmax_index(kk);
+            const int tok = ta.sampled ? ta.sampled[b] : argmax_index(kk);
             ta.tok_out[b * kSteps + (s - 1)] = tok;
             int fed = ta.force ? ta.force[b * kSteps + (s - 1)] : tok;
             if (fed < 0 || fed >= ta.V) {

@@ -96,3 +96,22 @@ def test_missing_weights_rejected(lib):
 def test_null_out_pointer(lib):
     g = bd.make_geometry(_tiny(), 4)
     assert lib.qp_create(C.byref(bd.QpWeights()), C.byref(g), 0, None) == bd.QP_ERR_INVALID_ARG
+
+
+def test_sampling_arguments_rejected_before_the_gpu(lib):
+    """Bad sampling parameters and shapes fail with INVALID_ARG without a
+    device call (rows = 0 and NULL pointers never reach a launch)."""
+    sp = bd.QpSampling(1.0, 0, 1.0)
+    assert lib.qp_sample_logits(None, 0, 256, 256, C.byref(sp), None, 1, None, None) == bd.QP_OK
+    for bad in (bd.QpSampling(0.0, 0, 1.0), bd.QpSampling(float("nan"), 0, 1.0), bd.QpSampling(float("inf"), 0, 1.0),
+                bd.QpSampling(1.0, -1, 1.0), bd.QpSampling(1.0, 0, 0.0), bd.QpSampling(1.0, 0, 1.5),
+                bd.QpSampling(1.0, 0, float("nan"))):
+        assert lib.qp_sample_logits(None, 0, 256, 256, C.byref(bad), None, 1, None, None) == bd.QP_ERR_INVALID_ARG
+    assert lib.qp_sample_logits(None, 0, 256, 256, None, None, 1, None, None) == bd.QP_ERR_INVALID_ARG
+    assert lib.qp_sample_logits(None, 0, 0, 256, C.byref(sp), None, 1, None, None) == bd.QP_ERR_INVALID_ARG
+    assert lib.qp_sample_logits(None, 0, 4097, 8192, C.byref(sp), None, 1, None, None) == bd.QP_ERR_INVALID_ARG
+    assert lib.qp_sample_logits(None, 0, 256, 255, C.byref(sp), None, 1, None, None) == bd.QP_ERR_INVALID_ARG
+    assert lib.qp_sample_logits(None, 0, 256, 256, C.byref(sp), None, 0, None, None) == bd.QP_ERR_INVALID_ARG
+    assert lib.qp_sample_logits(None, 3, 256, 256, C.byref(sp), None, 1, None, None) == bd.QP_ERR_INVALID_ARG
+    assert lib.qp_run_frames_sampled(None, 1, None, None, C.byref(sp), None, None, None, None, None, None) == \
+        bd.QP_ERR_INVALID_ARG
