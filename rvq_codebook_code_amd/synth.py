@@ -302,3 +302,110 @@ def workload_data(name: str, frames: Optional[int] = None, batch: Optional[int] 
     W = make_weights(wl.geom, wl.weight_seed)
     H, q0 = make_inputs(wl.geom, batch or wl.batch, frames or wl.frames, wl.input_seed)
     return wl, W, H, q0
+
+
+# ----------------------------------------------------------------------------
+# the Talker decode step (the step before the predictor)
+# ----------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class TalkerGeometry:
+    d_model: int
+    n_layers: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    d_ffn: int
+    vocab: int            # codec head rows (codebook-0 tokens and specials)
+    rms_eps: float
+    rope_base: float
+    weight_dtype: str     # "bf16" | "q8_0" | "q4_0"
+
+
+@dataclasses.dataclass(frozen=True)
+class TalkerWorkload:
+    name: str
+    geom: TalkerGeometry
+    batch: int
+    context: int          # history length of every request before the timed steps
+    weight_seed: int
+    input_seed: int
+    description: str
+
+
+_TALKER_17B = dict(d_model=2048, n_q_heads=16, n_kv_heads=8, head_dim=128, d_ffn=6144,
+                   vocab=3072, rms_eps=1e-6, rope_base=1e6)
+
+TALKER_WORKLOADS: Dict[str, TalkerWorkload] = {
+    "talker_tiny": TalkerWorkload(
+        "talker_tiny",
+        TalkerGeometry(d_model=256, n_layers=2, n_q_heads=4, n_kv_heads=2, head_dim=64, d_ffn=768,
+                       vocab=384, rms_eps=1e-6, rope_base=1e4, weight_dtype="bf16"),
+        batch=3, context=40, weight_seed=3001, input_seed=4001,
+        description="tiny Talker, bf16 weights, B=3, 40 positions of history"),
+    "talker_l2": TalkerWorkload(
+        "talker_l2", TalkerGeometry(n_layers=2, weight_dtype="bf16", **_TALKER_17B),
+        batch=4, context=300, weight_seed=3002, input_seed=4002,
+        description="1.7B Talker widths with 2 layers, bf16 weights, B=4, up to 300 positions of history"),
+    "talker_b1": TalkerWorkload(
+        "talker_b1", TalkerGeometry(n_layers=28, weight_dtype="bf16", **_TALKER_17B),
+        batch=1, context=1024, weight_seed=3003, input_seed=4003,
+        description="1.7B Talker, bf16 weights, B=1, 1024 positions of history"),
+    "talker_b16": TalkerWorkload(
+        "talker_b16", TalkerGeometry(n_layers=28, weight_dtype="bf16", **_TALKER_17B),
+        batch=16, context=1024, weight_seed=3003, input_seed=4004,
+        description="1.7B Talker, bf16 weights, B=16, 1024 positions of history each"),
+}
+
+
+def make_talker_weights(geom: TalkerGeometry, seed: int) -> dict:
+    """Draw a Talker weight set.  Layer l draws from its own generator
+    (seed, l), in the order attn_norm, wq, wk, wv, wo, q_norm, k_norm,
+    ffn_norm, w_gate, w_up, w_down; then output_norm and codec_head from
+    (seed, n_layers)."""
+    g = geom
+    wd = g.weight_dtype
+    qd = g.n_q_heads * g.head_dim
+    kd = g.n_kv_heads * g.head_dim
+
+    def one_layer(l):
+        rng = np.random.default_rng([seed, l])
+        lw = {}
+        lw["attn_norm"] = _gain(rng, g.d_model)
+        lw["wq"] = _matrix(rng, qd, g.d_model, wd)
+        lw["wk"] = _matrix(rng, kd, g.d_model, wd)
+        lw["wv"] = _matrix(rng, kd, g.d_model, wd)
+        lw["wo"] = _matrix(rng, g.d_model, qd, wd)
+        lw["q_norm"] = _gain(rng, g.head_dim)
+        lw["k_norm"] = _gain(rng, g.head_dim)
+        lw["ffn_norm"] = _gain(rng, g.d_model)
+        lw["w_gate"] = _matrix(rng, g.d_ffn, g.d_model, wd)
+        lw["w_up"] = _matrix(rng, g.d_ffn, g.d_model, wd)
+        lw["w_down"] = _matrix(rng, g.d_model, g.d_ffn, wd)
+        return lw
+
+    # every layer has its own generator, so the draw is the same however the
+    # layers are scheduled
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        layers = list(ex.map(one_layer, range(g.n_layers)))
+    rng = np.random.default_rng([seed, g.n_layers])
+    return {"weight_dtype": wd, "layers": layers, "output_norm": _gain(rng, g.d_model),
+            "codec_head": _matrix(rng, g.vocab, g.d_model, wd)}
+
+
+def make_talker_history(geom: TalkerGeometry, n_pos: int, seed: int):
+    """A request's cached history: keys and values of positions 0..n_pos-1 as
+    bf16 bit patterns [L, n_pos, nkv, hd] (N(0,1) draws: the scale of keys
+    after the per-head norm)."""
+    rng = np.random.default_rng(seed)
+    shape = (geom.n_layers, n_pos, geom.n_kv_heads, geom.head_dim)
+    K = f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+    V = f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+    return K, V
+
+
+def make_talker_inputs(geom: TalkerGeometry, batch: int, steps: int, seed: int):
+    """Step input rows [steps, batch, d_model] ~ N(0,1) fp32."""
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((steps, batch, geom.d_model), dtype=np.float32)
