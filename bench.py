@@ -56,6 +56,105 @@ def algorithmic_flops(g: synth.Geometry, B: int) -> int:
     return 2 * B * (15 * per_step + g.d_model * g.d_talker)
 
 
+TALKER_METRIC = "Talker decode steps/sec (H and q0 per request) at a 1024-position history; % HBM roofline"
+
+
+def talker_bytes(g, B: int, ctx: int) -> int:
+    """Bytes one Talker step must move: every weight once (the codec head
+    included) plus each request's cached keys and values (bf16) of the ctx
+    positions it attends over, and the new position's key and value."""
+    qd, kd = g.n_q_heads * g.head_dim, g.n_kv_heads * g.head_dim
+    per_layer = g.d_model * (qd + 2 * kd) + qd * g.d_model + 3 * g.d_model * g.d_ffn
+    weights = int((g.n_layers * per_layer + g.vocab * g.d_model) * bytes_per_weight(g.weight_dtype))
+    kv = B * g.n_layers * (ctx + 1) * 2 * kd * 2
+    return weights + kv
+
+
+def run_talker(args, torch, dev):
+    from oracle import talker as TK
+    from rvq_codebook_code_amd import binding as bd
+    wl = synth.TALKER_WORKLOADS[args.workload]
+    g, B, ctx = wl.geom, wl.batch, wl.context
+    W = synth.make_talker_weights(g, wl.weight_seed)
+    steps = args.steps + args.warmup
+    tk = bd.Talker(W, g, max_batch=B, n_slots=B, max_ctx=ctx + steps + 1)
+    K, V = synth.make_talker_history(g, ctx, wl.input_seed + 1)
+    Kd = torch.from_numpy(K.view(np.int16)).to(dev)
+    Vd = torch.from_numpy(V.view(np.int16)).to(dev)
+    for b in range(B):
+        tk.load_history(b, Kd, Vd)
+    del Kd, Vd
+    X = torch.from_numpy(synth.make_talker_inputs(g, B, 16, wl.input_seed)).to(dev)
+    slots = torch.arange(B, dtype=torch.int32, device=dev)
+    H = torch.zeros((B, g.d_model), device=dev)
+    q0 = torch.zeros((B,), dtype=torch.int32, device=dev)
+    posd = [torch.full((B,), ctx + i, dtype=torch.int32, device=dev) for i in range(steps)]
+    for i in range(args.warmup):
+        tk.step(X[i % 16], slots, posd[i], ctx + i + 1, H, q0)
+    torch.cuda.synchronize()
+    if tk.get_error():
+        raise RuntimeError("device flag raised during warm-up")
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.warmup, steps):
+        tk.step(X[i % 16], slots, posd[i], ctx + i + 1, H, q0)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    if tk.get_error():
+        raise RuntimeError("device flag raised during the timed steps")
+    ms_per_step = ms / args.steps
+    mid = ctx + args.warmup + args.steps // 2          # mean history over the timed steps
+    nbytes = talker_bytes(g, B, mid)
+    achieved = nbytes / (ms_per_step / 1e3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:  # pragma: no cover
+            threads = 1
+        model = TK.TalkerOracle(W, g, keep=True)
+        Kf = (K.astype(np.uint32) << 16).view(np.float32).astype(np.float64)[:, :ctx]
+        Vf = (V.astype(np.uint32) << 16).view(np.float32).astype(np.float64)[:, :ctx]
+        Xh = X.cpu().numpy()
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            TK.decode_step(model, Xh[n % 16, 0], ctx, Kf, Vf)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_budget or n >= 64:
+                break
+        cpu = {"value": round(n / el, 4), "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+               "sample": f"{n} decode step(s) of 1 request at a {ctx}-position history, fp64 NumPy, "
+                         f"{el:.1f} s (after materialising the weights)"}
+    line = {
+        "metric": TALKER_METRIC,
+        "value": round(B * args.steps / (ms / 1e3), 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "history": ctx,
+                   "talker": f"d={g.d_model} L={g.n_layers} heads={g.n_q_heads}/{g.n_kv_heads}x{g.head_dim} "
+                             f"F={g.d_ffn} V={g.vocab}",
+                   "weights": g.weight_dtype, "algorithmic_bytes_per_step": nbytes},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    tk.close()
+
+
 def cpu_baseline(wl, W, H, q0, budget_s: float, sampling=None, U=None):
     """The oracle as it stands, on the host, for about ``budget_s`` seconds of
     frames of the same workload (sampled frames when ``sampling`` is given)."""
@@ -151,7 +250,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--workload", default="b1", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--workload", default="b1", choices=sorted(synth.WORKLOADS) + sorted(synth.TALKER_WORKLOADS))
     ap.add_argument("--stepwise", action="store_true", help="one kernel per phase instead of the persistent kernel")
     ap.add_argument("--generic", action="store_true", help="the generic persistent kernel even where a specialised one exists")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -176,6 +275,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.calibrate_copy:
         calibrate_copy(torch, dev)
+        return
+    if args.workload in synth.TALKER_WORKLOADS:
+        run_talker(args, torch, dev)
         return
     wl = synth.WORKLOADS[args.workload]
     g = wl.geom

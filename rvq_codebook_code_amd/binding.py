@@ -40,6 +40,9 @@ EMB_FORMATS = {"f32": 0, "bf16": 1, "ema": 2}
 
 EXPORTED = ["qp_create", "qp_run_frames", "qp_run_frames_ex", "qp_run_frames_sampled", "qp_sample_logits",
             "qp_get_error", "qp_last_device_flags", "qp_destroy", "qp_status_string", "qp_last_error"]
+# include/qp_talker.h
+EXPORTED_TALKER = ["qp_talker_create", "qp_talker_load_history", "qp_talker_step", "qp_talker_get_error",
+                   "qp_talker_last_device_flags", "qp_talker_destroy"]
 
 
 class QpGeometry(C.Structure):
@@ -66,6 +69,17 @@ class QpSampling(C.Structure):
     _fields_ = [("temperature", C.c_float), ("top_k", C.c_int32), ("top_p", C.c_float)]
 
 
+class QpTalkerGeometry(C.Structure):
+    _fields_ = [("d_model", C.c_int32), ("n_layers", C.c_int32), ("n_q_heads", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("d_ffn", C.c_int32), ("vocab", C.c_int32),
+                ("rms_eps", C.c_float), ("rope_base", C.c_float), ("weight_dtype", C.c_int32),
+                ("max_batch", C.c_int32), ("n_slots", C.c_int32), ("max_ctx", C.c_int32)]
+
+
+class QpTalkerWeights(C.Structure):
+    _fields_ = [("layers", C.c_void_p), ("output_norm", C.c_void_p), ("codec_head", C.c_void_p)]
+
+
 class QpError(RuntimeError):
     def __init__(self, status: int, what: str, detail: str):
         super().__init__(f"{what}: status {status} ({detail})")
@@ -82,6 +96,12 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m rvq_codebook_code_amd.build`")
+    # torch brings its own HIP runtime with the same soname as the system one;
+    # load it first so that the library binds to the runtime torch uses
+    try:
+        import torch  # noqa: F401
+    except ImportError:  # pragma: no cover
+        pass
     lib = C.CDLL(path)
     vp, i32, u32 = C.c_void_p, C.c_int32, C.c_uint32
     lib.qp_create.argtypes = [C.POINTER(QpWeights), C.POINTER(QpGeometry), i32, C.POINTER(vp)]
@@ -94,6 +114,18 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     lib.qp_run_frames_sampled.restype = i32
     lib.qp_sample_logits.argtypes = [vp, i32, i32, C.c_int64, C.POINTER(QpSampling), vp, i32, vp, vp]
     lib.qp_sample_logits.restype = i32
+    lib.qp_talker_create.argtypes = [C.POINTER(QpTalkerWeights), C.POINTER(QpTalkerGeometry), i32, C.POINTER(vp)]
+    lib.qp_talker_create.restype = i32
+    lib.qp_talker_load_history.argtypes = [vp, i32, i32, vp, vp, vp]
+    lib.qp_talker_load_history.restype = i32
+    lib.qp_talker_step.argtypes = [vp, i32, vp, vp, vp, i32, vp, vp, vp, vp]
+    lib.qp_talker_step.restype = i32
+    lib.qp_talker_get_error.argtypes = [vp]
+    lib.qp_talker_get_error.restype = i32
+    lib.qp_talker_last_device_flags.argtypes = [vp]
+    lib.qp_talker_last_device_flags.restype = u32
+    lib.qp_talker_destroy.argtypes = [vp]
+    lib.qp_talker_destroy.restype = None
     lib.qp_get_error.argtypes = [vp]
     lib.qp_get_error.restype = i32
     lib.qp_last_device_flags.argtypes = [vp]
@@ -273,3 +305,83 @@ def sample_logits(logits, uniforms, tokens_out, temperature: float, top_k: int =
     st = lib.qp_sample_logits(_dptr(logits), rows, V, logits.stride(0), C.byref(sp), _dptr(uniforms), 1,
                               _dptr(tokens_out), stream)
     _check(lib, st, "qp_sample_logits")
+
+
+class Talker:
+    """One ``qp_talker``: Talker weights resident on one GPU, a bf16 KV cache
+    of n_slots x max_ctx positions, scratch for max_batch rows."""
+
+    def __init__(self, W: dict, geom, max_batch: int, n_slots: int, max_ctx: int, device: int = 0):
+        self.lib = load_library()
+        self.geom = geom
+        self.max_batch, self.n_slots, self.max_ctx = max_batch, n_slots, max_ctx
+        keep = []
+
+        def ptr(a):
+            a = np.ascontiguousarray(a)
+            keep.append(a)
+            return a.ctypes.data
+
+        n = len(W["layers"])
+        arr = (QpLayerWeights * max(n, 1))()
+        for i, lw in enumerate(W["layers"]):
+            for f, _ in QpLayerWeights._fields_:
+                setattr(arr[i], f, ptr(lw[f]))
+        w = QpTalkerWeights(C.cast(arr, C.c_void_p), ptr(W["output_norm"]), ptr(W["codec_head"]))
+        g = QpTalkerGeometry(geom.d_model, geom.n_layers, geom.n_q_heads, geom.n_kv_heads, geom.head_dim,
+                             geom.d_ffn, geom.vocab, geom.rms_eps, geom.rope_base, WEIGHT_DTYPES[geom.weight_dtype],
+                             max_batch, n_slots, max_ctx)
+        h = C.c_void_p()
+        _check(self.lib, self.lib.qp_talker_create(C.byref(w), C.byref(g), device, C.byref(h)), "qp_talker_create")
+        self.h = h
+
+    def load_history(self, slot: int, K, V, stream=None):
+        """K, V: device uint16 (bf16 bits) [L, n, nkv, hd] of positions 0..n-1."""
+        import torch
+        n = 0 if K is None else K.shape[1]
+        if K is not None:
+            assert K.is_cuda and K.is_contiguous() and V.is_contiguous() and K.dtype == torch.int16
+            assert tuple(K.shape) == tuple(V.shape)
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        _check(self.lib, self.lib.qp_talker_load_history(self.h, slot, n, _dptr(K), _dptr(V), stream),
+               "qp_talker_load_history")
+
+    def step(self, x, slots, pos, max_len: int, H_out, q0_out, logits_out=None, stream=None):
+        """Enqueue one decode step for B = x.shape[0] requests."""
+        import torch
+        B = x.shape[0]
+        for t in (x, slots, pos, H_out, q0_out, logits_out):
+            if t is not None:
+                assert t.is_cuda and t.is_contiguous()
+        assert x.dtype == torch.float32 and tuple(x.shape) == (B, self.geom.d_model)
+        assert slots.dtype == torch.int32 and pos.dtype == torch.int32 and tuple(slots.shape) == (B,)
+        assert H_out.dtype == torch.float32 and tuple(H_out.shape) == (B, self.geom.d_model)
+        assert q0_out.dtype == torch.int32 and tuple(q0_out.shape) == (B,)
+        if logits_out is not None:
+            assert logits_out.dtype == torch.float32 and tuple(logits_out.shape) == (B, self.geom.vocab)
+        if stream is None:
+            stream = torch.cuda.current_stream(x.device).cuda_stream
+        st = self.lib.qp_talker_step(self.h, B, _dptr(x), _dptr(slots), _dptr(pos), max_len, _dptr(H_out),
+                                     _dptr(q0_out), _dptr(logits_out), stream)
+        _check(self.lib, st, "qp_talker_step")
+
+    def get_error(self) -> int:
+        st = self.lib.qp_talker_get_error(self.h)
+        if st == QP_OK:
+            return 0
+        if st == QP_ERR_DEVICE_FLAG:
+            return int(self.lib.qp_talker_last_device_flags(self.h))
+        _check(self.lib, st, "qp_talker_get_error")
+        return 0
+
+    def close(self):
+        if getattr(self, "h", None):
+            self.lib.qp_talker_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -266,7 +266,7 @@ float half_to_float(uint16_t h) {
 }
 
 struct Uploader {
-    qp_handle* h;
+    std::vector<void*>* allocs;   // the owning handle's allocation list
     qp_status st = QP_OK;
     std::string msg;
 
@@ -280,7 +280,7 @@ struct Uploader {
             (void)hipGetLastError();
             return nullptr;
         }
-        h->allocs.push_back(p);
+        allocs->push_back(p);
         return p;
     }
     void* upload(const void* src, size_t bytes) {
@@ -464,8 +464,11 @@ namespace {
 // --- batched matrix-core path ---------------------------------------------
 
 // Launches one product; returns the number of column tiles (gridDim.x).
-template <int WT, int SRC, int EPI>
-int tiled_gemm(const qp_handle* h, qp::tiled::GemmArgs g, hipStream_t stream) {
+// h: any handle with the split-K scratch (t_part, t_part_floats, t_ctr, t_nctr).
+// split_rt1: also split K for a single row tile (large products; for the
+// predictor's shapes the fixup cost more than it saved).
+template <int WT, int SRC, int EPI, class Handle>
+int tiled_gemm(const Handle* h, qp::tiled::GemmArgs g, hipStream_t stream, bool split_rt1 = false) {
     namespace T = qp::tiled;
     const int RT = g.M <= 16 ? 1 : (g.M <= 32 ? 2 : 4);
     // one row tile: one 16-column fragment per workgroup (twice the
@@ -479,10 +482,12 @@ int tiled_gemm(const qp_handle* h, qp::tiled::GemmArgs g, hipStream_t stream) {
     // a single row tile the ordered fixup costs more than it saves.
     const int tiles = gx * gy;
     int KS = 1;
-    if ((EPI == T::EPI_RESID || EPI == T::EPI_BIAS) && RT > 1 && tiles < 256 &&
+    if ((EPI == T::EPI_RESID || EPI == T::EPI_BIAS) && (RT > 1 || split_rt1) && tiles < 256 &&
         static_cast<size_t>(tiles) <= h->t_nctr) {
         for (int c = 2; c <= T::kMaxKS; ++c) {
-            if ((g.K / 256) % c != 0) continue;
+            // whole pairs of 32-wide blocks per wave: 4 waves (RT > 1) need
+            // K / 256 divisible by c, 8 waves (RT = 1) by 2c
+            if ((g.K / 256) % (RT == 1 ? 2 * c : c) != 0) continue;
             if (static_cast<size_t>(c) * tiles * RT * CT * 256 > h->t_part_floats) break;
             KS = c;
             if (c * tiles >= 256) break;
@@ -879,7 +884,7 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
     m.eps = g->rms_eps;
     m.attn_scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(m.hd)));
 
-    Uploader up{h};
+    Uploader up{&h->allocs};
     const int wt = h->q4 ? WT_Q4 : m.wt;   // storage format of the host weights
     // batched matrix-core path: bf16 or Q8_0 weights whose widths tile into
     // 32 x 256 blocks (every K split four ways into whole 32-wide blocks,
@@ -1208,3 +1213,6 @@ void qp_destroy(qp_handle* h) {
 }
 
 }  // extern "C"
+
+// the Talker decode step (include/qp_talker.h)
+#include "qp_talker_host.h"

@@ -13,8 +13,8 @@ from rvq_codebook_code_amd import synth
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def header_functions():
-    text = open(os.path.join(ROOT, "include", "qp.h")).read()
+def header_functions(name="qp.h"):
+    text = open(os.path.join(ROOT, "include", name)).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(qp_[a-z_]+)\s*\(", text)))
 
@@ -115,3 +115,37 @@ def test_sampling_arguments_rejected_before_the_gpu(lib):
     assert lib.qp_sample_logits(None, 3, 256, 256, C.byref(sp), None, 1, None, None) == bd.QP_ERR_INVALID_ARG
     assert lib.qp_run_frames_sampled(None, 1, None, None, C.byref(sp), None, None, None, None, None, None) == \
         bd.QP_ERR_INVALID_ARG
+
+
+def test_talker_functions_exported_and_rejected_before_the_gpu(lib):
+    names = header_functions("qp_talker.h")
+    assert sorted(bd.EXPORTED_TALKER) == names
+    for n in names:
+        assert hasattr(lib, n), n
+    h = C.c_void_p()
+    assert lib.qp_talker_create(None, None, 0, C.byref(h)) == bd.QP_ERR_INVALID_ARG
+    assert lib.qp_talker_step(None, 1, None, None, None, 1, None, None, None, None) == bd.QP_ERR_INVALID_ARG
+    assert lib.qp_talker_load_history(None, 0, 0, None, None, None) == bd.QP_ERR_INVALID_ARG
+    assert lib.qp_talker_get_error(None) == bd.QP_ERR_INVALID_ARG
+    lib.qp_talker_destroy(None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("n_q_heads", 24, "QP_ERR_GEOMETRY"),      # neither nkv nor 2*nkv
+    ("head_dim", 96, "QP_ERR_GEOMETRY"),
+    ("d_model", 2000, "QP_ERR_SHAPE"),
+    ("vocab", 3000, "QP_ERR_SHAPE"),
+    ("weight_dtype", 0, "QP_ERR_DTYPE"),        # f32 talker weights are not supported
+    ("max_ctx", 0, "QP_ERR_GEOMETRY"),
+    ("n_slots", 0, "QP_ERR_GEOMETRY"),
+])
+def test_talker_geometry_validation(lib, field, value, status):
+    wl = synth.TALKER_WORKLOADS["talker_tiny"]
+    g = wl.geom
+    geo = bd.QpTalkerGeometry(g.d_model, g.n_layers, g.n_q_heads, g.n_kv_heads, g.head_dim, g.d_ffn, g.vocab,
+                              g.rms_eps, g.rope_base, bd.WEIGHT_DTYPES[g.weight_dtype], 4, 4, 64)
+    setattr(geo, field, value)
+    w = bd.QpTalkerWeights(None, None, None)
+    h = C.c_void_p()
+    assert lib.qp_talker_create(C.byref(w), C.byref(geo), 0, C.byref(h)) == getattr(bd, status)
+    assert not h.value

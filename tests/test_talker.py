@@ -13,6 +13,7 @@ pinned there.  GPU parity compares the HIP path with the oracle on the same
 seeded weights, histories and inputs.
 """
 import dataclasses
+import math
 
 import numpy as np
 import pytest
@@ -88,3 +89,182 @@ def synth_bits_to_f64(bits):
     helper) so the closed form above is checked by a second route."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
     return b.view(np.float32).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# GPU parity through the C ABI
+# ----------------------------------------------------------------------------
+
+MARGIN = 0.05       # q0 compared where the oracle's top-2 logit gap exceeds it
+
+
+def tol_for(n_layers):
+    """Bar for H and logits: the bf16 bar of the predictor (3e-2 at its 5
+    layers), scaled by sqrt(depth / 5).  Every layer rounds its product
+    operands, the attention output and the SwiGLU output to bf16; the
+    rounding errors are independent and add in quadrature, so the drift grows
+    as sqrt(depth).  (An oracle run that rounds at the same places drifts by
+    8.7e-3, 1.9e-2 and 3.6e-2 from the exact one at 2, 8 and 28 layers of the
+    1.7B widths.)"""
+    return 3e-2 * math.sqrt(max(n_layers, 5) / 5.0)
+
+
+def _torch_dev():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch, torch.device("cuda:0")
+
+
+def _bits_to_dev(torch, dev, bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev)
+
+
+def _run_and_compare(name, model, tk, geom, slots, hist, X, max_batch_rows=None, keep_layers=True):
+    """Load each row's history into its slot, run the steps on the GPU and
+    compare every step with the oracle run from the same history."""
+    torch, dev = _torch_dev()
+    from rvq_codebook_code_amd import binding as bd  # noqa: F401
+    B = len(slots)
+    steps = X.shape[0]
+    for b in range(B):
+        K, V = hist[b]
+        if K.shape[1]:
+            tk.load_history(int(slots[b]), _bits_to_dev(torch, dev, K), _bits_to_dev(torch, dev, V))
+    n0 = np.array([hist[b][0].shape[1] for b in range(B)])
+    st = torch.from_numpy(np.asarray(slots, dtype=np.int32)).to(dev)
+    H = torch.full((B, geom.d_model), float("nan"), device=dev)
+    q0 = torch.full((B,), -1, dtype=torch.int32, device=dev)
+    lg = torch.full((B, geom.vocab), float("nan"), device=dev)
+    got = []
+    for i in range(steps):
+        pos = n0 + i
+        pt = torch.from_numpy(pos.astype(np.int32)).to(dev)
+        tk.step(torch.from_numpy(np.ascontiguousarray(X[i])).to(dev), st, pt, int(pos.max()) + 1, H, q0, lg)
+        torch.cuda.synchronize()
+        got.append((H.cpu().numpy().copy(), q0.cpu().numpy().copy(), lg.cpu().numpy().copy()))
+    assert tk.get_error() == 0
+    worst_h = worst_l = 0.0
+    agree = sure_n = 0
+    for b in range(B):
+        K = synth_bits_to_f64(hist[b][0])
+        V = synth_bits_to_f64(hist[b][1])
+        ref = TK.run_steps(model, X[:, b].astype(np.float64), int(n0[b]), K, V)
+        for i in range(steps):
+            h_err = np.abs(got[i][0][b] - ref[i]["H"]).max()
+            l_err = np.abs(got[i][2][b] - ref[i]["logits"]).max()
+            worst_h, worst_l = max(worst_h, h_err), max(worst_l, l_err)
+            if ref[i]["margin"] > MARGIN:
+                sure_n += 1
+                agree += int(got[i][1][b] == ref[i]["q0"])
+                assert got[i][1][b] == ref[i]["q0"], (name, b, i)
+    tol = tol_for(geom.n_layers)
+    print(f"[{name}] H max-abs {worst_h:.3g} logits max-abs {worst_l:.3g} (bar {tol:.3g}) "
+          f"q0 decisive {sure_n}/{B * steps}")
+    assert worst_h <= tol and worst_l <= tol
+    return got
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name", ["talker_tiny", "talker_l2"])
+def test_talker_steps_against_oracle(name):
+    """Rows in permuted slots with histories of different lengths (empty,
+    short, several attention splits), three consecutive steps each."""
+    _torch_dev()
+    from rvq_codebook_code_amd import binding as bd
+    wl = synth.TALKER_WORKLOADS[name]
+    g = wl.geom
+    W = synth.make_talker_weights(g, wl.weight_seed)
+    model = TK.TalkerOracle(W, g)
+    lens = [0, 5, 37, wl.context] if name == "talker_l2" else [0, 3, 17, wl.context]
+    slots = [3, 0, 5, 1]
+    hist = [synth.make_talker_history(g, n, wl.input_seed + 10 + b) for b, n in enumerate(lens)]
+    X = synth.make_talker_inputs(g, len(slots), 3, wl.input_seed)
+    tk = bd.Talker(W, g, max_batch=8, n_slots=6, max_ctx=wl.context + 8)
+    _run_and_compare(name, model, tk, g, slots, hist, X)
+    tk.close()
+
+
+@pytest.mark.gpu
+def test_talker_flags_and_cache_untouched():
+    """A row with a position past max_len or an unknown slot raises its flag
+    and writes nothing: a later valid step still matches the oracle."""
+    torch, dev = _torch_dev()
+    from rvq_codebook_code_amd import binding as bd
+    wl = synth.TALKER_WORKLOADS["talker_tiny"]
+    g = wl.geom
+    W = synth.make_talker_weights(g, wl.weight_seed)
+    model = TK.TalkerOracle(W, g)
+    tk = bd.Talker(W, g, max_batch=4, n_slots=4, max_ctx=64)
+    K, V = synth.make_talker_history(g, 20, 77)
+    tk.load_history(2, _bits_to_dev(torch, dev, K), _bits_to_dev(torch, dev, V))
+    x = torch.from_numpy(synth.make_talker_inputs(g, 1, 1, 5)[0]).to(dev)
+    H = torch.zeros((1, g.d_model), device=dev)
+    q0 = torch.zeros((1,), dtype=torch.int32, device=dev)
+    for slot, pos, bit in [(2, 40, 1), (9, 20, 2), (-1, 20, 2), (2, -3, 1)]:
+        tk.step(x, torch.tensor([slot], dtype=torch.int32, device=dev), torch.tensor([pos], dtype=torch.int32, device=dev),
+                21, H, q0)
+        assert tk.get_error() & bit
+    with pytest.raises(bd.QpError):
+        tk.step(x, torch.tensor([2], dtype=torch.int32, device=dev), torch.tensor([20], dtype=torch.int32, device=dev),
+                65, H, q0)
+    X = synth.make_talker_inputs(g, 1, 2, 6)
+    _run_and_compare("talker_tiny after flags", model, tk, g, [2], [(K, V)], X)
+    tk.close()
+
+
+@pytest.mark.gpu
+def test_talker_full_depth_rows():
+    """The 1.7B Talker (28 layers) on two rows, 1 and 700 positions of
+    history, one step, against the oracle run layer by layer."""
+    _torch_dev()
+    from rvq_codebook_code_amd import binding as bd
+    wl = synth.TALKER_WORKLOADS["talker_b1"]
+    g = wl.geom
+    W = synth.make_talker_weights(g, wl.weight_seed)
+    model = TK.TalkerOracle(W, g, keep=False)
+    hist = [synth.make_talker_history(g, n, 901 + n) for n in (1, 700)]
+    X = synth.make_talker_inputs(g, 2, 1, 902)
+    tk = bd.Talker(W, g, max_batch=2, n_slots=2, max_ctx=704)
+    _run_and_compare("talker 1.7B", model, tk, g, [1, 0], hist, X)
+    tk.close()
+
+
+@pytest.mark.gpu
+def test_talker_graph_replays_equal_direct_launches():
+    """Steps replayed from graphs (no logits hook) equal the directly
+    launched ones bit for bit, as the history grows across split-count
+    buckets and the batch size changes."""
+    torch, dev = _torch_dev()
+    from rvq_codebook_code_amd import binding as bd
+    wl = synth.TALKER_WORKLOADS["talker_tiny"]
+    g = wl.geom
+    W = synth.make_talker_weights(g, wl.weight_seed)
+    tk = bd.Talker(W, g, max_batch=4, n_slots=8, max_ctx=160)
+    lens = [29, 60, 3, 0]
+    for b, n in enumerate(lens):
+        K, V = synth.make_talker_history(g, n, 300 + b)
+        if n:
+            for base in (0, 4):                   # the same history in slots b and b + 4
+                tk.load_history(b + base, _bits_to_dev(torch, dev, K), _bits_to_dev(torch, dev, V))
+    X = synth.make_talker_inputs(g, 4, 40, 301)
+    for i in range(40):
+        B = 4 if i % 7 else 2
+        pos = np.array(lens[:B]) + i
+        xs = torch.from_numpy(np.ascontiguousarray(X[i, :B])).to(dev)
+        pt = torch.from_numpy(pos.astype(np.int32)).to(dev)
+        outs = []
+        for base, with_logits in ((0, True), (4, False)):
+            st = torch.arange(base, base + B, dtype=torch.int32, device=dev)
+            H = torch.zeros((B, g.d_model), device=dev)
+            q0 = torch.zeros((B,), dtype=torch.int32, device=dev)
+            lg = torch.zeros((B, g.vocab), device=dev) if with_logits else None
+            tk.step(xs, st, pt, int(pos.max()) + 1, H, q0, lg)
+            torch.cuda.synchronize()
+            outs.append((H.cpu().numpy(), q0.cpu().numpy()))
+        np.testing.assert_array_equal(outs[0][0], outs[1][0])
+        np.testing.assert_array_equal(outs[0][1], outs[1][1])
+    # (rows 2 and 3 skip the steps with B = 2, leaving cleared positions in
+    # their history; both slot sets skip the same ones)
+    assert tk.get_error() == 0
+    tk.close()
