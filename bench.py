@@ -344,9 +344,9 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, W, H, q0, args.cpu_budget, sampling, U if sampling else None)
 
-    # arithmetic type of the products: fp32 on the dataflow/generic paths,
-    # bf16 operands with fp32 accumulation on the matrix cores
-    dtype = "bf16" if driver == "tiled" else "f32"
+    # arithmetic type of the products: bf16 operands with fp32 accumulation
+    # on the matrix cores and in the dataflow kernel, fp32 on the generic path
+    dtype = "bf16" if driver in ("tiled", "dataflow") else "f32"
     line = {
         "metric": METRIC,
         "value": round(frames_per_s, 2),

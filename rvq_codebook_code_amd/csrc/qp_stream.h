@@ -9,6 +9,10 @@
 //    records the workgroup needs (16-byte device-scope loads, two records per
 //    lane), stage them in one of two LDS slots and meet at one workgroup
 //    barrier; a single wave cannot pull the inputs fast enough alone;
+//  * the matrix-vector products round their activations to bf16 pairs and
+//    use the pairwise bf16 dot instruction with fp32 accumulation (the same
+//    operand rounding as the batched matrix-core path); norms, softmax,
+//    SwiGLU and the residual stream stay fp32;
 //  * each phase's weights are requested at the end of the previous phase,
 //    right after that phase's records were stored (a CU's memory requests
 //    drain roughly in order, so a store issued behind a weight burst would
@@ -228,6 +232,23 @@ __device__ __forceinline__ float dot8(const uint4 w, const float a[8], float acc
     return acc;
 }
 
+// activations packed to bf16 pairs (round to nearest even), element 2i in
+// the low half: the operand order of the weights' bf16 pairs
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void pack8(const float a[8], bf16x2_t p[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_convertvector(f32x2_t{a[2 * i], a[2 * i + 1]}, bf16x2_t);
+}
+// acc + w . a over 8 bf16 products (pairwise dot instructions)
+__device__ __forceinline__ float dot8p(const uint4 w, const bf16x2_t p[4], float acc) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x), p[0], acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y), p[1], acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.z), p[2], acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w), p[3], acc, false);
+    return acc;
+}
+
 __device__ __forceinline__ void lds8(const float* p, float a[8]) {
     const float4 u = *reinterpret_cast<const float4*>(p);
     const float4 v = *reinterpret_cast<const float4*>(p + 4);
@@ -430,7 +451,9 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                 for (int c = 0; c < 4; ++c) {
                     float x8[8];
                     lds8(Hs + r * DT + c * 512 + lane * 8, x8);
-                    acc = dot8(wP[c], x8, acc);
+                    bf16x2_t p8[4];
+                    pack8(x8, p8);
+                    acc = dot8p(wP[c], p8, acc);
                 }
                 const float v = wave_sum(acc) + bias;
                 if (lane == 0) st_rec(rc.X + static_cast<size_t>(r) * DP + n, v, tag_of(0));
@@ -490,8 +513,10 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                     for (int c = 0; c < 2; ++c) {
                         float x8[8];
                         act8(xs + r * DP, ga, c, x8);
+                        bf16x2_t p8[4];
+                        pack8(x8, p8);
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) acc[q] = dot8(wQ[q * 2 + c], x8, acc[q]);
+                        for (int q = 0; q < 4; ++q) acc[q] = dot8p(wQ[q * 2 + c], p8, acc[q]);
                     }
                     const float rinv = __builtin_amdgcn_rsqf(row_ss(par, r) / static_cast<float>(DP) + eps);
                     wave_sums(acc);
@@ -645,7 +670,9 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                     for (int c = 0; c < 4; ++c) {
                         float x8[8];
                         lds8(as + r * QD + c * 512 + lane * 8, x8);
-                        acc = dot8(wO[c], x8, acc);
+                        bf16x2_t p8[4];
+                        pack8(x8, p8);
+                        acc = dot8p(wO[c], p8, acc);
                     }
                     const float d = wave_sum(acc);
                     float nv = 0.f;
@@ -672,10 +699,12 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                     for (int c = 0; c < 2; ++c) {
                         float x8[8];
                         act8(xs + r * DP, gf, c, x8);
+                        bf16x2_t p8[4];
+                        pack8(x8, p8);
 #pragma unroll
                         for (int q = 0; q < 3; ++q) {
-                            ag[q] = dot8(wU[q * 2 + c], x8, ag[q]);
-                            au[q] = dot8(wU[6 + q * 2 + c], x8, au[q]);
+                            ag[q] = dot8p(wU[q * 2 + c], p8, ag[q]);
+                            au[q] = dot8p(wU[6 + q * 2 + c], p8, au[q]);
                         }
                     }
                     const float rinv = __builtin_amdgcn_rsqf(row_ss(par, r) / static_cast<float>(DP) + eps);
@@ -710,7 +739,9 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                     for (int c = 0; c < 6; ++c) {
                         float x8[8];
                         lds8(hs + r * F + c * 512 + lane * 8, x8);
-                        acc = dot8(wD[c], x8, acc);
+                        bf16x2_t p8[4];
+                        pack8(x8, p8);
+                        acc = dot8p(wD[c], p8, acc);
                     }
                     const float d = wave_sum(acc);
                     float nv = 0.f;
@@ -748,8 +779,10 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                     for (int c = 0; c < 2; ++c) {
                         float x8[8];
                         act8(xs + b * DP, g_out, c, x8);
-                        acc0 = dot8(wL[c], x8, acc0);
-                        acc1 = dot8(wL[2 + c], x8, acc1);
+                        bf16x2_t p8[4];
+                        pack8(x8, p8);
+                        acc0 = dot8p(wL[c], p8, acc0);
+                        acc1 = dot8p(wL[2 + c], p8, acc1);
                     }
                     const float rinv = __builtin_amdgcn_rsqf(row_ss(par, b) / static_cast<float>(DP) + eps);
                     float lg[2] = {acc0, acc1};

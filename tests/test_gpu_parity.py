@@ -207,8 +207,12 @@ def test_dataflow_kernel_against_oracle_and_generic(B):
     for f in range(3):
         ref, got = check_against_oracle(f"dataflow B={B}", model, pred, H[f], q0[f], rows)
         force = ref["tokens"].astype(np.int32)
+        # the dataflow kernel rounds its product operands to bf16 (the generic
+        # path keeps them fp32): the two agree to the bf16-weight bar
         gen = gpu_frame(pred, H[f], q0[f], force=force, generic=True)
-        assert np.abs(gen["logits"] - got["logits"]).max() <= 1e-4
+        lg = np.abs(gen["logits"] - got["logits"]).max()
+        print(f"[dataflow B={B} vs generic] logits max-abs {lg:.3g}")
+        assert lg <= TOL["bf16"]
         assert np.abs(gen["embsum"] - got["embsum"]).max() <= 1e-5
 
 
@@ -219,7 +223,7 @@ def test_dataflow_kernel_taps_and_repeat():
     got = gpu_frame(pred, H[0], q0[0], force=ref["tokens"].astype(np.int32), taps=True)
     err = np.abs(got["taps"] - ref["taps"]).max()
     print(f"[dataflow taps] max-abs {err:.3g}")
-    assert err <= 1e-3
+    assert err <= TOL["bf16"]
     again = gpu_frame(pred, H[0], q0[0], force=ref["tokens"].astype(np.int32), taps=True)
     for key in ("tokens", "logits", "embsum", "taps"):
         np.testing.assert_array_equal(again[key], got[key])
