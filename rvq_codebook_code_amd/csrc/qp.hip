@@ -113,6 +113,13 @@ __global__ void k_copy32(const uint32_t* __restrict__ src, uint32_t* __restrict_
         dst[i] = src[i];
 }
 
+// 64-bit word fill (clearing the dataflow kernel's records)
+__global__ void k_fill64(uint64_t* __restrict__ dst, size_t n) {
+    for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
+         i += static_cast<size_t>(gridDim.x) * blockDim.x)
+        dst[i] = 0ull;
+}
+
 // --- create-time kernels ----------------------------------------------------
 
 // EMA codebook: E[v][k] = S[v][k] / (u[v] + 1e-7), fp32 add then fp32 divide.
@@ -185,6 +192,7 @@ struct qp_handle {
     // dataflow kernel for small batches of the 1.7B predictor geometry
     bool stream_ok = false;
     qp::stream::Recs recs{};
+    size_t nrecs = 0;   // records in the allocation at recs.X
     uint32_t seq = 0;
     // batched matrix-core path
     bool tiled_ok = false;
@@ -775,6 +783,14 @@ qp_status launch_frame(qp_handle* h, const RunArgs& a, hipStream_t stream, bool 
     }
     if constexpr (WT == WT_BF16) {
         if (!stepwise && !generic && h->stream_ok && a.B <= 2) {
+            const uint32_t ppf = static_cast<uint32_t>(qp::stream::phases_per_frame(m.L));
+            if (h->seq > 0xFFFFFFFFu - 2u * ppf) {
+                // the 32-bit phase tags would wrap: clear every record (tag 0 is
+                // never current) so no record left from long ago can match a new tag
+                hipLaunchKernelGGL(k_fill64, dim3(64), dim3(256), 0, stream, h->recs.X, h->nrecs);
+                if (!check_hip(hipGetLastError(), "record clear", &st)) return st;
+                h->seq = 0;
+            }
             RunArgs ra = a;
             ra.seq0 = h->seq;
             Model mm = m;
@@ -786,7 +802,7 @@ qp_status launch_frame(qp_handle* h, const RunArgs& a, hipStream_t stream, bool 
                                                       0, stream),
                            "cooperative launch (dataflow kernel)", &st))
                 return st;
-            h->seq += static_cast<uint32_t>(qp::stream::phases_per_frame(m.L));
+            h->seq += ppf;
             return QP_OK;
         }
     }
@@ -1023,6 +1039,7 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
             const size_t nrec = static_cast<size_t>(MR) * (S::DP + S::NQKV + S::QD + S::F) + 2ull * S::kNwg * 2;
             uint64_t* r = static_cast<uint64_t*>(up.alloc(nrec * 8));
             if (r) {
+                h->nrecs = nrec;
                 h->recs.X = r;
                 h->recs.QKV = h->recs.X + MR * S::DP;
                 h->recs.AO = h->recs.QKV + MR * S::NQKV;
