@@ -220,18 +220,6 @@ __device__ __forceinline__ void dma64(const float* src, float* dst) {
 // compute side helpers
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ float dot8(const uint4 w, const float a[8], float acc) {
-    acc = fmaf(__uint_as_float(w.x << 16), a[0], acc);
-    acc = fmaf(__uint_as_float(w.x & 0xFFFF0000u), a[1], acc);
-    acc = fmaf(__uint_as_float(w.y << 16), a[2], acc);
-    acc = fmaf(__uint_as_float(w.y & 0xFFFF0000u), a[3], acc);
-    acc = fmaf(__uint_as_float(w.z << 16), a[4], acc);
-    acc = fmaf(__uint_as_float(w.z & 0xFFFF0000u), a[5], acc);
-    acc = fmaf(__uint_as_float(w.w << 16), a[6], acc);
-    acc = fmaf(__uint_as_float(w.w & 0xFFFF0000u), a[7], acc);
-    return acc;
-}
-
 // activations packed to bf16 pairs (round to nearest even), element 2i in
 // the low half: the operand order of the weights' bf16 pairs
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
@@ -256,21 +244,9 @@ __device__ __forceinline__ void lds8(const float* p, float a[8]) {
     a[4] = v.x; a[5] = v.y; a[6] = v.z; a[7] = v.w;
 }
 
-__device__ __forceinline__ void gain8(const float4 g0, const float4 g1, float a[8]) {
-    a[0] *= g0.x; a[1] *= g0.y; a[2] *= g0.z; a[3] *= g0.w;
-    a[4] *= g1.x; a[5] *= g1.y; a[6] *= g1.z; a[7] *= g1.w;
-}
-
 __device__ __forceinline__ uint32_t ordered_bits(float v) {
     uint32_t u = __float_as_uint(v == 0.0f ? 0.0f : v);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ void ld_gain(const float* g, int lane, float4 out[4]) {
-    // the 16 gains a lane needs for K = 1024: k = lane*8..+7 and 512 + lane*8..+7
-    const float4* p = reinterpret_cast<const float4*>(g + lane * 8);
-    const float4* q = reinterpret_cast<const float4*>(g + 512 + lane * 8);
-    out[0] = p[0]; out[1] = p[1]; out[2] = q[0]; out[3] = q[1];
 }
 
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
