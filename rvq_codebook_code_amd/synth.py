@@ -343,6 +343,18 @@ TALKER_WORKLOADS: Dict[str, TalkerWorkload] = {
                        vocab=384, rms_eps=1e-6, rope_base=1e4, weight_dtype="bf16"),
         batch=3, context=40, weight_seed=3001, input_seed=4001,
         description="tiny Talker, bf16 weights, B=3, 40 positions of history"),
+    "talker_tiny_q8": TalkerWorkload(
+        "talker_tiny_q8",
+        TalkerGeometry(d_model=256, n_layers=2, n_q_heads=4, n_kv_heads=2, head_dim=64, d_ffn=768,
+                       vocab=384, rms_eps=1e-6, rope_base=1e4, weight_dtype="q8_0"),
+        batch=3, context=40, weight_seed=3011, input_seed=4011,
+        description="tiny Talker, Q8_0 weights, B=3, 40 positions of history"),
+    "talker_tiny_q4": TalkerWorkload(
+        "talker_tiny_q4",
+        TalkerGeometry(d_model=256, n_layers=2, n_q_heads=4, n_kv_heads=2, head_dim=64, d_ffn=768,
+                       vocab=384, rms_eps=1e-6, rope_base=1e4, weight_dtype="q4_0"),
+        batch=3, context=40, weight_seed=3012, input_seed=4012,
+        description="tiny Talker, Q4_0 weights, B=3, 40 positions of history"),
     "talker_l2": TalkerWorkload(
         "talker_l2", TalkerGeometry(n_layers=2, weight_dtype="bf16", **_TALKER_17B),
         batch=4, context=300, weight_seed=3002, input_seed=4002,
