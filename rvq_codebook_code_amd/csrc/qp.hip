@@ -1211,7 +1211,9 @@ qp_status qp_get_error(qp_handle* h) {
         if (!check_hip(hipMemset(h->m.bar, 0, 4096), "hipMemset", &st)) return st;
         h->bar_base = 0;
     }
-    return fail(QP_ERR_DEVICE_FLAG, "device flags 0x" + std::to_string(flags));
+    char hex[16];
+    std::snprintf(hex, sizeof(hex), "0x%x", flags);
+    return fail(QP_ERR_DEVICE_FLAG, std::string("device flags ") + hex);
 }
 
 uint32_t qp_last_device_flags(qp_handle* h) { return h ? h->last_flags : 0u; }

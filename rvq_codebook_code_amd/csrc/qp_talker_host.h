@@ -442,7 +442,9 @@ qp_status qp_talker_get_error(qp_talker* t) {
     t->last_flags = flags;
     if (flags == 0) return QP_OK;
     if (!check_hip(hipMemset(t->err, 0, 4), "hipMemset", &st)) return st;
-    return fail(QP_ERR_DEVICE_FLAG, "talker device flags 0x" + std::to_string(flags));
+    char hex[16];
+    std::snprintf(hex, sizeof(hex), "0x%x", flags);
+    return fail(QP_ERR_DEVICE_FLAG, std::string("talker device flags ") + hex);
 }
 
 uint32_t qp_talker_last_device_flags(qp_talker* t) { return t ? t->last_flags : 0u; }
