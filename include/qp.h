@@ -23,8 +23,10 @@
  *
  * Conventions
  *   - Every function returns a qp_status (0 = success, negative = error) and
- *     never aborts or prints.  qp_last_error() returns a text for the last
- *     failing call on the calling thread.
+ *     never aborts.  qp_last_error() returns a text for the last failing call
+ *     on the calling thread.  Nothing is printed unless the environment
+ *     variable QP_LOG is set; then each failure also writes that text and the
+ *     status name to stderr, one line per failure.
  *   - Weight pointers given to qp_create are HOST pointers; the library copies
  *     and repacks everything before returning, so the caller keeps ownership
  *     and may free them afterwards.

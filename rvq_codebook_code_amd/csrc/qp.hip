@@ -236,8 +236,16 @@ namespace {
 
 thread_local std::string g_last_error;
 
+// QP_LOG set (to anything) in the environment: every failure is also
+// written to stderr, one line each
+bool log_failures() {
+    static const bool on = std::getenv("QP_LOG") != nullptr;
+    return on;
+}
+
 qp_status fail(qp_status st, const std::string& msg) {
     g_last_error = msg;
+    if (log_failures()) std::fprintf(stderr, "qp: %s (%s)\n", msg.c_str(), qp_status_string(st));
     return st;
 }
 
