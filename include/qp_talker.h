@@ -24,8 +24,10 @@
  *
  * Conventions as in qp.h: every call returns a qp_status; pointers to
  * per-step data are DEVICE pointers; calls are asynchronous on `stream`;
- * nothing aborts or prints.  The library owns the KV cache; its slots are
- * addressed by the caller, so any request may use any slot in any batch. */
+ * nothing aborts, and nothing is printed unless QP_LOG is set; calls on one
+ * handle must not overlap (its staging buffers, graphs and split counters are
+ * shared).  The library owns the KV cache; its slots are addressed by the
+ * caller, so any request may use any slot in any batch. */
 #ifndef QP_TALKER_H
 #define QP_TALKER_H
 
