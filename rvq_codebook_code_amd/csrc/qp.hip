@@ -782,7 +782,9 @@ qp_status launch_frame(qp_handle* h, const RunArgs& a, hipStream_t stream, bool 
     qp_status st = QP_OK;
     const Model& m = h->m;
     if constexpr (WT == WT_BF16 || WT == WT_Q8) {
-        if (tiled || (!stepwise && !generic && h->tiled_ok && a.B > 2)) {
+        // the batched path for B > 2, and for any B that the dataflow kernel
+        // cannot take (Q8_0 and Q4_0 weights, other geometries)
+        if (tiled || (!stepwise && !generic && h->tiled_ok && (a.B > 2 || !h->stream_ok))) {
             const bool hooks = a.force || a.logits_out || a.taps;
             if (WT == WT_Q8 && h->q4)
                 return hooks ? launch_tiled<WT_Q4>(h, a, stream) : launch_tiled_graph<WT_Q4>(h, a, stream);

@@ -358,3 +358,19 @@ def test_q4_generic_path_and_full_size():
     wl, W, model, pred = workload("q4_b16")
     H, q0 = synth.make_inputs(wl.geom, wl.batch, 2, wl.input_seed)
     check_against_oracle("q4_b16", model, pred, H[1], q0[1], np.array([0, 9, 15]))
+
+
+@pytest.mark.parametrize("name", ["tiny_q8ema", "tiny_q4"])
+def test_small_batches_with_block_formats_take_the_batched_path(name):
+    """B <= 2 with Q8_0 or Q4_0 weights runs on the batched matrix-core path
+    by default (the dataflow kernel takes bf16 weights only), not on the
+    generic fp32 kernel: the default call equals an explicitly batched one
+    bit for bit, and the oracle within tolerance."""
+    wl, W, model, pred = workload(name)
+    H, q0 = synth.make_inputs(wl.geom, 2, 1, 9100)
+    for B in (1, 2):
+        d = gpu_frame(pred, H[0][:B], q0[0][:B], logits=False)
+        t = gpu_frame(pred, H[0][:B], q0[0][:B], logits=False, tiled=True)
+        np.testing.assert_array_equal(d["tokens"], t["tokens"])
+        np.testing.assert_array_equal(d["embsum"], t["embsum"])
+    check_against_oracle(f"{name} B=1", model, pred, H[0][:1], q0[0][:1], np.arange(1))
