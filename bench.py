@@ -197,7 +197,7 @@ def select_driver(g, B: int, args) -> str:
         return "stepwise"
     if args.generic:
         return "generic"
-    if (B <= 2 and g.weight_dtype == "bf16" and 1 <= g.n_layers <= 5 and
+    if (B <= 2 and g.weight_dtype in ("bf16", "q8_0", "q4_0") and 1 <= g.n_layers <= 5 and
             all(getattr(g, k) == v for k, v in _DATAFLOW_GEOMETRY.items())):
         return "dataflow"
     qd = g.n_q_heads * g.head_dim
@@ -345,8 +345,13 @@ def main():
         cpu = cpu_baseline(wl, W, H, q0, args.cpu_budget, sampling, U if sampling else None)
 
     # arithmetic type of the products: bf16 operands with fp32 accumulation
-    # on the matrix cores and in the dataflow kernel, fp32 on the generic path
-    dtype = "bf16" if driver in ("tiled", "dataflow") else "f32"
+    # on the matrix cores and in the dataflow kernel with bf16 weights; the
+    # dataflow kernel multiplies Q8_0 / Q4_0 codes with fp32 activations, and
+    # the generic path computes in fp32
+    if driver == "tiled" or (driver == "dataflow" and g.weight_dtype == "bf16"):
+        dtype = "bf16"
+    else:
+        dtype = "f32"
     line = {
         "metric": METRIC,
         "value": round(frames_per_s, 2),

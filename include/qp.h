@@ -177,9 +177,9 @@ qp_status qp_run_frames(qp_handle* h, int32_t B, const float* H,
                                    and F multiples of 256, dP and dT <= 4096, nqkv and V multiples
                                    of 32 (else QP_ERR_INVALID_ARG); excludes
                                    the other flags.
-   Without flags the library picks: B <= 2 with bf16 weights and the 1.7B
-   predictor geometry -> the dataflow kernel; otherwise, where the batched
-   path applies -> it; otherwise the generic persistent kernel.             */
+   Without flags the library picks: B <= 2 with bf16, Q8_0 or Q4_0 weights
+   and the 1.7B predictor geometry -> the dataflow kernel; otherwise, where
+   the batched path applies -> it; otherwise the generic persistent kernel. */
 
 /* Same computation with test hooks (any hook may be NULL):
  *   force_tokens int32 [B, 15]  teacher forcing: the token fed back at step

@@ -791,7 +791,7 @@ qp_status launch_frame(qp_handle* h, const RunArgs& a, hipStream_t stream, bool 
             return hooks ? launch_tiled<WT>(h, a, stream) : launch_tiled_graph<WT>(h, a, stream);
         }
     }
-    if constexpr (WT == WT_BF16) {
+    if constexpr (WT == WT_BF16 || WT == WT_Q8) {
         if (!stepwise && !generic && h->stream_ok && a.B <= 2) {
             const uint32_t ppf = static_cast<uint32_t>(qp::stream::phases_per_frame(m.L));
             if (h->seq > 0xFFFFFFFFu - 2u * ppf) {
@@ -806,8 +806,8 @@ qp_status launch_frame(qp_handle* h, const RunArgs& a, hipStream_t stream, bool 
             Model mm = m;
             qp::stream::Recs rc = h->recs;
             void* args[] = {&mm, &ra, &rc};
-            const void* fn = a.B == 1 ? reinterpret_cast<const void*>(&qp::stream::k_stream<2>)
-                                      : reinterpret_cast<const void*>(&qp::stream::k_stream<4>);
+            const void* fn = a.B == 1 ? reinterpret_cast<const void*>(&qp::stream::k_stream<2, WT>)
+                                      : reinterpret_cast<const void*>(&qp::stream::k_stream<4, WT>);
             if (!check_hip(hipLaunchCooperativeKernel(fn, dim3(qp::stream::kNwg), dim3(qp::stream::kThreadsS), args,
                                                       0, stream),
                            "cooperative launch (dataflow kernel)", &st))
@@ -1039,11 +1039,12 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
         }
     }
 
-    // records of the dataflow kernel (1.7B geometry, bf16 weights, B <= 2)
+    // records of the dataflow kernel (1.7B geometry, bf16, Q8_0 or Q4_0 weights, B <= 2)
     {
         namespace S = qp::stream;
         h->stream_ok = m.dT == S::DT && m.dP == S::DP && m.nq == S::NQ && m.nkv == S::NKV && m.hd == S::HD &&
-                       m.F == S::F && m.V == S::V && wt == WT_BF16 && m.L >= 1 && m.L <= S::kMaxL;
+                       m.F == S::F && m.V == S::V && (wt == WT_BF16 || wt == WT_Q8 || wt == WT_Q4) && m.L >= 1 &&
+                       m.L <= S::kMaxL;
         if (h->stream_ok) {
             constexpr int MR = 4;
             const size_t nrec = static_cast<size_t>(MR) * (S::DP + S::NQKV + S::QD + S::F) + 2ull * S::kNwg * 2;

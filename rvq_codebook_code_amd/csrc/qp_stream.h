@@ -1,5 +1,6 @@
 // Dataflow frame kernel for small batches (B <= 2) of the 1.7B-shaped
-// predictor with bf16 weights.
+// predictor with bf16 weights, or Q8_0 / Q4_0 weights held as int8 codes
+// with fp32 block scales.
 //
 // One persistent workgroup of four waves per CU (256) and no grid barrier:
 //  * every value that crosses workgroups is published as a 64-bit record
@@ -93,16 +94,45 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
     const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
     return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
+__device__ __forceinline__ const float* uniform_f(const float* p) {
+    return static_cast<const float*>(uniform_ptr(p));
+}
 __device__ __forceinline__ rsrc_t wrsrc(const void* p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0), static_cast<int>(bytes),
                                              0x00020000);
 }
-// 8 bf16 weights of row `row` (K wide) at k = kc*512 + lane*8
-__device__ __forceinline__ uint4 ldw(rsrc_t r, int row, int K, int kc, uint32_t lane16) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, lane16 + static_cast<uint32_t>(kc) * 1024u,
-                                                         static_cast<uint32_t>(row) * static_cast<uint32_t>(K) * 2u, 0);
-    return make_uint4(static_cast<uint32_t>(v[0]), static_cast<uint32_t>(v[1]), static_cast<uint32_t>(v[2]),
-                      static_cast<uint32_t>(v[3]));
+// A weight matrix as buffer resources: the values (bf16, or int8 codes) and,
+// for the block formats, the fp32 scales [N][K/32].
+struct WSrc {
+    rsrc_t w, s;
+};
+template <int WT>
+__device__ __forceinline__ WSrc wsrc(const void* w, const float* scale, int N, int K) {
+    if constexpr (WT == WT_BF16) {
+        const rsrc_t r = wrsrc(w, N * K * 2);
+        return {r, r};
+    } else {
+        return {wrsrc(w, N * K), wrsrc(scale, N * (K / 32) * 4)};
+    }
+}
+// The 8 weights of row `row` (K wide) at k = kc*512 + lane*8: bf16, or for
+// the block formats 8 int8 codes (x, y) and their block's scale (z bits).
+template <int WT>
+__device__ __forceinline__ uint4 ldw(const WSrc& r, int row, int K, int kc, uint32_t lane16) {
+    if constexpr (WT == WT_BF16) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r.w, lane16 + static_cast<uint32_t>(kc) * 1024u,
+                                                             static_cast<uint32_t>(row) * static_cast<uint32_t>(K) * 2u, 0);
+        return make_uint4(static_cast<uint32_t>(v[0]), static_cast<uint32_t>(v[1]), static_cast<uint32_t>(v[2]),
+                          static_cast<uint32_t>(v[3]));
+    } else {
+        const uint32_t lane = lane16 >> 4;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r.w, lane * 8u + static_cast<uint32_t>(kc) * 512u,
+                                                            static_cast<uint32_t>(row) * static_cast<uint32_t>(K), 0);
+        const uint32_t sc = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(
+            r.s, ((lane >> 2) + static_cast<uint32_t>(kc) * 16u) * 4u,
+            static_cast<uint32_t>(row) * static_cast<uint32_t>(K / 32) * 4u, 0));
+        return make_uint4(static_cast<uint32_t>(v[0]), static_cast<uint32_t>(v[1]), sc, 0u);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -237,6 +267,28 @@ __device__ __forceinline__ float dot8p(const uint4 w, const bf16x2_t p[4], float
     return acc;
 }
 
+// acc + w . x over 8 weights: bf16 weights against the activations' bf16
+// pairs (p), or int8 codes (exact in fp32) against the fp32 activations (x),
+// the block's sum times its scale
+template <int WT>
+__device__ __forceinline__ float wdot8(const uint4 w, const float x[8], const bf16x2_t p[4], float acc) {
+    if constexpr (WT == WT_BF16) {
+        return dot8p(w, p, acc);
+    } else {
+        const uint32_t c[2] = {w.x, w.y};
+        float blk = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            blk = fmaf(static_cast<float>(static_cast<int8_t>((c[i >> 2] >> (8 * (i & 3))) & 0xFFu)), x[i], blk);
+        return fmaf(__uint_as_float(w.z), blk, acc);
+    }
+}
+// the activations' bf16 pairs, needed by the bf16 products only
+template <int WT>
+__device__ __forceinline__ void pack8w(const float a[8], bf16x2_t p[4]) {
+    if constexpr (WT == WT_BF16) pack8(a, p);
+}
+
 __device__ __forceinline__ void lds8(const float* p, float a[8]) {
     const float4 u = *reinterpret_cast<const float4*>(p);
     const float4 v = *reinterpret_cast<const float4*>(p + 4);
@@ -260,7 +312,7 @@ constexpr int kMaxL = 5;  // layers whose norm gains fit the LDS table
 // q_norm[l], k_norm[l] (HD each)
 constexpr int kGainFloats = (2 * kMaxL + 1) * DP + 2 * kMaxL * HD;
 
-template <int MR>
+template <int MR, int WT>
 __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs rc) {
     constexpr int BM = MR / 2;  // requests
     constexpr int SLOT = slot_floats(MR);
@@ -310,44 +362,44 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
     const uint32_t lane16 = static_cast<uint32_t>(lane) * 16u;
     uint4 wP[4], wQ[8], wO[4], wU[12], wD[6], wL[4];
     auto load_wQ = [&](int l) {
-        const rsrc_t W = wrsrc(uniform_ptr(LD[l].qkv.w), NQKV * DP * 2);
+        const WSrc W = wsrc<WT>(uniform_ptr(LD[l].qkv.w), uniform_f(LD[l].qkv.scale), NQKV, DP);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int c = 0; c < 2; ++c) wQ[q * 2 + c] = ldw(W, 16 * wg + 4 * wave + q, DP, c, lane16);
+            for (int c = 0; c < 2; ++c) wQ[q * 2 + c] = ldw<WT>(W, 16 * wg + 4 * wave + q, DP, c, lane16);
     };
     auto load_wO = [&](int l) {
-        const rsrc_t W = wrsrc(uniform_ptr(LD[l].o.w), DP * QD * 2);
+        const WSrc W = wsrc<WT>(uniform_ptr(LD[l].o.w), uniform_f(LD[l].o.scale), DP, QD);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) wO[c] = ldw(W, 4 * wg + wave, QD, c, lane16);
+        for (int c = 0; c < 4; ++c) wO[c] = ldw<WT>(W, 4 * wg + wave, QD, c, lane16);
     };
     auto load_wU = [&](int l) {
-        const rsrc_t Wg = wrsrc(uniform_ptr(LD[l].gate.w), F * DP * 2);
-        const rsrc_t Wu = wrsrc(uniform_ptr(LD[l].up.w), F * DP * 2);
+        const WSrc Wg = wsrc<WT>(uniform_ptr(LD[l].gate.w), uniform_f(LD[l].gate.scale), F, DP);
+        const WSrc Wu = wsrc<WT>(uniform_ptr(LD[l].up.w), uniform_f(LD[l].up.scale), F, DP);
 #pragma unroll
         for (int q = 0; q < 3; ++q)
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
-                wU[q * 2 + c] = ldw(Wg, 12 * wg + 3 * wave + q, DP, c, lane16);
-                wU[6 + q * 2 + c] = ldw(Wu, 12 * wg + 3 * wave + q, DP, c, lane16);
+                wU[q * 2 + c] = ldw<WT>(Wg, 12 * wg + 3 * wave + q, DP, c, lane16);
+                wU[6 + q * 2 + c] = ldw<WT>(Wu, 12 * wg + 3 * wave + q, DP, c, lane16);
             }
     };
     auto load_wD = [&](int l) {
-        const rsrc_t W = wrsrc(uniform_ptr(LD[l].down.w), DP * F * 2);
+        const WSrc W = wsrc<WT>(uniform_ptr(LD[l].down.w), uniform_f(LD[l].down.scale), DP, F);
 #pragma unroll
-        for (int c = 0; c < 6; ++c) wD[c] = ldw(W, 4 * wg + wave, F, c, lane16);
+        for (int c = 0; c < 6; ++c) wD[c] = ldw<WT>(W, 4 * wg + wave, F, c, lane16);
     };
     auto load_wL = [&](int s) {
-        const rsrc_t W = wrsrc(m.lm[s - 1].w, V * DP * 2);
+        const WSrc W = wsrc<WT>(m.lm[s - 1].w, m.lm[s - 1].scale, V, DP);
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
-            for (int c = 0; c < 2; ++c) wL[q * 2 + c] = ldw(W, 8 * wg + 2 * wave + q, DP, c, lane16);
+            for (int c = 0; c < 2; ++c) wL[q * 2 + c] = ldw<WT>(W, 8 * wg + 2 * wave + q, DP, c, lane16);
     };
     {
-        const rsrc_t W = wrsrc(m.proj.w, DP * DT * 2);
+        const WSrc W = wsrc<WT>(m.proj.w, m.proj.scale, DP, DT);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) wP[c] = ldw(W, 4 * wg + wave, DT, c, lane16);
+        for (int c = 0; c < 4; ++c) wP[c] = ldw<WT>(W, 4 * wg + wave, DT, c, lane16);
     }
     load_wQ(0);
     sched_fence();
@@ -428,8 +480,8 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                     float x8[8];
                     lds8(Hs + r * DT + c * 512 + lane * 8, x8);
                     bf16x2_t p8[4];
-                    pack8(x8, p8);
-                    acc = dot8p(wP[c], p8, acc);
+                    pack8w<WT>(x8, p8);
+                    acc = wdot8<WT>(wP[c], x8, p8, acc);
                 }
                 const float v = wave_sum(acc) + bias;
                 if (lane == 0) st_rec(rc.X + static_cast<size_t>(r) * DP + n, v, tag_of(0));
@@ -490,9 +542,9 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                         float x8[8];
                         act8(xs + r * DP, ga, c, x8);
                         bf16x2_t p8[4];
-                        pack8(x8, p8);
+                        pack8w<WT>(x8, p8);
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) acc[q] = dot8p(wQ[q * 2 + c], p8, acc[q]);
+                        for (int q = 0; q < 4; ++q) acc[q] = wdot8<WT>(wQ[q * 2 + c], x8, p8, acc[q]);
                     }
                     const float rinv = __builtin_amdgcn_rsqf(row_ss(par, r) / static_cast<float>(DP) + eps);
                     wave_sums(acc);
@@ -647,8 +699,8 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                         float x8[8];
                         lds8(as + r * QD + c * 512 + lane * 8, x8);
                         bf16x2_t p8[4];
-                        pack8(x8, p8);
-                        acc = dot8p(wO[c], p8, acc);
+                        pack8w<WT>(x8, p8);
+                        acc = wdot8<WT>(wO[c], x8, p8, acc);
                     }
                     const float d = wave_sum(acc);
                     float nv = 0.f;
@@ -676,11 +728,11 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                         float x8[8];
                         act8(xs + r * DP, gf, c, x8);
                         bf16x2_t p8[4];
-                        pack8(x8, p8);
+                        pack8w<WT>(x8, p8);
 #pragma unroll
                         for (int q = 0; q < 3; ++q) {
-                            ag[q] = dot8p(wU[q * 2 + c], p8, ag[q]);
-                            au[q] = dot8p(wU[6 + q * 2 + c], p8, au[q]);
+                            ag[q] = wdot8<WT>(wU[q * 2 + c], x8, p8, ag[q]);
+                            au[q] = wdot8<WT>(wU[6 + q * 2 + c], x8, p8, au[q]);
                         }
                     }
                     const float rinv = __builtin_amdgcn_rsqf(row_ss(par, r) / static_cast<float>(DP) + eps);
@@ -716,8 +768,8 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                         float x8[8];
                         lds8(hs + r * F + c * 512 + lane * 8, x8);
                         bf16x2_t p8[4];
-                        pack8(x8, p8);
-                        acc = dot8p(wD[c], p8, acc);
+                        pack8w<WT>(x8, p8);
+                        acc = wdot8<WT>(wD[c], x8, p8, acc);
                     }
                     const float d = wave_sum(acc);
                     float nv = 0.f;
@@ -756,9 +808,9 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                         float x8[8];
                         act8(xs + b * DP, g_out, c, x8);
                         bf16x2_t p8[4];
-                        pack8(x8, p8);
-                        acc0 = dot8p(wL[c], p8, acc0);
-                        acc1 = dot8p(wL[2 + c], p8, acc1);
+                        pack8w<WT>(x8, p8);
+                        acc0 = wdot8<WT>(wL[c], x8, p8, acc0);
+                        acc1 = wdot8<WT>(wL[2 + c], x8, p8, acc1);
                     }
                     const float rinv = __builtin_amdgcn_rsqf(row_ss(par, b) / static_cast<float>(DP) + eps);
                     float lg[2] = {acc0, acc1};

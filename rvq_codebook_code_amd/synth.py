@@ -127,6 +127,10 @@ WORKLOADS: Dict[str, Workload] = {
         "q4_b16", Geometry(**_PRED_17B, weight_dtype="q4_0", emb_format="bf16"),
         batch=16, frames=64, weight_seed=1006, input_seed=2006,
         description="1.7B-shaped predictor, Q4_0 linears, bf16 tables, B=16 x 64 frames"),
+    "q4_b1": Workload(
+        "q4_b1", Geometry(**_PRED_17B, weight_dtype="q4_0", emb_format="bf16"),
+        batch=1, frames=256, weight_seed=1006, input_seed=2007,
+        description="1.7B-shaped predictor, Q4_0 linears, bf16 tables, B=1 x 256 frames"),
 }
 
 

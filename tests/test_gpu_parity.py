@@ -199,19 +199,22 @@ def test_full_size_sampled(name, frames, rows):
 # the small-batch dataflow kernel (1.7B geometry, bf16, B <= 2)
 # ----------------------------------------------------------------------------
 
+@pytest.mark.parametrize("name", ["b16", "q8ema", "q4_b16"])
 @pytest.mark.parametrize("B", [1, 2])
-def test_dataflow_kernel_against_oracle_and_generic(B):
-    wl, W, model, pred = workload("b16")
+def test_dataflow_kernel_against_oracle_and_generic(B, name):
+    """bf16 weights, and Q8_0 / Q4_0 codes with their block scales (Q8_0
+    with the EMA codebook tables)."""
+    wl, W, model, pred = workload(name)
     H, q0 = synth.make_inputs(wl.geom, B, 3, 4242 + B)
     rows = np.arange(B)
     for f in range(3):
-        ref, got = check_against_oracle(f"dataflow B={B}", model, pred, H[f], q0[f], rows)
+        ref, got = check_against_oracle(f"dataflow {name} B={B}", model, pred, H[f], q0[f], rows)
         force = ref["tokens"].astype(np.int32)
         # the dataflow kernel rounds its product operands to bf16 (the generic
         # path keeps them fp32): the two agree to the bf16-weight bar
         gen = gpu_frame(pred, H[f], q0[f], force=force, generic=True)
         lg = np.abs(gen["logits"] - got["logits"]).max()
-        print(f"[dataflow B={B} vs generic] logits max-abs {lg:.3g}")
+        print(f"[dataflow {name} B={B} vs generic] logits max-abs {lg:.3g}")
         assert lg <= TOL["bf16"]
         assert np.abs(gen["embsum"] - got["embsum"]).max() <= 1e-5
 
@@ -362,10 +365,10 @@ def test_q4_generic_path_and_full_size():
 
 @pytest.mark.parametrize("name", ["tiny_q8ema", "tiny_q4"])
 def test_small_batches_with_block_formats_take_the_batched_path(name):
-    """B <= 2 with Q8_0 or Q4_0 weights runs on the batched matrix-core path
-    by default (the dataflow kernel takes bf16 weights only), not on the
-    generic fp32 kernel: the default call equals an explicitly batched one
-    bit for bit, and the oracle within tolerance."""
+    """B <= 2 with Q8_0 or Q4_0 weights on a geometry the dataflow kernel does
+    not take (it is built for the 1.7B one) runs on the batched matrix-core
+    path by default, not on the generic fp32 kernel: the default call equals
+    an explicitly batched one bit for bit, and the oracle within tolerance."""
     wl, W, model, pred = workload(name)
     H, q0 = synth.make_inputs(wl.geom, 2, 1, 9100)
     for B in (1, 2):
