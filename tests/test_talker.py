@@ -189,27 +189,29 @@ def test_talker_steps_against_oracle(name):
 
 @pytest.mark.gpu
 def test_talker_flags_and_cache_untouched():
-    """A row with a position past max_len or an unknown slot raises its flag
-    and writes nothing: a later valid step still matches the oracle."""
+    """A row with a position beyond the attention grid that max_len sizes
+    (chunks of at least 64 positions), past max_ctx, negative, or an unknown
+    slot raises its flag and writes nothing: a later valid step still
+    matches the oracle."""
     torch, dev = _torch_dev()
     from rvq_codebook_code_amd import binding as bd
     wl = synth.TALKER_WORKLOADS["talker_tiny"]
     g = wl.geom
     W = synth.make_talker_weights(g, wl.weight_seed)
     model = TK.TalkerOracle(W, g)
-    tk = bd.Talker(W, g, max_batch=4, n_slots=4, max_ctx=64)
+    tk = bd.Talker(W, g, max_batch=4, n_slots=4, max_ctx=200)
     K, V = synth.make_talker_history(g, 20, 77)
     tk.load_history(2, _bits_to_dev(torch, dev, K), _bits_to_dev(torch, dev, V))
     x = torch.from_numpy(synth.make_talker_inputs(g, 1, 1, 5)[0]).to(dev)
     H = torch.zeros((1, g.d_model), device=dev)
     q0 = torch.zeros((1,), dtype=torch.int32, device=dev)
-    for slot, pos, bit in [(2, 40, 1), (9, 20, 2), (-1, 20, 2), (2, -3, 1)]:
+    for slot, pos, bit in [(2, 100, 1), (2, 200, 1), (9, 20, 2), (-1, 20, 2), (2, -3, 1)]:
         tk.step(x, torch.tensor([slot], dtype=torch.int32, device=dev), torch.tensor([pos], dtype=torch.int32, device=dev),
                 21, H, q0)
         assert tk.get_error() & bit
     with pytest.raises(bd.QpError):
         tk.step(x, torch.tensor([2], dtype=torch.int32, device=dev), torch.tensor([20], dtype=torch.int32, device=dev),
-                65, H, q0)
+                201, H, q0)
     X = synth.make_talker_inputs(g, 1, 2, 6)
     _run_and_compare("talker_tiny after flags", model, tk, g, [2], [(K, V)], X)
     tk.close()
