@@ -914,7 +914,7 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
 
     Uploader up{&h->allocs};
     const int wt = h->q4 ? WT_Q4 : m.wt;   // storage format of the host weights
-    // batched matrix-core path: bf16 or Q8_0 weights whose widths tile into
+    // batched matrix-core path: bf16, Q8_0 or Q4_0 weights whose widths tile into
     // 32 x 256 blocks (every K split four ways into whole 32-wide blocks,
     // two at a time; every N a whole number of 32-column tiles)
     h->tiled_ok = (wt == WT_BF16 || wt == WT_Q8 || wt == WT_Q4) && m.dT % 256 == 0 && m.dP % 256 == 0 && m.dP <= 4096 && m.dT <= 4096 &&

@@ -62,9 +62,10 @@ struct qp_talker {
 
 namespace {
 
-// 64 positions per attention split at the least (a B = 1 step: 1.26 ms
-// against 1.32 with 32-position chunks; 128 and 256 were slower)
-constexpr int kTalkerMinCh = 64;
+// 64 positions per attention split (a B = 1 step over 1,024 positions of
+// history: 1.27 ms against 1.32 with 32-position chunks; 128 and 256 were
+// slower)
+constexpr int kTalkerCh = qp::talker::kMaxCh;
 
 qp_status validate_talker(const qp_talker_geometry* g) {
     if (g->d_model <= 0 || g->n_layers < 0 || g->n_q_heads <= 0 || g->n_kv_heads <= 0 || g->head_dim <= 0 ||
@@ -84,15 +85,11 @@ qp_status validate_talker(const qp_talker_geometry* g) {
     return QP_OK;
 }
 
-// attention split of a step: the smallest chunk (at least 64 positions) that
-// keeps the grid near 2048 workgroups, and the number of chunks rounded up to
+// attention split of a step: 64-position chunks, their number rounded up to
 // a power of two (chunks past a request's history exit at once), so that a
 // growing history changes the launch shape only when it doubles
-void talker_split(const qp_talker* t, int B, int max_len, int* ch_out, int* nsplit_out) {
-    int ch = kTalkerMinCh;
-    while (ch < qp::talker::kMaxCh &&
-           static_cast<long long>(B) * t->g.n_kv_heads * ((max_len + ch - 1) / ch) > 2048)
-        ch *= 2;
+void talker_split(int max_len, int* ch_out, int* nsplit_out) {
+    const int ch = kTalkerCh;
     int ns = 1;
     while (ns * ch < max_len) ns *= 2;
     *ch_out = ch;
@@ -359,7 +356,7 @@ qp_status qp_talker_create(const qp_talker_weights* w, const qp_talker_geometry*
     t->hb = static_cast<uint16_t*>(up.alloc(mb * F * 2));
     t->keys = static_cast<unsigned long long*>(up.alloc(mb * (g->vocab / 16) * 8));
     t->max_split = 1;   // split counts are powers of two
-    while (t->max_split * kTalkerMinCh < g->max_ctx) t->max_split *= 2;
+    while (t->max_split * kTalkerCh < g->max_ctx) t->max_split *= 2;
     t->apart = static_cast<float*>(up.alloc(mb * g->n_q_heads * t->max_split * (hd + 2) * 4));
     t->actr = static_cast<unsigned*>(up.alloc(mb * g->n_kv_heads * 4));
     t->t_part_floats = 512ull * 4 * 2 * 256;
@@ -419,7 +416,7 @@ qp_status qp_talker_step(qp_talker* t, int32_t B, const float* x, const int32_t*
     DeviceGuard guard(t->device);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     int ch = 0, ns = 0;
-    talker_split(t, B, max_len, &ch, &ns);
+    talker_split(max_len, &ch, &ns);
     if (logits_out) {
         switch (t->wt) {
             case WT_BF16: return talker_launch<WT_BF16>(t, B, x, slots, pos, ch, ns, H_out, q0_out, logits_out, s);

@@ -1,4 +1,4 @@
-// Batched frame driver (any B; bf16 or Q8_0 weights): one kernel per phase,
+// Batched frame driver (any B; bf16, Q8_0 or Q4_0 weights): one kernel per phase,
 // every projection on the matrix cores.
 //
 // The predictor step is the same as in the other drivers (Qwen3 decoder
@@ -29,9 +29,11 @@
 //    block's partial sum before accumulation.  The weights therefore enter
 //    the product exactly.  Q4_0 fragments hold a lane's 8 codes in one
 //    32-bit word (256 B per fragment).
-//  * A workgroup (4 waves) owns a tile of 16*RT rows x 32 output columns
-//    (2 fragments wide; for SwiGLU the gate and up fragments of the same 16
-//    columns).  The 4 waves split K and their partial tiles are summed through
+//  * A workgroup of NW waves owns a tile of 16*RT rows x 16*CT output
+//    columns (for SwiGLU the gate and up fragments of the same 16 columns).
+//    RT = 1 (up to 64 rows) takes CT = 1 (SwiGLU: its pair) and NW = 8 where
+//    K holds 16 pairs of 32-wide blocks, else 4; RT = 2 takes CT = 2 and
+//    NW = 4.  The NW waves split K and their partial tiles are summed through
 //    LDS in wave order.  Small-N products also split K across KS workgroups:
 //    every workgroup writes its partial tile, and the last to arrive (a
 //    counter per tile) sums the KS partials in order and runs the epilogue,
