@@ -481,33 +481,32 @@ namespace {
 
 // Launches one product; returns the number of column tiles (gridDim.x).
 // h: any handle with the split-K scratch (t_part, t_part_floats, t_ctr, t_nctr).
-// split_rt1: also split K for a single row tile (large products; for the
-// predictor's shapes the fixup cost more than it saved).
 template <int WT, int SRC, int EPI, class Handle>
-int tiled_gemm(const Handle* h, qp::tiled::GemmArgs g, hipStream_t stream, bool split_rt1 = false) {
+int tiled_gemm(const Handle* h, qp::tiled::GemmArgs g, hipStream_t stream) {
     namespace T = qp::tiled;
     // one 16-row tile per workgroup up to 64 rows (more workgroups per CU to
     // cover memory latency; the weights are re-read from L2 per row tile),
     // two above (measured: B = 64 Q8_0 +27 %, B = 128 bf16 +11 % over tiles
-    // of up to 64 rows)
-    const int RT = g.M <= 64 ? 1 : 2;
+    // of up to 64 rows).  Residual products (N = dP) keep one row tile at any
+    // M: with two they need the split-K fixup to fill the chip, and its extra
+    // round trips cost more (B = 128 bf16: 4.15 against 4.29 ms per
+    // frame-batch; one row tile for the other products was slower)
+    const int RT = (g.M <= 64 || EPI == T::EPI_RESID) ? 1 : 2;
     // one row tile: one 16-column fragment per workgroup (twice the
     // workgroups streaming weights); SwiGLU always pairs gate and up
     const int CT = (RT == 1 && EPI != T::EPI_SWIGLU) ? 1 : 2;
     const int gx = EPI == T::EPI_SWIGLU ? g.N / 16 : g.N / (16 * CT);
     const int gy = (g.M + 16 * RT - 1) / (16 * RT);
-    // Products with few output tiles (the N = dP ones) and more than one row
-    // tile also split K over workgroups: the smallest split (into whole pairs
-    // of 32-wide blocks per wave, at most 4) that fills 256 workgroups.  With
-    // a single row tile the ordered fixup costs more than it saves.
+    // The projection of H (N = dP, few output tiles) with more than one row
+    // tile also splits K over workgroups: the smallest split (into whole
+    // pairs of 32-wide blocks per wave, at most 4) that fills 256 workgroups.
+    // With a single row tile the ordered fixup costs more than it saves.
     const int tiles = gx * gy;
     int KS = 1;
-    if ((EPI == T::EPI_RESID || EPI == T::EPI_BIAS) && (RT > 1 || split_rt1) && tiles < 256 &&
-        static_cast<size_t>(tiles) <= h->t_nctr) {
+    if (EPI == T::EPI_BIAS && RT > 1 && tiles < 256 && static_cast<size_t>(tiles) <= h->t_nctr) {
         for (int c = 2; c <= T::kMaxKS; ++c) {
-            // whole pairs of 32-wide blocks per wave: 4 waves (RT > 1) need
-            // K / 256 divisible by c, 8 waves (RT = 1) by 2c
-            if ((g.K / 256) % (RT == 1 ? 2 * c : c) != 0) continue;
+            // whole pairs of 32-wide blocks for each of the 4 waves
+            if ((g.K / 256) % c != 0) continue;
             if (static_cast<size_t>(c) * tiles * RT * CT * 256 > h->t_part_floats) break;
             KS = c;
             if (c * tiles >= 256) break;
@@ -1022,7 +1021,7 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
         // of up to 4 row fragments x 2 column fragments suffice
         h->t_part_floats = 512ull * 4 * 2 * 256;
         h->t_part = static_cast<float*>(up.alloc(h->t_part_floats * 4));
-        h->t_nctr = 256;  // split K only applies below 256 tiles
+        h->t_nctr = 256;  // split K (the projection of H) only applies below 256 tiles
         h->t_ctr = static_cast<unsigned*>(up.alloc(h->t_nctr * 4));
         h->t_xg = static_cast<uint16_t*>(up.alloc(rows * m.dP * 2));
         h->st_H = static_cast<float*>(up.alloc(static_cast<size_t>(m.max_batch) * m.dT * 4));

@@ -35,7 +35,9 @@ struct qp_talker {
     float* apart = nullptr;           // attention partials [max_batch][nq][max_split][hd+2]
     int max_split = 0;
     unsigned* actr = nullptr;         // [max_batch][nkv]
-    float* t_part = nullptr;          // split-K partial tiles of the products
+    // split-K scratch of the products: none (the Talker has no projection
+    // of H, the one product that splits K), so t_nctr = 0 keeps KS = 1
+    float* t_part = nullptr;
     size_t t_part_floats = 0;
     unsigned* t_ctr = nullptr;
     size_t t_nctr = 0;
@@ -359,10 +361,6 @@ qp_status qp_talker_create(const qp_talker_weights* w, const qp_talker_geometry*
     while (t->max_split * kTalkerCh < g->max_ctx) t->max_split *= 2;
     t->apart = static_cast<float*>(up.alloc(mb * g->n_q_heads * t->max_split * (hd + 2) * 4));
     t->actr = static_cast<unsigned*>(up.alloc(mb * g->n_kv_heads * 4));
-    t->t_part_floats = 512ull * 4 * 2 * 256;
-    t->t_part = static_cast<float*>(up.alloc(t->t_part_floats * 4));
-    t->t_nctr = 256;
-    t->t_ctr = static_cast<unsigned*>(up.alloc(t->t_nctr * 4));
     t->err = static_cast<unsigned*>(up.alloc(256));
     t->st_x = static_cast<float*>(up.alloc(mb * d * 4));
     t->st_slots = static_cast<int*>(up.alloc(mb * 4));
@@ -372,7 +370,6 @@ qp_status qp_talker_create(const qp_talker_weights* w, const qp_talker_geometry*
     if (up.st == QP_OK) {
         // counters start (and are left) at zero; the cache starts cleared
         if (!check_hip(hipMemset(t->actr, 0, mb * g->n_kv_heads * 4), "hipMemset", &st) ||
-            !check_hip(hipMemset(t->t_ctr, 0, t->t_nctr * 4), "hipMemset", &st) ||
             !check_hip(hipMemset(t->err, 0, 256), "hipMemset", &st) ||
             !check_hip(hipMemset(t->kc, 0, kvn * 2), "hipMemset", &st) ||
             !check_hip(hipMemset(t->vc, 0, kvn * 2), "hipMemset", &st) ||

@@ -34,7 +34,8 @@
 //    RT = 1 (up to 64 rows) takes CT = 1 (SwiGLU: its pair) and NW = 8 where
 //    K holds 16 pairs of 32-wide blocks, else 4; RT = 2 takes CT = 2 and
 //    NW = 4.  The NW waves split K and their partial tiles are summed through
-//    LDS in wave order.  Small-N products also split K across KS workgroups:
+//    LDS in wave order.  The projection of H (small N) with two row
+//    fragments also splits K across KS workgroups:
 //    every workgroup writes its partial tile, and the last to arrive (a
 //    counter per tile) sums the KS partials in order and runs the epilogue,
 //    so results do not depend on timing.

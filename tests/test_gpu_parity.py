@@ -233,7 +233,7 @@ def test_dataflow_kernel_taps_and_repeat():
 
 
 # ----------------------------------------------------------------------------
-# the batched matrix-core path (bf16 / Q8_0 weights, any B)
+# the batched matrix-core path (bf16 / Q8_0 / Q4_0 weights, any B)
 # ----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("name", ["tiny_bf16", "tiny_q8ema", "tiny_q4"])
@@ -251,6 +251,21 @@ def test_tiled_batch_sizes(B):
     wl, W, model, pred = workload("tiny_bf16")
     H, q0 = synth.make_inputs(wl.geom, B, 1, 3100 + B)
     check_against_oracle(f"tiled B={B}", model, pred, H[0], q0[0], np.arange(B), tiled=True)
+
+
+@pytest.mark.parametrize("name", ["tiny_bf16", "tiny_q8ema", "tiny_q4"])
+@pytest.mark.parametrize("B", [65, 100, 160])
+def test_tiled_large_batches(name, B):
+    """Above 64 rows: tiles of two 16-row fragments with ragged tails for
+    q/k/v, gate/up and lm_head, one-fragment tiles for the residual products,
+    split-K for the projection; every row against the oracle."""
+    wl, W, model, _ = workload(name)
+    key = name + "_large"
+    if key not in _cache:
+        _cache[key] = bd.Predictor(W, wl.geom, max_batch=160)
+    pred = _cache[key]
+    H, q0 = synth.make_inputs(wl.geom, B, 1, 3200 + B)
+    check_against_oracle(f"tiled {name} B={B}", model, pred, H[0], q0[0], np.arange(B), tiled=True)
 
 
 def test_tiled_taps_composition_and_repeat():
