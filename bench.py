@@ -34,16 +34,23 @@ def bytes_per_weight(dtype: str) -> float:
     return {"f32": 4.0, "bf16": 2.0, "q8_0": 34.0 / 32.0, "q4_0": 18.0 / 32.0}[dtype]
 
 
-def algorithmic_bytes(g: synth.Geometry) -> int:
+def algorithmic_bytes(g: synth.Geometry, B: int = 1, qkv0_table: bool = False) -> int:
     """Weights the method must stream per frame-batch: every layer matrix and
     one lm_head per step (15 steps), plus the projection once per frame.  The
-    gathered embedding rows (B*16 rows) are left out: a lower bound."""
+    gathered embedding rows (B*16 rows) are left out: a lower bound.
+
+    qkv0_table: the driver reads layer 0's q/k/v rows of steps 2..15 from the
+    create-time table (B fp32 rows per step) instead of streaming layer 0's
+    q/k/v weights, so those weights count once, not 15 times."""
     qd = g.n_q_heads * g.head_dim
     nqkv = (g.n_q_heads + 2 * g.n_kv_heads) * g.head_dim
     per_layer = nqkv * g.d_model + g.d_model * qd + 2 * g.d_ffn * g.d_model + g.d_model * g.d_ffn
     per_step = g.n_layers * per_layer + g.vocab * g.d_model
     bpw = bytes_per_weight(g.weight_dtype)
-    return int(round(15 * per_step * bpw + g.d_model * g.d_talker * bpw))
+    total = 15 * per_step * bpw + g.d_model * g.d_talker * bpw
+    if qkv0_table:
+        total += 14 * (B * nqkv * 4 - nqkv * g.d_model * bpw)
+    return int(round(total))
 
 
 def algorithmic_flops(g: synth.Geometry, B: int) -> int:
@@ -327,7 +334,7 @@ def main():
     frames_per_s = B * args.steps / (ms / 1e3)
 
     driver = select_driver(g, B, args)
-    nbytes = algorithmic_bytes(g)
+    nbytes = algorithmic_bytes(g, B, qkv0_table=driver == "dataflow")
     nflops = algorithmic_flops(g, B)
     if B >= 128:
         # throughput batch: graded against the bf16 matrix-core peak

@@ -147,7 +147,11 @@ typedef struct qp_handle qp_handle;
  * failure returned as status), allocates every device buffer the later calls
  * need for up to max_batch requests (later calls never allocate), copies and
  * repacks the weights, computes EMA tables and the per-codebook projected
- * tables W_p . E_j + b_p.  On failure *out is NULL and nothing is leaked. */
+ * tables W_p . E_j + b_p.  For the 1.7B geometry with bf16, Q8_0 or Q4_0
+ * weights (the small-batch dataflow driver) it also computes layer 0's q/k/v
+ * rows of every projected-table row of codebooks 1..14 (fp32, 14 x V x
+ * (nq + 2 nkv) hd values, 470 MB), which that driver reads from step 2 on.
+ * On failure *out is NULL and nothing is leaked. */
 qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device,
                     qp_handle** out);
 

@@ -176,6 +176,51 @@ __global__ __launch_bounds__(256) void k_ptab(Model m, float* P) {
     }
 }
 
+// Layer 0's q/k/v rows for every row of the projected tables P_1 .. P_14:
+//   Q0[j-1][v][n] = rsqrt(mean_k P_j[v][k]^2 + eps) * sum_k W_qkv[n][k] g[k] P_j[v][k]
+// with g = layer 0's attn_norm (the fused q/k/v projection of the RMSNorm of
+// the row; fp32, 64x64 output tiles as in k_ptab).  From step 2 on a
+// position's layer-0 input is such a row, chosen by the previous token.
+__global__ __launch_bounds__(256) void k_qkv0(Model m, const float* g, float* Q0) {
+    __shared__ float As[32][65];  // [k][v]
+    __shared__ float Bs[32][65];  // [k][n]
+    const int j = blockIdx.z + 1;
+    const int v0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    const Mat w = m.layers[0].qkv;
+    const float* P = m.ptab + static_cast<size_t>(j) * m.V * m.dP;
+    float acc[4][4] = {};
+    float ss[4] = {};
+    for (int k0 = 0; k0 < m.dP; k0 += 32) {
+        for (int idx = threadIdx.x; idx < 32 * 64; idx += 256) {
+            const int kk = idx & 31, rr = idx >> 5;
+            const int v = v0 + rr, n = n0 + rr, k = k0 + kk;
+            As[kk][rr] = (v < m.V && k < m.dP) ? P[static_cast<size_t>(v) * m.dP + k] : 0.f;
+            Bs[kk][rr] = (n < m.nqkv && k < m.dP) ? mat_elem(w, m.wt, m.dP, n, k) * g[k] : 0.f;
+        }
+        __syncthreads();
+        for (int kk = 0; kk < 32; ++kk) {
+            float av[4], bv[4];
+            for (int i = 0; i < 4; ++i) av[i] = As[kk][ty * 4 + i];
+            for (int i = 0; i < 4; ++i) bv[i] = Bs[kk][tx * 4 + i];
+            for (int i = 0; i < 4; ++i) {
+                ss[i] = fmaf(av[i], av[i], ss[i]);
+                for (int q = 0; q < 4; ++q) acc[i][q] = fmaf(av[i], bv[q], acc[i][q]);
+            }
+        }
+        __syncthreads();
+    }
+    for (int i = 0; i < 4; ++i) {
+        const int v = v0 + ty * 4 + i;
+        if (v >= m.V) continue;
+        const float rinv = 1.0f / sqrtf(ss[i] / static_cast<float>(m.dP) + m.eps);
+        for (int q = 0; q < 4; ++q) {
+            const int n = n0 + tx * 4 + q;
+            if (n < m.nqkv) Q0[(static_cast<size_t>(j - 1) * m.V + v) * m.nqkv + n] = acc[i][q] * rinv;
+        }
+    }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -1011,6 +1056,7 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
     m.err = static_cast<unsigned*>(up.alloc(256));
     m.bar = static_cast<unsigned long long*>(up.alloc(4096));
     float* ptab = static_cast<float*>(up.alloc(static_cast<size_t>(kSteps) * m.V * m.dP * 4));
+    float* qkv0 = nullptr;
     m.ptab = ptab;
     if (h->tiled_ok) {
         // argmax keys of the lm_head tiles; split-K partial tiles and counters
@@ -1060,6 +1106,9 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
                     up.msg = "hipMemset of the record buffers failed";
                 }
             }
+            // layer 0's q/k/v rows of every table row (k_qkv0, after k_ptab)
+            qkv0 = static_cast<float*>(up.alloc(static_cast<size_t>(kSteps - 1) * m.V * m.nqkv * 4));
+            m.qkv0 = qkv0;
         }
     }
 
@@ -1078,6 +1127,9 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
         return st;
     }
     hipLaunchKernelGGL(k_ptab, dim3((m.dP + 63) / 64, (m.V + 63) / 64, kSteps), dim3(256), 0, 0, m, ptab);
+    if (qkv0)
+        hipLaunchKernelGGL(k_qkv0, dim3((m.nqkv + 63) / 64, (m.V + 63) / 64, kSteps - 1), dim3(256), 0, 0, m,
+                           h->layers_host[0].attn_norm, qkv0);
     if (!check_hip(hipGetLastError(), "projected-table kernel launch", &st) ||
         !check_hip(hipDeviceSynchronize(), "projected-table kernel", &st)) {
         free_all(h);

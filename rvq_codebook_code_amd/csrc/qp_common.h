@@ -51,6 +51,8 @@ struct Model {
     const float* proj_b;
     const void* emb[kCodebooks];   // [V][dT] fp32 or bf16
     const float* ptab;             // [15][V][dP]: W_p . E_j + b_p, j = 0..14
+    const float* qkv0;             // [14][V][nqkv]: layer 0's q/k/v rows of P_j[v], j = 1..14
+                                   // (dataflow kernel only; null elsewhere)
     const LayerDev* layers;        // device array [L]
     const float* out_norm;
     Mat lm[kSteps];

@@ -332,6 +332,9 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
     auto tag_of = [&](int ph) { return seq0 + static_cast<uint32_t>(ph) + 1u; };
     const float eps = m.eps;
     unsigned* err = m.err;
+    // layer 0's q/k/v rows of every table row P_j[v] (j = 1..14), computed at
+    // create time: from step 2 on, layer 0 takes its head vectors from here
+    const float* t0 = m.qkv0;
 
     // ---- tables into LDS: layer pointers, norm gains, RoPE
     if (threadIdx.x < L) lay_s[threadIdx.x] = m.layers[threadIdx.x];
@@ -495,7 +498,24 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
         const int M = (s == 1) ? 2 * B : B;
         for (int l = 0; l < L; ++l) {
             // ================= QKV(l) =================
-            {
+            if (l == 0 && s > 1 && t0) {
+                // the input row is P_{s-1}[fed], whose q/k/v rows are in the
+                // table: decide the tokens and take this wave's residual element
+                decide(s - 1, ph_lm(L, s - 1));
+                if (wave == 3 && eb < B) {
+                    int fb = fed[0];
+#pragma unroll
+                    for (int b = 1; b < BM; ++b)
+                        if (b == eb) fb = fed[b];
+                    es += emb_elem(m, s - 1, fb, ek);
+                }
+#pragma unroll
+                for (int r = 0; r < MR; ++r) xr[r] = 0.f;
+#pragma unroll
+                for (int b = 0; b < BM; ++b)
+                    if (b < B) xr[b] = m.ptab[(static_cast<size_t>(s - 1) * V + fed[b]) * DP + 4 * wg + wave];
+                ++ph;
+            } else {
                 const int par = ph & 1;
                 float* xs = slot[par];
                 if (l == 0) {
@@ -577,10 +597,21 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                     }
                     // new head vectors: wave w takes q 2g, q 2g+1, k g, v g
                     const int col = wave < 2 ? (2 * g + wave) * HD : (wave == 2 ? (NQ + g) * HD : (NQ + NKV + g) * HD);
-                    const uint32_t qt = tag_of(ph - 1);
-                    for (int pi = 0; pi < npos; ++pi)
-                        poll_head(rc.QKV + static_cast<size_t>(pi * B + b) * NQKV + col, qt,
-                                  hist + 4096 + 512 * pi + wave * HD, err);
+                    if (l == 0 && s > 1 && t0) {
+                        // from the table (one position): row P_{s-1}[fed[b]]
+                        int fb = fed[0];
+#pragma unroll
+                        for (int bb = 1; bb < BM; ++bb)
+                            if (bb == b) fb = fed[bb];
+                        const float* trow = t0 + (static_cast<size_t>(s - 2) * V + fb) * NQKV + col;
+                        *reinterpret_cast<float2*>(hist + 4096 + wave * HD + 2 * lane) =
+                            *reinterpret_cast<const float2*>(trow + 2 * lane);
+                    } else {
+                        const uint32_t qt = tag_of(ph - 1);
+                        for (int pi = 0; pi < npos; ++pi)
+                            poll_head(rc.QKV + static_cast<size_t>(pi * B + b) * NQKV + col, qt,
+                                      hist + 4096 + 512 * pi + wave * HD, err);
+                    }
                     __builtin_amdgcn_s_waitcnt(0);
                 }
                 __syncthreads();
@@ -841,7 +872,7 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                 st_rec_u(kr + 1, 0xFFFFFFFFu - static_cast<uint32_t>(best & 0xFFFFFFFFu), tag_of(ph));
             }
             sched_fence();
-            if (s < kSteps) load_wQ(0);
+            if (s < kSteps && !t0) load_wQ(0);
             sched_fence();
             ++ph;
         }
