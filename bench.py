@@ -53,14 +53,25 @@ def algorithmic_bytes(g: synth.Geometry, B: int = 1, qkv0_table: bool = False) -
     return int(round(total))
 
 
-def algorithmic_flops(g: synth.Geometry, B: int) -> int:
+def algorithmic_flops(g: synth.Geometry, B: int, qkv0_table: bool = False) -> int:
     """2 flops per weight per request row (15 steps; the prefill's extra row
-    and attention are left out)."""
+    and attention are left out).  qkv0_table: layer 0's q/k/v product runs at
+    step 1 only (see algorithmic_bytes)."""
     qd = g.n_q_heads * g.head_dim
     nqkv = (g.n_q_heads + 2 * g.n_kv_heads) * g.head_dim
     per_layer = nqkv * g.d_model + g.d_model * qd + 2 * g.d_ffn * g.d_model + g.d_model * g.d_ffn
     per_step = g.n_layers * per_layer + g.vocab * g.d_model
-    return 2 * B * (15 * per_step + g.d_model * g.d_talker)
+    total = 15 * per_step + g.d_model * g.d_talker
+    if qkv0_table:
+        total -= 14 * nqkv * g.d_model
+    return 2 * B * total
+
+
+def has_qkv0_table(g: synth.Geometry) -> bool:
+    """The library builds the layer-0 q/k/v table for the 1.7B geometry with
+    bf16, Q8_0 or Q4_0 weights (the handles the dataflow driver can run)."""
+    return (g.weight_dtype in ("bf16", "q8_0", "q4_0") and 1 <= g.n_layers <= 5 and
+            all(getattr(g, k) == v for k, v in _DATAFLOW_GEOMETRY.items()))
 
 
 TALKER_METRIC = "Talker decode steps/sec (H and q0 per request) at a 1024-position history; % HBM roofline"
@@ -204,8 +215,7 @@ def select_driver(g, B: int, args) -> str:
         return "stepwise"
     if args.generic:
         return "generic"
-    if (B <= 2 and g.weight_dtype in ("bf16", "q8_0", "q4_0") and 1 <= g.n_layers <= 5 and
-            all(getattr(g, k) == v for k, v in _DATAFLOW_GEOMETRY.items())):
+    if B <= 2 and has_qkv0_table(g):
         return "dataflow"
     qd = g.n_q_heads * g.head_dim
     nqkv = (g.n_q_heads + 2 * g.n_kv_heads) * g.head_dim
@@ -334,8 +344,11 @@ def main():
     frames_per_s = B * args.steps / (ms / 1e3)
 
     driver = select_driver(g, B, args)
-    nbytes = algorithmic_bytes(g, B, qkv0_table=driver == "dataflow")
-    nflops = algorithmic_flops(g, B)
+    # the dataflow and batched drivers read layer 0's q/k/v rows of steps
+    # 2..15 from the create-time table
+    table = driver in ("dataflow", "tiled") and has_qkv0_table(g)
+    nbytes = algorithmic_bytes(g, B, qkv0_table=table)
+    nflops = algorithmic_flops(g, B, qkv0_table=table)
     if B >= 128:
         # throughput batch: graded against the bf16 matrix-core peak
         achieved = nflops / (launch_ms / 1e3) / 1e12

@@ -604,6 +604,8 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
     ta.err = m.err;
     ta.emb = m.emb[0];
     ta.ptab = m.ptab;
+    ta.qkv = m.qkv;
+    ta.nqkv = m.nqkv;
     hipLaunchKernelGGL(T::k_start, dim3(nb), dim3(T::kThreadsT), 0, stream, ta);
     T::AttnArgs aa{};
     aa.B = B;
@@ -641,20 +643,23 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
         for (int l = 0; l < m.L; ++l) {
             const LayerDev& L = h->layers_host[l];
             const float* g_after = l + 1 < m.L ? h->layers_host[l + 1].attn_norm : m.out_norm;
-            // q, k, v = W_qkv . RMSNorm(x)
-            g = T::GemmArgs{};
-            g.eps = m.eps;
-            g.M = M;
-            g.a = h->t_xg;
-            g.lda = m.dP;
-            g.ss_in = h->t_ss;
-            g.nss = nss;
-            g.N = m.nqkv;
-            g.K = m.dP;
-            g.w0 = h->t_qkv[l];
-            g.out = m.qkv;
-            g.ldo = m.nqkv;
-            tiled_gemm<WT, T::SRC_BF16_NORM, T::EPI_SCALE>(h, g, stream);
+            // q, k, v = W_qkv . RMSNorm(x); from step 2 on, with the layer-0
+            // table, k_next has already copied layer 0's rows
+            if (l > 0 || s == 1 || !m.qkv0) {
+                g = T::GemmArgs{};
+                g.eps = m.eps;
+                g.M = M;
+                g.a = h->t_xg;
+                g.lda = m.dP;
+                g.ss_in = h->t_ss;
+                g.nss = nss;
+                g.N = m.nqkv;
+                g.K = m.dP;
+                g.w0 = h->t_qkv[l];
+                g.out = m.qkv;
+                g.ldo = m.nqkv;
+                tiled_gemm<WT, T::SRC_BF16_NORM, T::EPI_SCALE>(h, g, stream);
+            }
             // attention
             aa.s = s;
             aa.l = l;
@@ -748,6 +753,7 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
         ta.s = s;
         ta.emb = m.emb[s];
         ta.ptab = s < kSteps ? m.ptab + static_cast<size_t>(s) * m.V * m.dP : nullptr;
+        ta.qkv0 = s < kSteps && m.qkv0 ? m.qkv0 + static_cast<size_t>(s - 1) * m.V * m.nqkv : nullptr;
         hipLaunchKernelGGL(T::k_next, dim3(nb), dim3(T::kThreadsT), 0, stream, ta);
     }
     if (!check_hip(hipGetLastError(), "batched path kernel launch", &st)) return st;

@@ -116,6 +116,12 @@ struct TokArgs {
     float* ss;                        // 16-column sums of x^2 [2B][dP/16]
     const float* gain0;               // attn_norm of layer 0 (out_norm without layers)
     unsigned* err;
+    // layer 0's q/k/v rows of the next position's table rows [V][nqkv], or
+    // null; when set, the fed token's row is copied to qkv [B][nqkv] and the
+    // next step runs no layer-0 q/k/v product
+    const float* qkv0;
+    float* qkv;
+    int nqkv;
 };
 
 struct AttnArgs {
@@ -766,7 +772,8 @@ __global__ __launch_bounds__(kThreadsT) void k_start(TokArgs ta) {
 
 // Step s's token per request from the lm_head tiles' keys; the fed-back
 // token (forced or own) adds E_s[t] to embsum and, before the last step,
-// sets the next position's input row P_s[t].
+// sets the next position's input row P_s[t] (and, with the table, that row's
+// layer-0 q/k/v rows).
 __global__ __launch_bounds__(kThreadsT) void k_next(TokArgs ta) {
     __shared__ unsigned long long red[kThreadsT / 64];
     __shared__ int fed_s;
@@ -802,6 +809,11 @@ __global__ __launch_bounds__(kThreadsT) void k_next(TokArgs ta) {
         const int t = __builtin_amdgcn_readfirstlane(fed_s);
         load_emb(ta, t, e);
         if (ta.ptab) load_vec(ta.ptab + static_cast<size_t>(t) * ta.dP, np, v);
+        if (ta.qkv0) {
+            const float4* src = reinterpret_cast<const float4*>(ta.qkv0 + static_cast<size_t>(t) * ta.nqkv);
+            float4* dst = reinterpret_cast<float4*>(ta.qkv + static_cast<size_t>(b) * ta.nqkv);
+            for (int i = threadIdx.x; i < ta.nqkv / 4; i += kThreadsT) dst[i] = src[i];
+        }
 #pragma unroll
         for (int i = 0; i < kMaxPer; ++i)
             if (i < ne) es[threadIdx.x + kThreadsT * i] = o[i] + e[i];
