@@ -1,0 +1,94 @@
+"""bench.py's work model and driver choice (CPU only).
+
+The byte and flop counts set every roofline fraction the bench reports, so
+they are pinned here against the frame's weight shapes written out one matrix
+at a time (Qwen3-TTS code predictor, rightkit-qts exporter README, "Loader
+contract": per layer the fused q/k/v, output, gate, up and down projections;
+fifteen lm_head matrices; the input projection W_p), not against bench.py's
+own per-layer formula.
+"""
+import argparse
+import os
+import subprocess
+import sys
+
+import bench
+from rvq_codebook_code_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _weight_counts(g):
+    """(per-step weights, layer-0 q/k/v weights, projection weights) from the
+    matrix shapes [out, in]."""
+    qd = g.n_q_heads * g.head_dim
+    nqkv = (g.n_q_heads + 2 * g.n_kv_heads) * g.head_dim
+    layer = [(nqkv, g.d_model), (g.d_model, qd), (g.d_ffn, g.d_model), (g.d_ffn, g.d_model), (g.d_model, g.d_ffn)]
+    step = sum(o * i for _ in range(g.n_layers) for o, i in layer) + g.vocab * g.d_model
+    return step, nqkv * g.d_model, g.d_model * g.d_talker
+
+
+def test_frame_bytes_follow_the_weight_shapes():
+    g = synth.WORKLOADS["b1"].geom
+    step, qkv0, proj = _weight_counts(g)
+    assert bench.algorithmic_bytes(g) == (15 * step + proj) * 2 == 2_426_404_864
+    # with the layer-0 table: that layer's q/k/v weights at step 1 only, plus
+    # one fp32 row of (nq + 2 nkv) hd values per request and step 2..15
+    nqkv = (g.n_q_heads + 2 * g.n_kv_heads) * g.head_dim
+    for B in (1, 2, 16):
+        want = (15 * step + proj - 14 * qkv0) * 2 + 14 * B * nqkv * 4
+        assert bench.algorithmic_bytes(g, B, qkv0_table=True) == want
+    assert bench.algorithmic_bytes(g, 1, qkv0_table=True) == 2_309_193_728
+
+
+def test_block_format_bytes():
+    """Q8_0 blocks are 34 B per 32 weights, Q4_0 blocks 18 B (an f16 scale
+    plus the codes)."""
+    g4 = synth.WORKLOADS["q4_b1"].geom
+    step, _, proj = _weight_counts(g4)
+    assert bench.algorithmic_bytes(g4) == (15 * step + proj) * 18 // 32 == 682_426_368
+    g8 = synth.WORKLOADS["q8ema"].geom
+    step, _, proj = _weight_counts(g8)
+    assert bench.algorithmic_bytes(g8) == (15 * step + proj) * 34 // 32
+
+
+def test_frame_flops():
+    g = synth.WORKLOADS["b128"].geom
+    step, qkv0, proj = _weight_counts(g)
+    assert bench.algorithmic_flops(g, 128) == 2 * 128 * (15 * step + proj)
+    assert bench.algorithmic_flops(g, 128, qkv0_table=True) == 2 * 128 * (15 * step + proj - 14 * qkv0)
+
+
+def test_talker_step_bytes():
+    """Every Talker weight once plus the history's bf16 keys and values."""
+    wl = synth.TALKER_WORKLOADS["talker_b1"]
+    g = wl.geom
+    qd, kd = g.n_q_heads * g.head_dim, g.n_kv_heads * g.head_dim
+    mats = [(qd + 2 * kd, g.d_model), (g.d_model, qd), (g.d_ffn, g.d_model), (g.d_ffn, g.d_model),
+            (g.d_model, g.d_ffn)]
+    weights = (g.n_layers * sum(o * i for o, i in mats) + g.vocab * g.d_model) * 2
+    kv = 1 * g.n_layers * (1024 + 1) * 2 * kd * 2
+    assert bench.talker_bytes(g, 1, 1024) == weights + kv
+
+
+def test_driver_choice():
+    args = argparse.Namespace(sample=None, stepwise=False, generic=False)
+    W = synth.WORKLOADS
+    assert bench.select_driver(W["b1"].geom, 1, args) == "dataflow"
+    assert bench.select_driver(W["b1"].geom, 2, args) == "dataflow"
+    assert bench.select_driver(W["b16"].geom, 16, args) == "tiled"
+    assert bench.select_driver(W["q4_b1"].geom, 1, args) == "dataflow"
+    assert bench.select_driver(W["q8ema"].geom, 64, args) == "tiled"
+    assert bench.select_driver(W["tiny_bf16"].geom, 1, args) == "tiled"
+    assert bench.select_driver(W["tiny"].geom, 4, args) == "generic"
+    assert bench.select_driver(W["b1"].geom, 1, argparse.Namespace(sample="0.9,50,0.95", stepwise=False,
+                                                                   generic=False)) == "tiled"
+    assert bench.has_qkv0_table(W["b128"].geom) and bench.has_qkv0_table(W["q4_b16"].geom)
+    assert not bench.has_qkv0_table(W["tiny_bf16"].geom)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
