@@ -396,7 +396,7 @@ def main():
                    "ms_per_launch": round(launch_ms, 4),
                    "tokens_per_s": round(15 * frames_per_s, 1),
                    "algorithmic_bytes_per_step": nbytes,
-                   "algorithmic_flops_per_step": algorithmic_flops(g, B)},
+                   "algorithmic_flops_per_step": nflops},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
