@@ -27,6 +27,10 @@
  *     on the calling thread.  Nothing is printed unless the environment
  *     variable QP_LOG is set; then each failure also writes that text and the
  *     status name to stderr, one line per failure.
+ *   - For tests only: QP_TEST_EPOCH0, if set when qp_create runs, is the first
+ *     32-bit record tag of the new handle's small-batch dataflow frames (the
+ *     tags restart, after every record is cleared, before they would wrap; a
+ *     test sets it near that point).  Results do not depend on it.
  *   - Weight pointers given to qp_create are HOST pointers; the library copies
  *     and repacks everything before returning, so the caller keeps ownership
  *     and may free them afterwards.

@@ -219,6 +219,28 @@ def test_dataflow_kernel_against_oracle_and_generic(B, name):
         assert np.abs(gen["embsum"] - got["embsum"]).max() <= 1e-5
 
 
+def test_dataflow_record_tags_restart(monkeypatch):
+    """The dataflow kernel's 32-bit record tags restart, after every record
+    is cleared, before they would wrap (after about 11 million frames).  A
+    handle that starts just below that point runs frames on both sides of the
+    restart; they equal a fresh handle's bit for bit."""
+    wl, W, model, pred = workload("b1")
+    ppf = 1 + 15 * (5 * wl.geom.n_layers + 1) + 1
+    last = 2**32 - 1 - 2 * ppf            # the highest start the kernel runs without a restart
+    for start in (last - 100, last):
+        monkeypatch.setenv("QP_TEST_EPOCH0", str(start))
+        late = bd.Predictor(W, wl.geom, max_batch=2)
+        monkeypatch.delenv("QP_TEST_EPOCH0")
+        H, q0 = synth.make_inputs(wl.geom, 2, 3, 5150 + start % 7)
+        for f in range(3):
+            for B in (1, 2):
+                a = gpu_frame(pred, H[f][:B], q0[f][:B])
+                b = gpu_frame(late, H[f][:B], q0[f][:B])
+                for key in ("tokens", "logits", "embsum"):
+                    np.testing.assert_array_equal(a[key], b[key])
+        late.close()
+
+
 def test_dataflow_kernel_taps_and_repeat():
     wl, W, model, pred = workload("b1")
     H, q0 = synth.make_inputs(wl.geom, 1, 2, 777)
