@@ -562,6 +562,12 @@ int tiled_gemm(const Handle* h, qp::tiled::GemmArgs g, hipStream_t stream) {
     g.part = h->t_part;
     g.part_bytes = static_cast<uint32_t>(h->t_part_floats * 4);
     g.ctr = h->t_ctr;
+    // Workgroups go to the 8 XCDs round-robin by linear id x + gx (y + gy z).
+    // With gx a multiple of 8 (every product of the 1.7B predictor and the
+    // Talker: gx = N/16 or N/32 with N a multiple of 256), every row tile and
+    // K split of column tile x runs on XCD x mod 8, so each weight slice is
+    // fetched into one XCD's L2 only; the activation rows, read by all, are
+    // small.
     const dim3 grid(gx, gy, KS);
     if (RT == 1) {
         // little work per output: 8 waves per workgroup keep twice the weight
