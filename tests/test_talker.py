@@ -235,6 +235,44 @@ def test_talker_full_depth_rows():
 
 
 @pytest.mark.gpu
+def test_talker_full_size_batch_from_graph():
+    """The configuration the bench times: the 1.7B Talker, B = 16 requests
+    with 1,024 positions of history each, one step replayed from a graph (no
+    logits hook).  Rows 0 and 15 (own histories; the other rows share a third
+    one) against the oracle: H within the depth-scaled bar, q0 where the
+    oracle's top-2 gap is decisive."""
+    torch, dev = _torch_dev()
+    from rvq_codebook_code_amd import binding as bd
+    wl = synth.TALKER_WORKLOADS["talker_b16"]
+    g, B, ctx = wl.geom, wl.batch, wl.context
+    W = synth.make_talker_weights(g, wl.weight_seed)
+    model = TK.TalkerOracle(W, g, keep=False)
+    tk = bd.Talker(W, g, max_batch=B, n_slots=B, max_ctx=ctx + 8)
+    own = {0: synth.make_talker_history(g, ctx, 911), B - 1: synth.make_talker_history(g, ctx, 912)}
+    shared = synth.make_talker_history(g, ctx, 913)
+    for b in range(B):
+        K, V = own.get(b, shared)
+        tk.load_history(b, _bits_to_dev(torch, dev, K), _bits_to_dev(torch, dev, V))
+    X = synth.make_talker_inputs(g, B, 1, 914)[0]
+    H = torch.full((B, g.d_model), float("nan"), device=dev)
+    q0 = torch.full((B,), -1, dtype=torch.int32, device=dev)
+    tk.step(torch.from_numpy(np.ascontiguousarray(X)).to(dev), torch.arange(B, dtype=torch.int32, device=dev),
+            torch.full((B,), ctx, dtype=torch.int32, device=dev), ctx + 1, H, q0)
+    torch.cuda.synchronize()
+    assert tk.get_error() == 0
+    Hg, qg = H.cpu().numpy(), q0.cpu().numpy()
+    tol = tol_for(g.n_layers)
+    for b, (K, V) in own.items():
+        ref = TK.decode_step(model, X[b].astype(np.float64), ctx, synth_bits_to_f64(K), synth_bits_to_f64(V))
+        err = np.abs(Hg[b] - ref["H"]).max()
+        print(f"[talker B=16 graph] row {b} H max-abs {err:.3g} (bar {tol:.3g}) margin {ref['margin']:.3g}")
+        assert err <= tol
+        if ref["margin"] > MARGIN:
+            assert qg[b] == ref["q0"]
+    tk.close()
+
+
+@pytest.mark.gpu
 def test_talker_graph_replays_equal_direct_launches():
     """Steps replayed from graphs (no logits hook) equal the directly
     launched ones bit for bit, as the history grows across split-count
