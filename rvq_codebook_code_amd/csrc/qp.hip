@@ -1035,14 +1035,17 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
         d.k_norm = static_cast<const float*>(up.upload(lw.k_norm, sizeof(float) * m.hd));
         d.ffn_norm = static_cast<const float*>(up.upload(lw.ffn_norm, sizeof(float) * m.dP));
     }
-    m.layers = static_cast<const LayerDev*>(up.upload(layers.data(), sizeof(LayerDev) * (layers.empty() ? 1 : layers.size())));
+    h->layers_host = layers;
+    // a geometry without layers still gets a (never read) one-entry table:
+    // the copy source must be a real host array
+    if (layers.empty()) layers.push_back(LayerDev{});
+    m.layers = static_cast<const LayerDev*>(up.upload(layers.data(), sizeof(LayerDev) * layers.size()));
     m.out_norm = static_cast<const float*>(up.upload(w->out_norm, sizeof(float) * m.dP));
     for (int k = 0; k < kSteps && up.st == QP_OK; ++k) {
         const Uploader::HostMat hl = Uploader::build({w->lm_head[k]}, {m.V}, m.dP, wt);
         m.lm[k] = up.rowmajor(hl);
         if (h->tiled_ok) h->t_lm[k] = up.fragments(hl);
     }
-    h->layers_host = layers;
 
     // RoPE table, fp64 then rounded: angle(p, i) = p * base^(-2i/hd)
     const int half = m.hd / 2;

@@ -8,6 +8,8 @@ Bar (per workload): under teacher forcing with the oracle's own tokens,
 Free-run token agreement is printed as context.  Large batches are checked on
 sampled rows (rows are independent, so the oracle computes only those).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -288,6 +290,27 @@ def test_tiled_large_batches(name, B):
     pred = _cache[key]
     H, q0 = synth.make_inputs(wl.geom, B, 1, 3200 + B)
     check_against_oracle(f"tiled {name} B={B}", model, pred, H[0], q0[0], np.arange(B), tiled=True)
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_bf16"])
+def test_zero_layers(name):
+    """Degenerate geometry without decoder layers: step k's logits are the
+    lm_head of the normed projected-table row (the oracle's zero-layer pin).
+    fp32 weights on the generic path (persistent and stepwise), bf16 on the
+    batched path."""
+    wl = synth.WORKLOADS[name]
+    g = dataclasses.replace(wl.geom, n_layers=0)
+    W = synth.make_weights(g, wl.weight_seed)
+    model = O.OracleModel(W, g)
+    pred = bd.Predictor(W, g, max_batch=8)
+    H, q0 = synth.make_inputs(g, 5, 1, 6060)
+    rows = np.arange(5)
+    if name == "tiny":
+        check_against_oracle("tiny L=0", model, pred, H[0], q0[0], rows)
+        check_against_oracle("tiny L=0 stepwise", model, pred, H[0], q0[0], rows, stepwise=True)
+    else:
+        check_against_oracle("tiny_bf16 L=0", model, pred, H[0], q0[0], rows, tiled=True)
+    pred.close()
 
 
 def test_tiled_taps_composition_and_repeat():

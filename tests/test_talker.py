@@ -188,6 +188,24 @@ def test_talker_steps_against_oracle(name):
 
 
 @pytest.mark.gpu
+def test_talker_zero_layers():
+    """Degenerate Talker without blocks: H is the output norm of the input
+    row and q0 the head's argmax (the oracle's zero-layer closed form); the
+    histories are empty tensors."""
+    _torch_dev()
+    from rvq_codebook_code_amd import binding as bd
+    wl = synth.TALKER_WORKLOADS["talker_tiny"]
+    g = dataclasses.replace(wl.geom, n_layers=0)
+    W = synth.make_talker_weights(g, wl.weight_seed)
+    model = TK.TalkerOracle(W, g)
+    hist = [synth.make_talker_history(g, n, 70 + n) for n in (0, 3)]
+    X = synth.make_talker_inputs(g, 2, 2, 71)
+    tk = bd.Talker(W, g, max_batch=4, n_slots=4, max_ctx=16)
+    _run_and_compare("talker L=0", model, tk, g, [1, 3], hist, X)
+    tk.close()
+
+
+@pytest.mark.gpu
 def test_talker_flags_and_cache_untouched():
     """A row with a position beyond the attention grid that max_len sizes
     (chunks of at least 64 positions), past max_ctx, negative, or an unknown
