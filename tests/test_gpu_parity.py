@@ -243,6 +243,30 @@ def test_dataflow_record_tags_restart(monkeypatch):
         late.close()
 
 
+@pytest.mark.parametrize("name", ["b16", "q4_b16"])
+def test_dataflow_table_rows_at_vocabulary_ends(name):
+    """Forced tokens 0 and V-1 alternating (and q0 at both ends): the fed
+    rows of the projected tables and of the layer-0 q/k/v table at the
+    vocabulary's first and last index, on the dataflow kernel (B = 1, 2)
+    against the oracle under the same forcing."""
+    wl, W, model, pred = workload(name)
+    V = wl.geom.vocab
+    H, _ = synth.make_inputs(wl.geom, 2, 1, 8080)
+    q0 = np.array([V - 1, 0], dtype=np.int32)
+    force = np.zeros((2, 15), dtype=np.int32)
+    force[0, 1::2] = V - 1
+    force[1, 0::2] = V - 1
+    for B in (1, 2):
+        ref = O.run_frames(model, H[0][:B], q0[:B], force=force[:B])
+        got = gpu_frame(pred, H[0][:B], q0[:B], force=force[:B])
+        lg = np.abs(got["logits"] - ref["logits"]).max()
+        em = np.abs(got["embsum"] - ref["embsum"]).max()
+        print(f"[dataflow {name} ends B={B}] logits max-abs {lg:.3g} embsum max-abs {em:.3g}")
+        assert lg <= TOL[wl.geom.weight_dtype] and em <= TOL[wl.geom.weight_dtype]
+        sure = ref["margin"] > MARGIN
+        assert (got["tokens"] == ref["tokens"])[sure].all()
+
+
 def test_dataflow_kernel_taps_and_repeat():
     wl, W, model, pred = workload("b1")
     H, q0 = synth.make_inputs(wl.geom, 1, 2, 777)

@@ -188,6 +188,29 @@ def test_talker_steps_against_oracle(name):
 
 
 @pytest.mark.gpu
+def test_talker_last_position():
+    """Steps up to the last position a slot holds (max_ctx - 1 = 129: three
+    64-position chunks, the split count rounded up to four), then one more
+    step, which raises the position flag."""
+    torch, dev = _torch_dev()
+    from rvq_codebook_code_amd import binding as bd
+    wl = synth.TALKER_WORKLOADS["talker_tiny"]
+    g = wl.geom
+    W = synth.make_talker_weights(g, wl.weight_seed)
+    model = TK.TalkerOracle(W, g)
+    tk = bd.Talker(W, g, max_batch=2, n_slots=2, max_ctx=130)
+    hist = [synth.make_talker_history(g, 127, 81), synth.make_talker_history(g, 60, 82)]
+    X = synth.make_talker_inputs(g, 2, 3, 83)
+    _run_and_compare("talker last position", model, tk, g, [1, 0], hist, X)
+    H = torch.zeros((1, g.d_model), device=dev)
+    q0 = torch.zeros((1,), dtype=torch.int32, device=dev)
+    tk.step(torch.from_numpy(X[0][:1]).to(dev), torch.tensor([1], dtype=torch.int32, device=dev),
+            torch.tensor([130], dtype=torch.int32, device=dev), 130, H, q0)
+    assert tk.get_error() & 1
+    tk.close()
+
+
+@pytest.mark.gpu
 def test_talker_zero_layers():
     """Degenerate Talker without blocks: H is the output norm of the input
     row and q0 the head's argmax (the oracle's zero-layer closed form); the
