@@ -267,6 +267,24 @@ def test_dataflow_table_rows_at_vocabulary_ends(name):
         assert (got["tokens"] == ref["tokens"])[sure].all()
 
 
+@pytest.mark.parametrize("n_layers", [1, 2])
+def test_dataflow_kernel_fewer_layers(n_layers):
+    """The dataflow kernel takes 1 to 5 layers of the 1.7B widths: its phase
+    count and weight-prefetch chain change with L (with one layer, layer 0 is
+    also the last, and its q/k/v comes from the table from step 2 on).
+    B = 1 and 2 against the oracle."""
+    wl = synth.WORKLOADS["b16"]
+    g = dataclasses.replace(wl.geom, n_layers=n_layers)
+    W = synth.make_weights(g, wl.weight_seed)
+    model = O.OracleModel(W, g)
+    pred = bd.Predictor(W, g, max_batch=2)
+    H, q0 = synth.make_inputs(g, 2, 2, 7070 + n_layers)
+    for f in range(2):
+        for B in (1, 2):
+            check_against_oracle(f"dataflow L={n_layers} B={B}", model, pred, H[f][:B], q0[f][:B], np.arange(B))
+    pred.close()
+
+
 def test_dataflow_kernel_taps_and_repeat():
     wl, W, model, pred = workload("b1")
     H, q0 = synth.make_inputs(wl.geom, 1, 2, 777)
