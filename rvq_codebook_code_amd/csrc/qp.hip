@@ -670,17 +670,27 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
                 g.ldo = m.nqkv;
                 tiled_gemm<WT, T::SRC_BF16_NORM, T::EPI_SCALE>(h, g, stream);
             }
-            // attention
+            // attention (layer 0 from step 2 on, with the table: also the
+            // previous step's token decision, handed over below)
             aa.s = s;
             aa.l = l;
+            aa.tok_on = (l == 0 && s > 1 && m.qkv0) ? 1 : 0;
             aa.k_norm = L.k_norm;
             aa.q_norm = L.q_norm;
             aa.ao = ao;
             const dim3 ag(B * m.nkv);
-            switch (m.hd) {
-                case 64: hipLaunchKernelGGL(T::k_attn<64>, ag, dim3(T::kThreadsT), 0, stream, aa); break;
-                case 128: hipLaunchKernelGGL(T::k_attn<128>, ag, dim3(T::kThreadsT), 0, stream, aa); break;
-                default: hipLaunchKernelGGL(T::k_attn<256>, ag, dim3(T::kThreadsT), 0, stream, aa); break;
+            if (aa.tok_on) {
+                switch (m.hd) {
+                    case 64: hipLaunchKernelGGL((T::k_attn<64, true>), ag, dim3(T::kThreadsT), 0, stream, aa); break;
+                    case 128: hipLaunchKernelGGL((T::k_attn<128, true>), ag, dim3(T::kThreadsT), 0, stream, aa); break;
+                    default: hipLaunchKernelGGL((T::k_attn<256, true>), ag, dim3(T::kThreadsT), 0, stream, aa); break;
+                }
+            } else {
+                switch (m.hd) {
+                    case 64: hipLaunchKernelGGL((T::k_attn<64, false>), ag, dim3(T::kThreadsT), 0, stream, aa); break;
+                    case 128: hipLaunchKernelGGL((T::k_attn<128, false>), ag, dim3(T::kThreadsT), 0, stream, aa); break;
+                    default: hipLaunchKernelGGL((T::k_attn<256, false>), ag, dim3(T::kThreadsT), 0, stream, aa); break;
+                }
             }
             // x += W_o . attention; publishes bf16(ffn_norm * x)
             g = T::GemmArgs{};
@@ -764,7 +774,13 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
         ta.emb = m.emb[s];
         ta.ptab = s < kSteps ? m.ptab + static_cast<size_t>(s) * m.V * m.dP : nullptr;
         ta.qkv0 = s < kSteps && m.qkv0 ? m.qkv0 + static_cast<size_t>(s - 1) * m.V * m.nqkv : nullptr;
-        hipLaunchKernelGGL(T::k_next, dim3(nb), dim3(T::kThreadsT), 0, stream, ta);
+        if (ta.qkv0) {
+            // the next step's layer-0 attention decides this step's token and
+            // reads its q/k/v rows from the table: no k_next launch
+            aa.tok = ta;
+        } else {
+            hipLaunchKernelGGL(T::k_next, dim3(nb), dim3(T::kThreadsT), 0, stream, ta);
+        }
     }
     if (!check_hip(hipGetLastError(), "batched path kernel launch", &st)) return st;
     return QP_OK;

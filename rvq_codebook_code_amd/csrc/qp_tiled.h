@@ -135,6 +135,11 @@ struct AttnArgs {
     const float* rope_cos;            // [16][hd/2]
     const float* rope_sin;
     uint16_t* ao;                     // [M][nq*hd] bf16 output
+    // layer 0 from step 2 on, with the layer-0 q/k/v table: the previous
+    // step's token decision (tok.s = that step) happens here instead of in
+    // k_next, and the head vectors come from tok.qkv0 [V][nqkv]
+    int tok_on;
+    TokArgs tok;
 };
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -599,7 +604,38 @@ __device__ __forceinline__ void norm_rope_regs(const float (&v)[HD / 64], const 
 // formed at once: key t on lanes 4t..4t+3, each lane a quarter of the head.
 // Output: bf16 rows [M][nq*hd], the operand of the output projection.
 // ---------------------------------------------------------------------------
-template <int HD>
+// Step ta.s's token of request b from the lm_head tiles' keys (or the drawn
+// token of a sampled frame), and the token fed back (forced or own), checked
+// and clamped; block-wide, uniform result.  The writer also stores the token
+// and raises the flags.  red: [kThreadsT / 64] LDS scratch, fed_s: one int.
+__device__ __forceinline__ int decide_fed(const TokArgs& ta, int b, bool writer, uint64_t* red, int* fed_s) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nkt = ta.nkt;
+    uint64_t k = 0;
+    if (!ta.sampled)
+        for (int t = threadIdx.x; t < nkt; t += kThreadsT) k = umax64(k, ta.keys[static_cast<size_t>(b) * nkt + t]);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) k = umax64(k, shfl_xor64(k, off));
+    __syncthreads();
+    if (lane == 0) red[wave] = k;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint64_t kk = red[0];
+        for (int w = 1; w < kThreadsT / 64; ++w) kk = umax64(kk, red[w]);
+        const int tok = ta.sampled ? ta.sampled[b] : argmax_index(kk);
+        int fed = ta.force ? ta.force[b * kSteps + (ta.s - 1)] : tok;
+        const bool bad = fed < 0 || fed >= ta.V;
+        if (writer) {
+            ta.tok_out[b * kSteps + (ta.s - 1)] = tok;
+            if (bad) atomicOr(ta.err, ta.force ? kErrBadForced : kErrBadQ0);
+        }
+        *fed_s = bad ? 0 : fed;
+    }
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(*fed_s);
+}
+
+template <int HD, bool TOK>
 __global__ __launch_bounds__(kThreadsT) void k_attn(AttnArgs m) {
     constexpr int J = HD / 64;        // elements per lane in the lane + 64 j layout
     constexpr int SL = HD / 4;        // slice of the head per lane in the score
@@ -608,6 +644,8 @@ __global__ __launch_bounds__(kThreadsT) void k_attn(AttnArgs m) {
     __shared__ float Vs[kPositions][HD];
     __shared__ float qs[4][HD];
     __shared__ float es[4][kPositions];
+    __shared__ uint64_t red_s[kThreadsT / 64];
+    __shared__ int fed_s;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int B = m.B, s = m.s, l = m.l;
@@ -630,13 +668,35 @@ __global__ __launch_bounds__(kThreadsT) void k_attn(AttnArgs m) {
             hv[i] = m.vc[off];
         }
     }
+    // layer 0 with the table: the previous step's token first (the history
+    // loads above are in flight meanwhile); kv head 0's workgroup also moves
+    // the request to the token: embsum += E[t], residual row = P[t]
+    const TokArgs& ta = m.tok;
+    int fed = -1;
+    float o_es[TOK ? kMaxPer : 1], o_e[TOK ? kMaxPer : 1], o_v[TOK ? kMaxPer : 1], o_gv[TOK ? kMaxPer : 1];
+    const int ne = ta.dT / kThreadsT, np = ta.dP / kThreadsT;
+    if constexpr (TOK) {
+        if (g == 0) {
+            load_vec(ta.gain0, np, o_gv);
+            load_vec(ta.embsum + static_cast<size_t>(b) * ta.dT, ne, o_es);
+        }
+        fed = decide_fed(ta, b, g == 0, red_s, &fed_s);
+        if (g == 0) {
+            load_emb(ta, fed, o_e);
+            load_vec(ta.ptab + static_cast<size_t>(fed) * ta.dP, np, o_v);
+        }
+    }
+    // the step's q/k/v row of position pi: from the table when fed >= 0
+    auto qkv_row = [&](int pi) {
+        const int r = (s == 1) ? pi * B + b : b;
+        return fed >= 0 ? ta.qkv0 + static_cast<size_t>(fed) * m.nqkv : m.qkv + static_cast<size_t>(r) * m.nqkv;
+    };
     // wave 0: the step's key rows, wave 1: value rows, wave w: query head
     // g * grp + w (later heads of a large group are read when used)
     float pin[2][J];
 #pragma unroll
     for (int pi = 0; pi < 2; ++pi) {
-        const int r = (s == 1) ? pi * B + b : b;
-        const float* row = m.qkv + static_cast<size_t>(r) * m.nqkv;
+        const float* row = qkv_row(pi);
         const int col = wave == 0 ? (m.nq + g) * HD : (wave == 1 ? (m.nq + nkv + g) * HD : 0);
 #pragma unroll
         for (int j = 0; j < J; ++j) pin[pi][j] = 0.f;
@@ -648,13 +708,23 @@ __global__ __launch_bounds__(kThreadsT) void k_attn(AttnArgs m) {
     float qin[2][J];
 #pragma unroll
     for (int pi = 0; pi < 2; ++pi) {
-        const int r = (s == 1) ? pi * B + b : b;
-        const float* row = m.qkv + static_cast<size_t>(r) * m.nqkv;
+        const float* row = qkv_row(pi);
 #pragma unroll
         for (int j = 0; j < J; ++j) qin[pi][j] = 0.f;
         if (pi < npos && wave < grp) {
 #pragma unroll
             for (int j = 0; j < J; ++j) qin[pi][j] = row[(g * grp + wave) * HD + lane + 64 * j];
+        }
+    }
+    // the request's move to the token (its loads were issued before the head
+    // vectors', so this waits for nothing the attention does not need)
+    if constexpr (TOK) {
+        if (g == 0) {
+            float* es_row = ta.embsum + static_cast<size_t>(b) * ta.dT;
+#pragma unroll
+            for (int i = 0; i < kMaxPer; ++i)
+                if (i < ne) es_row[threadIdx.x + kThreadsT * i] = o_es[i] + o_e[i];
+            store_row(ta, b, o_v, o_gv);
         }
     }
 #pragma unroll
@@ -694,7 +764,7 @@ __global__ __launch_bounds__(kThreadsT) void k_attn(AttnArgs m) {
 #pragma unroll
                 for (int j = 0; j < J; ++j) qv[j] = qin[pi][j];
             } else {
-                const float* row = m.qkv + static_cast<size_t>(r) * m.nqkv + h * HD;
+                const float* row = qkv_row(pi) + h * HD;
 #pragma unroll
                 for (int j = 0; j < J; ++j) qv[j] = row[lane + 64 * j];
             }
@@ -775,38 +845,16 @@ __global__ __launch_bounds__(kThreadsT) void k_start(TokArgs ta) {
 // sets the next position's input row P_s[t] (and, with the table, that row's
 // layer-0 q/k/v rows).
 __global__ __launch_bounds__(kThreadsT) void k_next(TokArgs ta) {
-    __shared__ unsigned long long red[kThreadsT / 64];
+    __shared__ uint64_t red[kThreadsT / 64];
     __shared__ int fed_s;
-    const int B = ta.B, s = ta.s, nkt = ta.nkt;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int B = ta.B;
     const int ne = ta.dT / kThreadsT, np = ta.dP / kThreadsT;
     float gv[kMaxPer], o[kMaxPer], v[kMaxPer], e[kMaxPer];
     if (ta.ptab) load_vec(ta.gain0, np, gv);
     for (int b = blockIdx.x; b < B; b += gridDim.x) {
         float* es = ta.embsum + static_cast<size_t>(b) * ta.dT;
         load_vec(es, ne, o);
-        uint64_t k = 0;
-        if (!ta.sampled)
-            for (int t = threadIdx.x; t < nkt; t += kThreadsT) k = umax64(k, ta.keys[static_cast<size_t>(b) * nkt + t]);
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) k = umax64(k, shfl_xor64(k, off));
-        __syncthreads();
-        if (lane == 0) red[wave] = k;
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            uint64_t kk = red[0];
-            for (int w = 1; w < kThreadsT / 64; ++w) kk = umax64(kk, red[w]);
-            const int tok = ta.sampled ? ta.sampled[b] : argmax_index(kk);
-            ta.tok_out[b * kSteps + (s - 1)] = tok;
-            int fed = ta.force ? ta.force[b * kSteps + (s - 1)] : tok;
-            if (fed < 0 || fed >= ta.V) {
-                atomicOr(ta.err, ta.force ? kErrBadForced : kErrBadQ0);
-                fed = 0;
-            }
-            fed_s = fed;
-        }
-        __syncthreads();
-        const int t = __builtin_amdgcn_readfirstlane(fed_s);
+        const int t = decide_fed(ta, b, true, red, &fed_s);
         load_emb(ta, t, e);
         if (ta.ptab) load_vec(ta.ptab + static_cast<size_t>(t) * ta.dP, np, v);
         if (ta.qkv0) {
