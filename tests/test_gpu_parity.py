@@ -409,10 +409,13 @@ def test_tiled_graph_replays_match_stream_path():
         np.testing.assert_array_equal(again["embsum"], graph["embsum"])
 
 
-@pytest.mark.parametrize("name,tiled", [("tiny_bf16", True), ("b16", False)], ids=["batched", "dataflow"])
+@pytest.mark.parametrize("name,tiled", [("tiny_bf16", True), ("b16", True), ("b16", False)],
+                         ids=["batched", "batched-table", "dataflow"])
 def test_flags_on_fast_paths(name, tiled):
     """Out-of-range q0 (graph and direct launches) and forced tokens raise the
-    sticky flag, are read as token 0, and leave the next call clean."""
+    sticky flag, are read as token 0, and leave the next call clean.  On the
+    1.7B geometry the batched path decides tokens in the next step's layer-0
+    attention (the layer-0 table), elsewhere in k_next."""
     wl, W, model, pred = workload(name)
     dev = _dev()
     g = wl.geom
