@@ -572,10 +572,11 @@ int tiled_gemm(const Handle* h, qp::tiled::GemmArgs g, hipStream_t stream) {
     if (RT == 1) {
         // up to 16 rows there is little work per output: 8 waves per
         // workgroup keep twice the weight bytes in flight where K splits into
-        // 16 pairs of blocks (M = 1: 5 % faster per Talker step than 4 waves;
-        // M = 16: equal).  Above 16 rows 4 waves are faster (M = 64 Q8_0:
-        // 3.5 % per frame-batch).
-        const bool w8 = g.M <= 16 && (g.K / 32) % 16 == 0;
+        // 16 pairs of blocks (M = 1: 5 % faster per Talker step than 4 waves,
+        // from the residual products).  Above 16 rows 4 waves are faster
+        // (M = 64 Q8_0: 3.5 % per frame-batch), and so is SwiGLU, whose
+        // workgroups read two fragments, at any M (B = 16: 0.5 %).
+        const bool w8 = EPI != T::EPI_SWIGLU && g.M <= 16 && (g.K / 32) % 16 == 0;
         constexpr int C1 = EPI == T::EPI_SWIGLU ? 2 : 1;
         if (w8)
             hipLaunchKernelGGL((T::k_gemm<WT, 1, SRC, EPI, 8, C1>), grid, dim3(512), 0, stream, g);
