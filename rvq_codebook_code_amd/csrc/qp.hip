@@ -530,14 +530,15 @@ namespace {
 template <int WT, int SRC, int EPI, class Handle>
 int tiled_gemm(const Handle* h, qp::tiled::GemmArgs g, hipStream_t stream) {
     namespace T = qp::tiled;
-    // one 16-row tile per workgroup up to 64 rows (more workgroups per CU to
+    // one 16-row tile per workgroup up to 32 rows (more workgroups per CU to
     // cover memory latency; the weights are re-read from L2 per row tile),
     // two above (measured: B = 64 Q8_0 +27 %, B = 128 bf16 +11 % over tiles
-    // of up to 64 rows).  Residual products (N = dP) keep one row tile at any
-    // M: with two they need the split-K fixup to fill the chip, and its extra
-    // round trips cost more (B = 128 bf16: 4.15 against 4.29 ms per
-    // frame-batch; one row tile for the other products was slower)
-    const int RT = (g.M <= 64 || EPI == T::EPI_RESID) ? 1 : 2;
+    // of up to 64 rows; B = 64 Q8_0 +1.5 % over one row tile up to 64 rows).
+    // Residual products (N = dP) keep one row tile at any M: with two they
+    // need the split-K fixup to fill the chip, and its extra round trips cost
+    // more (B = 128 bf16: 4.15 against 4.29 ms per frame-batch; one row tile
+    // for the other products was slower)
+    const int RT = (g.M <= 32 || EPI == T::EPI_RESID) ? 1 : 2;
     // one row tile: one 16-column fragment per workgroup (twice the
     // workgroups streaming weights); SwiGLU always pairs gate and up
     const int CT = (RT == 1 && EPI != T::EPI_SWIGLU) ? 1 : 2;

@@ -31,7 +31,7 @@
 //    32-bit word (256 B per fragment).
 //  * A workgroup of NW waves owns a tile of 16*RT rows x 16*CT output
 //    columns (for SwiGLU the gate and up fragments of the same 16 columns).
-//    RT = 1 (up to 64 rows, and the residual products) takes CT = 1
+//    RT = 1 (up to 32 rows, and the residual products) takes CT = 1
 //    (SwiGLU: its pair) and, except SwiGLU, NW = 8 up to 16 rows where K
 //    holds 16 pairs of 32-wide blocks, else 4; RT = 2 takes CT = 2 and
 //    NW = 4.  The NW waves split K and their partial tiles are summed through
