@@ -331,6 +331,24 @@ def test_sampled_top_k_one_is_the_greedy_frame_and_graphs_match_direct_launches(
 
 
 @pytest.mark.gpu
+def test_sampled_full_size_graph_equals_direct():
+    """1.7B-shaped bf16 predictor (where the layer-0 attention decides each
+    drawn token): a sampled frame replayed from its graph equals the same
+    frame launched directly (logits hook) bit for bit, at B = 16 and 5,
+    interleaved with a greedy frame."""
+    from rvq_codebook_code_amd import synth
+    wl, model, pred = _pred("b16", 16)
+    H, q0 = synth.make_inputs(wl.geom, 16, 1, 2469)
+    U = synth.make_uniforms(16, 1, 1358)[0]
+    for B, (T, K, P) in [(16, (0.9, 50, 0.95)), (5, (1.2, 0, 0.8)), (16, (0.9, 50, 0.95))]:
+        a = _sampled_frame(pred, H[0][:B], q0[0][:B], U[:B], T, K, P, logits=False)
+        _sampled_frame(pred, H[0][:B], q0[0][:B], U[:B], 0.7, 1, 1.0, logits=False)
+        b = _sampled_frame(pred, H[0][:B], q0[0][:B], U[:B], T, K, P, logits=True)
+        np.testing.assert_array_equal(a["tokens"], b["tokens"])
+        np.testing.assert_array_equal(a["embsum"], b["embsum"])
+
+
+@pytest.mark.gpu
 def test_sampled_full_size_rows():
     """1.7B-shaped bf16 predictor, B = 16: two rows checked against the
     oracle under teacher forcing with its draws."""
