@@ -153,6 +153,31 @@ def test_argmax_lowest_index_on_ties():
 # the loop against brute force and the library's code predictor
 # ----------------------------------------------------------------------------
 
+def test_top2_margin_hand_built():
+    """The gap that gates every token comparison: the largest logit minus the
+    second largest, counting an exactly repeated maximum as the second (gap
+    0), over the last axis only."""
+    cases = [([1.0, 3.0, 2.5, -1.0], 0.5),          # max not first, runner-up not adjacent
+             ([-4.0, -2.0, -3.5], 1.5),              # all negative
+             ([2.0, 2.0, 1.0], 0.0),                 # tied maximum
+             ([0.25, 7.0], 6.75),
+             ([5.0, -5.0, 4.875, 4.875], 0.125)]     # tied runners-up
+    for row, want in cases:
+        assert O.top2_margin(np.array(row))[()] == want, (row, want)
+    # batched: one gap per row of the last axis, order of rows kept
+    batch = np.array([[1.0, 3.0, 2.5, -1.0], [2.0, 2.0, 1.0, 0.0], [9.0, 0.0, 0.0, 8.0]])
+    np.testing.assert_array_equal(O.top2_margin(batch), [0.5, 0.0, 1.0])
+    np.testing.assert_array_equal(O.top2_margin(batch[None, :, :])[0], [0.5, 0.0, 1.0])
+    # brute force on random rows: remove one occurrence of the maximum, take
+    # the maximum of the rest
+    rng = np.random.default_rng(8)
+    for _ in range(50):
+        row = np.round(rng.standard_normal(9), 1)
+        i = int(np.argmax(row))
+        rest = np.delete(row, i)
+        assert O.top2_margin(row)[()] == row[i] - rest.max()
+
+
 def test_cached_loop_equals_uncached_brute_force():
     geom = micro_geometry()
     _, model, H, q0 = model_and_inputs(geom, B=3)

@@ -8,9 +8,17 @@ The oracle (oracle/talker.py) is pinned to:
   * the zero-layer closed form: H = output_norm * x / rms(x), logits = head . H;
   * the bf16 rounding of the cache: hand-worked values at and around the
     rounding midpoints.
-The block arithmetic (norms, RoPE, GQA, SwiGLU) is the predictor oracle's,
-pinned there.  GPU parity compares the HIP path with the oracle on the same
-seeded weights, histories and inputs.
+  * an independent implementation of the same block: transformers' dense
+    Qwen3 decoder stack (input RMSNorm, q/k/v with per-head q/k RMSNorm and
+    rotate-half RoPE, GQA, output projection, post-attention RMSNorm, SwiGLU,
+    final norm) loaded with the same weights, over whole sequences, and the
+    predictor oracle's block step (itself pinned to transformers' code
+    predictor) fed the same layer weights.  The pages give the Talker the
+    predictor's block tensors (rightkit-qts exporter README, "Loader
+    contract"), so a swapped gate/up, a misplaced q/k norm or a wrong GQA
+    grouping in the Talker step fails here.
+GPU parity compares the HIP path with the oracle on the same seeded weights,
+histories and inputs.
 """
 import dataclasses
 import math
@@ -82,6 +90,96 @@ def test_zero_layers_closed_form():
     np.testing.assert_allclose(r["H"], H, rtol=0, atol=1e-12)
     head = np.array([[synth_bits_to_f64(w) for w in row] for row in W["codec_head"][:5]])
     np.testing.assert_allclose(r["logits"][:5], head @ H, rtol=0, atol=1e-12)
+
+
+def _library_talker(model, g):
+    """transformers' dense Qwen3 decoder stack with the oracle's (materialised)
+    weights, float64, eager attention."""
+    import torch
+    from transformers.models.qwen3.configuration_qwen3 import Qwen3Config
+    from transformers.models.qwen3.modeling_qwen3 import Qwen3Model
+    cfg = Qwen3Config(vocab_size=8, hidden_size=g.d_model, intermediate_size=g.d_ffn,
+                      num_hidden_layers=g.n_layers, num_attention_heads=g.n_q_heads,
+                      num_key_value_heads=g.n_kv_heads, head_dim=g.head_dim, rms_norm_eps=g.rms_eps,
+                      rope_parameters={"rope_type": "default", "rope_theta": g.rope_base},
+                      attention_bias=False, use_sliding_window=False, max_position_embeddings=4096)
+    cfg._attn_implementation = "eager"
+    m = Qwen3Model(cfg).double().eval()
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))
+    with torch.no_grad():
+        for li in range(g.n_layers):
+            lw, L = model.layer(li), m.layers[li]
+            L.input_layernorm.weight.copy_(T(lw["attn_norm"]))
+            L.post_attention_layernorm.weight.copy_(T(lw["ffn_norm"]))
+            L.self_attn.q_proj.weight.copy_(T(lw["wq"]))
+            L.self_attn.k_proj.weight.copy_(T(lw["wk"]))
+            L.self_attn.v_proj.weight.copy_(T(lw["wv"]))
+            L.self_attn.o_proj.weight.copy_(T(lw["wo"]))
+            L.self_attn.q_norm.weight.copy_(T(lw["q_norm"]))
+            L.self_attn.k_norm.weight.copy_(T(lw["k_norm"]))
+            L.mlp.gate_proj.weight.copy_(T(lw["w_gate"]))
+            L.mlp.up_proj.weight.copy_(T(lw["w_up"]))
+            L.mlp.down_proj.weight.copy_(T(lw["w_down"]))
+        m.norm.weight.copy_(T(model.output_norm))
+    return m
+
+
+@pytest.mark.parametrize("which", ["tiny", "l2_widths"])
+def test_decode_steps_match_library_qwen3_stack(which):
+    """Cached decode steps from an empty history (exact cache values) against
+    transformers' Qwen3 decoder stack run over the whole sequence: H at every
+    position, and the codec head's logits of that H."""
+    import torch
+    if which == "tiny":
+        wl, g, W = _tiny()
+        n = 6
+    else:
+        wl = synth.TALKER_WORKLOADS["talker_l2"]
+        g = dataclasses.replace(wl.geom, n_layers=1, d_ffn=1024, vocab=64)
+        W = synth.make_talker_weights(g, 3101)
+        n = 4
+    model = TK.TalkerOracle(W, g)
+    X = synth.make_talker_inputs(g, 1, n, 31)[:, 0].astype(np.float64)
+    empty = np.zeros((g.n_layers, 0, g.n_kv_heads, g.head_dim))
+    steps = TK.run_steps(model, X, 0, empty, empty, kv_round=False)
+    lib = _library_talker(model, g)
+    with torch.no_grad():
+        ref = lib(inputs_embeds=torch.from_numpy(X[None]), use_cache=False).last_hidden_state[0].numpy()
+    got = np.stack([r["H"] for r in steps])
+    # the library builds its RoPE table in fp32 (about 4e-7 here); a wrong
+    # block (a swapped gate/up, a misplaced q/k norm) moves H by O(1)
+    err = np.abs(got - ref).max()
+    assert err <= 1e-5, err
+    lg = np.stack([r["logits"] for r in steps])
+    np.testing.assert_allclose(lg, ref @ model.head.T, rtol=0, atol=1e-5)
+
+
+def test_decode_step_block_equals_predictor_block():
+    """One Talker step against the predictor oracle's block step on the same
+    layer weights (the predictor's decode_position is pinned to transformers'
+    code predictor): from an exact history written by earlier positions, the
+    residual stream after the stack, normed with the output gain, is H."""
+    from oracle import predictor as PO
+    wl, g, W = _tiny()
+    model = TK.TalkerOracle(W, g)
+    n = 5
+    X = synth.make_talker_inputs(g, 1, n, 41)[:, 0].astype(np.float64)
+    empty = np.zeros((g.n_layers, 0, g.n_kv_heads, g.head_dim))
+    steps = TK.run_steps(model, X, 0, empty, empty, kv_round=False)
+
+    class _PredView:     # the predictor oracle reads .g and .layers only
+        pass
+    pv = _PredView()
+    pv.g = g
+    pv.layers = [model.layer(l) for l in range(g.n_layers)]
+    kc = np.zeros((g.n_layers, 1, n, g.n_kv_heads, g.head_dim))
+    vc = np.zeros_like(kc)
+    for pos in range(n):
+        x = PO.decode_position(pv, X[pos][None], pos, kc, vc)[0]
+        H = PO.rms_norm(x, model.output_norm, g.rms_eps)
+        assert np.abs(H - steps[pos]["H"]).max() <= 1e-12
+        np.testing.assert_allclose(steps[pos]["k_new"], kc[:, 0, pos], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(steps[pos]["v_new"], vc[:, 0, pos], rtol=0, atol=1e-12)
 
 
 def synth_bits_to_f64(bits):
