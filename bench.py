@@ -8,9 +8,12 @@ with the 1.7B predictor's shapes.
 
 Prints one JSON line: frames/s (whole job), the roofline of the frame kernel
 (algorithmic weight bytes per frame-batch over the measured time per launch,
-against 8 TB/s HBM) and the CPU oracle's own rate on a bounded sample.
+against 8 TB/s HBM; at B = 128 flops against the bf16 matrix-core peak) and
+the CPU oracle's own rate on a bounded sample.  The metric is quoted at B = 1,
+16 and 128: the default run's line is the B = 1 workload, and it carries the
+B = 16 and B = 128 workloads, timed in the same run, under "workloads".
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload b1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload b1] [--only]
 """
 import argparse
 import json
@@ -128,11 +131,7 @@ def run_talker(args, torch, dev):
     achieved = nbytes / (ms_per_step / 1e3) / 1e9
     cpu = None
     if not args.no_cpu_baseline:
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-        except Exception:  # pragma: no cover
-            threads = 1
+        threads, host = host_cores()
         model = TK.TalkerOracle(W, g, keep=True)
         Kf = (K.astype(np.uint32) << 16).view(np.float32).astype(np.float64)[:, :ctx]
         Vf = (V.astype(np.uint32) << 16).view(np.float32).astype(np.float64)[:, :ctx]
@@ -145,7 +144,7 @@ def run_talker(args, torch, dev):
             el = time.perf_counter() - t0
             if el >= args.cpu_budget or n >= 64:
                 break
-        cpu = {"value": round(n / el, 4), "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+        cpu = {"value": round(n / el, 4), "unit": "steps/s", "cores": int(threads), "kind": "oracle", "host": host,
                "sample": f"{n} decode step(s) of 1 request at a {ctx}-position history, fp64 NumPy, "
                          f"{el:.1f} s (after materialising the weights)"}
     line = {
@@ -173,15 +172,26 @@ def run_talker(args, torch, dev):
     tk.close()
 
 
-def cpu_baseline(wl, W, H, q0, budget_s: float, sampling=None, U=None):
-    """The oracle as it stands, on the host, for about ``budget_s`` seconds of
-    frames of the same workload (sampled frames when ``sampling`` is given)."""
-    from oracle import predictor as O
+def host_cores():
+    """BLAS threads the oracle's products use, the host's CPU count and the
+    CPUs this process may run on."""
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except Exception:  # pragma: no cover
+        nproc = os.cpu_count()
+    return int(threads), {"blas_threads": int(threads), "os_cpu_count": os.cpu_count(), "nproc": nproc}
+
+
+def cpu_baseline(wl, W, H, q0, budget_s: float, sampling=None, U=None):
+    """The oracle as it stands, on the host, for about ``budget_s`` seconds of
+    frames of the same workload (sampled frames when ``sampling`` is given)."""
+    from oracle import predictor as O
+    threads, host = host_cores()
     model = O.OracleModel(W, wl.geom)
     B = H.shape[1]
     n = 0
@@ -196,7 +206,7 @@ def cpu_baseline(wl, W, H, q0, budget_s: float, sampling=None, U=None):
         if el >= budget_s or n >= H.shape[0]:
             break
     return {"value": round(n * B / el, 3), "unit": "frames/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "host": host,
             "sample": f"{n} frame(s) of {B} request(s) of the {wl.name} workload"
                       f"{' (sampled)' if sampling else ''}, fp64 NumPy, {el:.1f} s"}
 
@@ -274,6 +284,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sample", default=None, metavar="T,K,P",
                     help="draw every token (temperature T, top-k K, top-p P) with seeded uniforms instead of the argmax")
+    ap.add_argument("--only", action="store_true",
+                    help="time the named workload alone (by default the b1 line also times b16 and b128)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (to scale HBM byte counters)")
     args = ap.parse_args()
@@ -296,7 +308,22 @@ def main():
     if args.workload in synth.TALKER_WORKLOADS:
         run_talker(args, torch, dev)
         return
-    wl = synth.WORKLOADS[args.workload]
+    line = measure(args.workload, args, torch, dev, bd)
+    if args.workload == "b1" and not args.only and not args.sample and not (args.stepwise or args.generic):
+        # the metric is quoted at B = 1, 16 and 128: the other two batch sizes
+        # are timed in the same run, each with its own roofline and oracle
+        line["workloads"] = {}
+        for name in ("b16", "b128"):
+            sub = measure(name, args, torch, dev, bd)
+            line["workloads"][name] = {k: sub[k] for k in ("value", "unit", "ms_per_step", "dtype", "config",
+                                                           "roofline", "cpu_baseline")}
+    print(json.dumps(line), flush=True)
+
+
+def measure(name, args, torch, dev, bd):
+    """Time one workload (frames of its batch, inputs resident on the GPU) and
+    return its JSON record."""
+    wl = synth.WORKLOADS[name]
     g = wl.geom
     B = wl.batch
     W = synth.make_weights(g, wl.weight_seed)
@@ -349,16 +376,30 @@ def main():
     table = driver in ("dataflow", "tiled") and has_qkv0_table(g)
     nbytes = algorithmic_bytes(g, B, qkv0_table=table)
     nflops = algorithmic_flops(g, B, qkv0_table=table)
+    # the unreduced model: every step streams layer 0's q/k/v weights too
+    nbytes_full = algorithmic_bytes(g, B, qkv0_table=False)
+    nflops_full = algorithmic_flops(g, B, qkv0_table=False)
+    # achieved: per call, over the mean event-pair duration around each call
+    # (the dataflow driver: exactly one kernel launch; the batched driver: the
+    # staging copies and the graph replay of the frame's kernels); the
+    # end-to-end fraction uses ms_per_step, gaps between calls included
+    scope = "one kernel launch" if driver in ("dataflow", "generic") else "one frame call (staging + graph replay)"
     if B >= 128:
         # throughput batch: graded against the bf16 matrix-core peak
         achieved = nflops / (launch_ms / 1e3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "frac_end_to_end": round(nflops / (ms_per_step / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "frac_unreduced_model": round(nflops_full / (launch_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "algorithmic_flops_unreduced": nflops_full, "per": scope}
     else:
         achieved_gbs = nbytes / (launch_ms / 1e3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-                    "traffic": measured_traffic(wl.name) if driver == "dataflow" else None}
+                    "traffic": measured_traffic(wl.name) if driver == "dataflow" else None,
+                    "frac_end_to_end": round(nbytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "frac_unreduced_model": round(nbytes_full / (launch_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "algorithmic_bytes_unreduced": nbytes_full, "per": scope}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -400,8 +441,10 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(line), flush=True)
+    # every launch has finished before the handle is destroyed
+    torch.cuda.synchronize()
     pred.close()
+    return line
 
 
 if __name__ == "__main__":

@@ -151,7 +151,9 @@ typedef struct qp_handle qp_handle;
  * failure returned as status), allocates every device buffer the later calls
  * need for up to max_batch requests (later calls never allocate), copies and
  * repacks the weights, computes EMA tables and the per-codebook projected
- * tables W_p . E_j + b_p.  For the 1.7B geometry with bf16, Q8_0 or Q4_0
+ * tables W_p . E_j + b_p.  Where the batched matrix-core path applies, it
+ * also captures and instantiates that path's frame graphs, one per batch
+ * bucket (greedy, and sampled for V <= 4096), kept until qp_destroy.  For the 1.7B geometry with bf16, Q8_0 or Q4_0
  * weights (the small-batch dataflow driver) it also computes layer 0's q/k/v
  * rows of every projected-table row of codebooks 1..14 (fp32, 14 x V x
  * (nq + 2 nkv) hd values, 470 MB), which that driver reads from step 2 on.
@@ -168,9 +170,11 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device,
  *                              summed in that order
  * Row b of the outputs depends only on (H[b], q0[b]).  An out-of-range q0 is
  * replaced by 0 and raises the sticky device flag (qp_get_error).
- * On the batched matrix-core path the frame replays a graph captured once
- * per batch size (the handle keeps the 4 most recent); the first call with
- * a new B captures and instantiates it before enqueueing. */
+ * On the batched matrix-core path the frame replays a graph that qp_create
+ * prepared for the smallest batch bucket holding B rows (buckets 1, 2, 4, 8,
+ * 16, 32, 48, 64, 96, 128, 192, ... below max_batch, and max_batch); the
+ * bucket's extra rows are computed on zero inputs and not returned.  No call
+ * captures, instantiates or frees a graph, and none allocates. */
 qp_status qp_run_frames(qp_handle* h, int32_t B, const float* H,
                         const int32_t* q0, int32_t* tokens_out,
                         float* embsum_out, void* stream);
@@ -236,7 +240,7 @@ typedef struct {
  * the logits.  Runs on the batched matrix-core path (its weight and geometry
  * conditions under QP_FLAG_TILED, and V <= 4096), else QP_ERR_INVALID_ARG;
  * invalid parameters give QP_ERR_INVALID_ARG.  Without hooks the frame
- * replays a captured graph, as qp_run_frames does. */
+ * replays the bucket's prepared graph, as qp_run_frames does. */
 qp_status qp_run_frames_sampled(qp_handle* h, int32_t B, const float* H,
                                 const int32_t* q0, const qp_sampling* sampling,
                                 const float* uniforms, int32_t* tokens_out,

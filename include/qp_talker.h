@@ -67,8 +67,9 @@ typedef struct {
 typedef struct qp_talker qp_talker;
 
 /* Validate, allocate everything later calls need (the KV cache: 2 x n_slots x
- * n_layers x n_kv_heads x max_ctx x head_dim bf16), repack the weights.  On
- * failure *out is NULL and nothing is leaked. */
+ * n_layers x n_kv_heads x max_ctx x head_dim bf16), repack the weights, and
+ * capture and instantiate the step graphs, one per batch bucket, kept until
+ * qp_talker_destroy.  On failure *out is NULL and nothing is leaked. */
 qp_status qp_talker_create(const qp_talker_weights* w, const qp_talker_geometry* g,
                            int32_t device, qp_talker** out);
 
@@ -95,9 +96,12 @@ qp_status qp_talker_load_history(qp_talker* t, int32_t slot, int32_t n,
  * when it lies beyond that grid), or whose slot is outside [0, n_slots),
  * raises the sticky device flag (qp_talker_get_error), writes nothing into
  * the cache and returns unspecified values.
- * Without logits_out the step replays a graph captured once per (B,
- * attention chunk, power-of-two split count); the handle keeps the 6 most
- * recent.  With logits_out the same kernels are launched directly. */
+ * Without logits_out the step replays a graph that qp_talker_create
+ * prepared for the smallest batch bucket holding B rows (buckets as for
+ * qp_run_frames); its attention grid covers max_ctx, and the call's B and
+ * max_len (the split limit above) are written to device memory before the
+ * replay.  With logits_out the same kernels are launched directly with a grid
+ * sized by max_len.  No step captures, instantiates or frees a graph. */
 qp_status qp_talker_step(qp_talker* t, int32_t B, const float* x, const int32_t* slots,
                          const int32_t* pos, int32_t max_len, float* H_out, int32_t* q0_out,
                          float* logits_out, void* stream);

@@ -114,6 +114,15 @@ __global__ void k_copy32(const uint32_t* __restrict__ src, uint32_t* __restrict_
         dst[i] = src[i];
 }
 
+// Staging of a call's rows into a prepared graph's buffers: the first n
+// words are copied, the rest up to n_total (the padding rows of the batch
+// bucket) are zeroed, so padded rows compute on valid inputs (H = 0, token 0).
+__global__ void k_stage32(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst, size_t n, size_t n_total) {
+    for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n_total;
+         i += static_cast<size_t>(gridDim.x) * blockDim.x)
+        dst[i] = i < n ? src[i] : 0u;
+}
+
 // 64-bit word fill (clearing the dataflow kernel's records)
 __global__ void k_fill64(uint64_t* __restrict__ dst, size_t n) {
     for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
@@ -252,17 +261,18 @@ struct qp_handle {
     size_t t_part_floats = 0;
     unsigned* t_ctr = nullptr;              // split-K tile counters
     size_t t_nctr = 0;
-    // one frame of the batched path captured as a graph per batch size,
-    // reading and writing handle-owned staging buffers
+    // one frame of the batched path captured as a graph per batch bucket
+    // (greedy, and sampled where the handle can sample), all built by
+    // qp_create and kept until qp_destroy; each reads and writes handle-owned
+    // staging buffers, and a call with B rows replays the smallest bucket
+    // that holds them, its extra rows zero-padded
     struct FrameGraph {
         int B = 0;
         bool sampled = false;
         hipGraph_t graph = nullptr;
         hipGraphExec_t exec = nullptr;
     };
-    static constexpr int kGraphs = 4;
-    FrameGraph graphs[kGraphs];
-    int graph_next = 0;
+    std::vector<FrameGraph> graphs;
     hipStream_t cap_stream = nullptr;
     float* st_H = nullptr;                  // [max_batch][dT]
     int* st_q0 = nullptr;                   // [max_batch]
@@ -517,6 +527,24 @@ qp_status validate_weights(const qp_weights* w, const qp_geometry* g) {
 void free_all(qp_handle* h) {
     for (void* p : h->allocs) (void)hipFree(p);
     h->allocs.clear();
+}
+
+// Wait for the device (no replay of the handle's graphs is in flight after
+// that), free the graphs, the capture stream and every buffer, and the handle.
+void destroy_handle(qp_handle* h) {
+    {
+        DeviceGuard guard(h->device);
+        (void)hipDeviceSynchronize();
+        for (auto& e : h->graphs) {
+            if (e.exec) (void)hipGraphExecDestroy(e.exec);
+            if (e.graph) (void)hipGraphDestroy(e.graph);
+        }
+        h->graphs.clear();
+        if (h->cap_stream) (void)hipStreamDestroy(h->cap_stream);
+        h->cap_stream = nullptr;
+        free_all(h);
+    }
+    delete h;
 }
 
 }  // namespace
@@ -794,60 +822,96 @@ void copy32(const void* src, void* dst, size_t words, hipStream_t stream) {
                        static_cast<uint32_t*>(dst), words);
 }
 
-// The batched path without test hooks: inputs are staged into handle-owned
-// buffers, the frame (about 400 kernels) replays as one graph captured once
-// per batch size, and the outputs are copied back.  Nothing in the graph
-// clears memory with a memset node: the split-K counters are left at zero by
-// the kernels themselves.
+// Row buckets of the prepared graphs: 1, 2, 4, 8, 16, 32, then 48, 64, 96,
+// 128, 192, 256, ... (alternately x1.5 and x4/3, so every bucket above 16 is
+// a whole number of 16-row tiles), those below max_batch, and max_batch.
+std::vector<int> batch_buckets(int max_batch) {
+    std::vector<int> b;
+    for (int v = 1; v < max_batch;) {
+        b.push_back(v);
+        if (v < 32) v *= 2;
+        else v = (v & (v - 1)) == 0 ? v + v / 2 : (v / 3) * 4;
+    }
+    b.push_back(max_batch);
+    return b;
+}
+
+void stage32(const void* src, void* dst, size_t words, size_t total, hipStream_t stream) {
+    const int blocks = static_cast<int>(std::min<size_t>((total + 255) / 256, 1024));
+    hipLaunchKernelGGL(k_stage32, dim3(blocks), dim3(256), 0, stream, static_cast<const uint32_t*>(src),
+                       static_cast<uint32_t*>(dst), words, total);
+}
+
+// Capture one frame of bucket Bk (greedy or sampled) on the handle's capture
+// stream and instantiate it; the graph reads and writes the staging buffers.
+// Nothing in it clears memory with a memset node: the split-K counters are
+// left at zero by the kernels themselves.
 template <int WT>
+qp_status capture_tiled_graph(qp_handle* h, int Bk, bool sampled) {
+    qp_status st = QP_OK;
+    RunArgs sa{};
+    sa.B = Bk;
+    sa.H = h->st_H;
+    sa.q0 = h->st_q0;
+    sa.tok_out = h->st_tok;
+    sa.embsum = h->st_emb;
+    sa.uniforms = sampled ? h->st_u : nullptr;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    if (!check_hip(hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture", &st))
+        return st;
+    const qp_status lst = launch_tiled<WT>(h, sa, h->cap_stream);
+    const hipError_t ce = hipStreamEndCapture(h->cap_stream, &graph);
+    if (lst != QP_OK) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return lst;
+    }
+    if (!check_hip(ce, "hipStreamEndCapture", &st)) return st;
+    if (!check_hip(hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0), "hipGraphInstantiate", &st)) {
+        (void)hipGraphDestroy(graph);
+        return st;
+    }
+    qp_handle::FrameGraph fg;
+    fg.B = Bk;
+    fg.sampled = sampled;
+    fg.graph = graph;
+    fg.exec = exec;
+    h->graphs.push_back(fg);
+    return QP_OK;
+}
+
+// All graphs of a handle (qp_create, after the tables are built).
+qp_status prepare_tiled_graphs(qp_handle* h) {
+    qp_status st = QP_OK;
+    if (!check_hip(hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking), "hipStreamCreate", &st)) return st;
+    for (int Bk : batch_buckets(h->m.max_batch)) {
+        for (int sampled = 0; sampled < (h->sample_ok ? 2 : 1); ++sampled) {
+            if (h->m.wt == WT_BF16) st = capture_tiled_graph<WT_BF16>(h, Bk, sampled != 0);
+            else if (h->q4) st = capture_tiled_graph<WT_Q4>(h, Bk, sampled != 0);
+            else st = capture_tiled_graph<WT_Q8>(h, Bk, sampled != 0);
+            if (st != QP_OK) return st;
+        }
+    }
+    return QP_OK;
+}
+
+// The batched path without test hooks: the call's inputs are staged into the
+// handle's buffers (rows past B up to the bucket zeroed), the bucket's
+// prepared graph replays the frame (about 400 kernels), and B rows of the
+// outputs are copied back.  Nothing is captured, instantiated or freed here.
 qp_status launch_tiled_graph(qp_handle* h, const RunArgs& a, hipStream_t stream) {
     qp_status st = QP_OK;
     const Model& m = h->m;
     const int B = a.B;
     const bool sampled = a.uniforms != nullptr;
-    copy32(a.H, h->st_H, static_cast<size_t>(B) * m.dT, stream);
-    copy32(a.q0, h->st_q0, static_cast<size_t>(B), stream);
-    if (sampled) copy32(a.uniforms, h->st_u, static_cast<size_t>(B) * kSteps, stream);
-    qp_handle::FrameGraph* fg = nullptr;
-    for (auto& e : h->graphs)
-        if (e.exec && e.B == B && e.sampled == sampled) fg = &e;
-    if (!fg) {
-        if (!h->cap_stream &&
-            !check_hip(hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking), "hipStreamCreate", &st))
-            return st;
-        RunArgs sa = a;
-        sa.H = h->st_H;
-        sa.q0 = h->st_q0;
-        sa.tok_out = h->st_tok;
-        sa.embsum = h->st_emb;
-        if (sampled) sa.uniforms = h->st_u;
-        fg = &h->graphs[h->graph_next];
-        h->graph_next = (h->graph_next + 1) % qp_handle::kGraphs;
-        if (fg->exec) {
-            (void)hipGraphExecDestroy(fg->exec);
-            (void)hipGraphDestroy(fg->graph);
-            *fg = qp_handle::FrameGraph{};
-        }
-        hipGraph_t graph = nullptr;
-        hipGraphExec_t exec = nullptr;
-        if (!check_hip(hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeRelaxed), "hipStreamBeginCapture", &st))
-            return st;
-        const qp_status lst = launch_tiled<WT>(h, sa, h->cap_stream);
-        const hipError_t ce = hipStreamEndCapture(h->cap_stream, &graph);
-        if (lst != QP_OK) {
-            if (graph) (void)hipGraphDestroy(graph);
-            return lst;
-        }
-        if (!check_hip(ce, "hipStreamEndCapture", &st)) return st;
-        if (!check_hip(hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0), "hipGraphInstantiate", &st)) {
-            (void)hipGraphDestroy(graph);
-            return st;
-        }
-        fg->B = B;
-        fg->sampled = sampled;
-        fg->graph = graph;
-        fg->exec = exec;
-    }
+    const qp_handle::FrameGraph* fg = nullptr;
+    for (const auto& e : h->graphs)
+        if (e.sampled == sampled && e.B >= B && (!fg || e.B < fg->B)) fg = &e;
+    if (!fg) return fail(QP_ERR_HIP, "no prepared graph for B=" + std::to_string(B));
+    const size_t Bk = static_cast<size_t>(fg->B);
+    stage32(a.H, h->st_H, static_cast<size_t>(B) * m.dT, Bk * m.dT, stream);
+    stage32(a.q0, h->st_q0, static_cast<size_t>(B), Bk, stream);
+    if (sampled) stage32(a.uniforms, h->st_u, static_cast<size_t>(B) * kSteps, Bk * kSteps, stream);
     if (!check_hip(hipGraphLaunch(fg->exec, stream), "hipGraphLaunch", &st)) return st;
     copy32(h->st_tok, a.tok_out, static_cast<size_t>(B) * kSteps, stream);
     copy32(h->st_emb, a.embsum, static_cast<size_t>(B) * m.dT, stream);
@@ -864,9 +928,9 @@ qp_status launch_frame(qp_handle* h, const RunArgs& a, hipStream_t stream, bool 
         // cannot take (Q8_0 and Q4_0 weights, other geometries)
         if (tiled || (!stepwise && !generic && h->tiled_ok && (a.B > 2 || !h->stream_ok))) {
             const bool hooks = a.force || a.logits_out || a.taps;
-            if (WT == WT_Q8 && h->q4)
-                return hooks ? launch_tiled<WT_Q4>(h, a, stream) : launch_tiled_graph<WT_Q4>(h, a, stream);
-            return hooks ? launch_tiled<WT>(h, a, stream) : launch_tiled_graph<WT>(h, a, stream);
+            if (!hooks) return launch_tiled_graph(h, a, stream);
+            if (WT == WT_Q8 && h->q4) return launch_tiled<WT_Q4>(h, a, stream);
+            return launch_tiled<WT>(h, a, stream);
         }
     }
     if constexpr (WT == WT_BF16 || WT == WT_Q8) {
@@ -1173,6 +1237,15 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
         delete h;
         return st;
     }
+    // every graph a later call can replay, built now so that no call
+    // captures, instantiates or frees one
+    if (h->tiled_ok) {
+        st = prepare_tiled_graphs(h);
+        if (st != QP_OK) {
+            destroy_handle(h);
+            return st;
+        }
+    }
     // testing only: the dataflow kernel's first record epoch, so that a test
     // reaches the tag-restart path without running 11 million frames first
     if (const char* e = std::getenv("QP_TEST_EPOCH0")) h->seq = static_cast<uint32_t>(std::strtoul(e, nullptr, 0));
@@ -1322,17 +1395,7 @@ uint32_t qp_last_device_flags(qp_handle* h) { return h ? h->last_flags : 0u; }
 
 void qp_destroy(qp_handle* h) {
     if (!h) return;
-    {
-        DeviceGuard guard(h->device);
-        (void)hipDeviceSynchronize();
-        for (auto& e : h->graphs) {
-            if (e.exec) (void)hipGraphExecDestroy(e.exec);
-            if (e.graph) (void)hipGraphDestroy(e.graph);
-        }
-        if (h->cap_stream) (void)hipStreamDestroy(h->cap_stream);
-        free_all(h);
-    }
-    delete h;
+    destroy_handle(h);
 }
 
 }  // extern "C"

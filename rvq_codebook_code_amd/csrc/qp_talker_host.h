@@ -43,18 +43,19 @@ struct qp_talker {
     size_t t_nctr = 0;
     unsigned* err = nullptr;
     unsigned last_flags = 0;
-    // a step without the logits hook replays a graph captured per (B, attention
-    // chunk, split count rounded up to a power of two), reading and writing
-    // handle-owned staging buffers
+    // a step without the logits hook replays a graph prepared by
+    // qp_talker_create for the smallest batch bucket that holds its rows
+    // (attention grid for max_ctx; the call's row count and split limit are
+    // read from st_live), reading and writing handle-owned staging buffers;
+    // the graphs are kept until qp_talker_destroy
     struct StepGraph {
-        int B = 0, ch = 0, nsplit = 0;
+        int B = 0;
         hipGraph_t graph = nullptr;
         hipGraphExec_t exec = nullptr;
     };
-    static constexpr int kGraphs = 6;
-    StepGraph graphs[kGraphs];
-    int graph_next = 0;
+    std::vector<StepGraph> graphs;
     hipStream_t cap_stream = nullptr;
+    int* st_live = nullptr;           // {split limit, rows} of the replayed call
     float* st_x = nullptr;            // [max_batch][d]
     int* st_slots = nullptr;          // [max_batch]
     int* st_pos = nullptr;            // [max_batch]
@@ -100,7 +101,8 @@ void talker_split(int max_len, int* ch_out, int* nsplit_out) {
 
 template <int WT>
 qp_status talker_launch(qp_talker* t, int B, const float* x, const int* slots, const int* pos, int ch, int nsplit,
-                        float* H_out, int* q0_out, float* logits_out, hipStream_t stream) {
+                        float* H_out, int* q0_out, float* logits_out, hipStream_t stream,
+                        const int* live = nullptr) {
     namespace T = qp::tiled;
     namespace K = qp::talker;
     const qp_talker_geometry& G = t->g;
@@ -133,6 +135,7 @@ qp_status talker_launch(qp_talker* t, int B, const float* x, const int* slots, c
     aa.ctr = t->actr;
     aa.ao = t->ao;
     aa.err = t->err;
+    aa.live = live;
     T::GemmArgs g{};
     for (int l = 0; l < L; ++l) {
         const qp_talker::Layer& Ly = t->layers[l];
@@ -232,50 +235,64 @@ qp_status talker_launch(qp_talker* t, int B, const float* x, const int* slots, c
     return QP_OK;
 }
 
+// Capture one step of batch bucket Bk (attention grid for max_ctx) and
+// instantiate it.
 template <int WT>
-qp_status talker_launch_graph(qp_talker* t, int B, const float* x, const int* slots, const int* pos, int ch,
-                              int nsplit, float* H_out, int* q0_out, hipStream_t stream) {
+qp_status talker_capture(qp_talker* t, int Bk) {
     qp_status st = QP_OK;
-    const int d = t->g.d_model;
-    copy32(x, t->st_x, static_cast<size_t>(B) * d, stream);
-    copy32(slots, t->st_slots, static_cast<size_t>(B), stream);
-    copy32(pos, t->st_pos, static_cast<size_t>(B), stream);
-    qp_talker::StepGraph* sg = nullptr;
-    for (auto& e : t->graphs)
-        if (e.exec && e.B == B && e.ch == ch && e.nsplit == nsplit) sg = &e;
-    if (!sg) {
-        if (!t->cap_stream &&
-            !check_hip(hipStreamCreateWithFlags(&t->cap_stream, hipStreamNonBlocking), "hipStreamCreate", &st))
-            return st;
-        sg = &t->graphs[t->graph_next];
-        t->graph_next = (t->graph_next + 1) % qp_talker::kGraphs;
-        if (sg->exec) {
-            (void)hipGraphExecDestroy(sg->exec);
-            (void)hipGraphDestroy(sg->graph);
-            *sg = qp_talker::StepGraph{};
-        }
-        hipGraph_t graph = nullptr;
-        hipGraphExec_t exec = nullptr;
-        if (!check_hip(hipStreamBeginCapture(t->cap_stream, hipStreamCaptureModeRelaxed), "hipStreamBeginCapture", &st))
-            return st;
-        const qp_status lst = talker_launch<WT>(t, B, t->st_x, t->st_slots, t->st_pos, ch, nsplit, t->st_H, t->st_q0,
-                                                nullptr, t->cap_stream);
-        const hipError_t ce = hipStreamEndCapture(t->cap_stream, &graph);
-        if (lst != QP_OK) {
-            if (graph) (void)hipGraphDestroy(graph);
-            return lst;
-        }
-        if (!check_hip(ce, "hipStreamEndCapture", &st)) return st;
-        if (!check_hip(hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0), "hipGraphInstantiate", &st)) {
-            (void)hipGraphDestroy(graph);
-            return st;
-        }
-        sg->B = B;
-        sg->ch = ch;
-        sg->nsplit = nsplit;
-        sg->graph = graph;
-        sg->exec = exec;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    if (!check_hip(hipStreamBeginCapture(t->cap_stream, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture", &st))
+        return st;
+    const qp_status lst = talker_launch<WT>(t, Bk, t->st_x, t->st_slots, t->st_pos, kTalkerCh, t->max_split, t->st_H,
+                                            t->st_q0, nullptr, t->cap_stream, t->st_live);
+    const hipError_t ce = hipStreamEndCapture(t->cap_stream, &graph);
+    if (lst != QP_OK) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return lst;
     }
+    if (!check_hip(ce, "hipStreamEndCapture", &st)) return st;
+    if (!check_hip(hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0), "hipGraphInstantiate", &st)) {
+        (void)hipGraphDestroy(graph);
+        return st;
+    }
+    qp_talker::StepGraph sg;
+    sg.B = Bk;
+    sg.graph = graph;
+    sg.exec = exec;
+    t->graphs.push_back(sg);
+    return QP_OK;
+}
+
+qp_status talker_prepare_graphs(qp_talker* t) {
+    qp_status st = QP_OK;
+    if (!check_hip(hipStreamCreateWithFlags(&t->cap_stream, hipStreamNonBlocking), "hipStreamCreate", &st)) return st;
+    for (int Bk : batch_buckets(t->g.max_batch)) {
+        switch (t->wt) {
+            case WT_BF16: st = talker_capture<WT_BF16>(t, Bk); break;
+            case WT_Q8: st = talker_capture<WT_Q8>(t, Bk); break;
+            default: st = talker_capture<WT_Q4>(t, Bk); break;
+        }
+        if (st != QP_OK) return st;
+    }
+    return QP_OK;
+}
+
+// A step without the logits hook: stage the call's rows (padding rows of the
+// bucket zeroed), write its limits, replay the bucket's prepared graph and
+// copy B rows of H and q0 back.  Nothing is captured or freed here.
+qp_status talker_launch_graph(qp_talker* t, int B, const float* x, const int* slots, const int* pos, int nsplit,
+                              float* H_out, int* q0_out, hipStream_t stream) {
+    qp_status st = QP_OK;
+    const qp_talker::StepGraph* sg = nullptr;
+    for (const auto& e : t->graphs)
+        if (e.B >= B && (!sg || e.B < sg->B)) sg = &e;
+    if (!sg) return fail(QP_ERR_HIP, "no prepared talker graph for B=" + std::to_string(B));
+    const size_t d = static_cast<size_t>(t->g.d_model), Bk = static_cast<size_t>(sg->B);
+    stage32(x, t->st_x, static_cast<size_t>(B) * d, Bk * d, stream);
+    stage32(slots, t->st_slots, static_cast<size_t>(B), Bk, stream);
+    stage32(pos, t->st_pos, static_cast<size_t>(B), Bk, stream);
+    hipLaunchKernelGGL(qp::talker::k_set_live, dim3(1), dim3(64), 0, stream, t->st_live, nsplit, B);
     if (!check_hip(hipGraphLaunch(sg->exec, stream), "hipGraphLaunch", &st)) return st;
     copy32(t->st_H, H_out, static_cast<size_t>(B) * d, stream);
     copy32(t->st_q0, q0_out, static_cast<size_t>(B), stream);
@@ -286,6 +303,24 @@ qp_status talker_launch_graph(qp_talker* t, int B, const float* x, const int* sl
 void talker_free(qp_talker* t) {
     for (void* p : t->allocs) (void)hipFree(p);
     t->allocs.clear();
+}
+
+// Wait for the device (no replay is in flight after that), then free the
+// graphs, the capture stream, every buffer and the handle.
+void talker_destroy(qp_talker* t) {
+    {
+        DeviceGuard guard(t->device);
+        (void)hipDeviceSynchronize();
+        for (auto& e : t->graphs) {
+            if (e.exec) (void)hipGraphExecDestroy(e.exec);
+            if (e.graph) (void)hipGraphDestroy(e.graph);
+        }
+        t->graphs.clear();
+        if (t->cap_stream) (void)hipStreamDestroy(t->cap_stream);
+        t->cap_stream = nullptr;
+        talker_free(t);
+    }
+    delete t;
 }
 
 }  // namespace
@@ -367,6 +402,7 @@ qp_status qp_talker_create(const qp_talker_weights* w, const qp_talker_geometry*
     t->st_pos = static_cast<int*>(up.alloc(mb * 4));
     t->st_H = static_cast<float*>(up.alloc(mb * d * 4));
     t->st_q0 = static_cast<int*>(up.alloc(mb * 4));
+    t->st_live = static_cast<int*>(up.alloc(2 * 4));
     if (up.st == QP_OK) {
         // counters start (and are left) at zero; the cache starts cleared
         if (!check_hip(hipMemset(t->actr, 0, mb * g->n_kv_heads * 4), "hipMemset", &st) ||
@@ -382,6 +418,13 @@ qp_status qp_talker_create(const qp_talker_weights* w, const qp_talker_geometry*
         talker_free(t);
         delete t;
         return s2;
+    }
+    // every graph a later step can replay, built now so that no step
+    // captures, instantiates or frees one
+    st = talker_prepare_graphs(t);
+    if (st != QP_OK) {
+        talker_destroy(t);
+        return st;
     }
     *out = t;
     return QP_OK;
@@ -421,11 +464,7 @@ qp_status qp_talker_step(qp_talker* t, int32_t B, const float* x, const int32_t*
             default: return talker_launch<WT_Q4>(t, B, x, slots, pos, ch, ns, H_out, q0_out, logits_out, s);
         }
     }
-    switch (t->wt) {
-        case WT_BF16: return talker_launch_graph<WT_BF16>(t, B, x, slots, pos, ch, ns, H_out, q0_out, s);
-        case WT_Q8: return talker_launch_graph<WT_Q8>(t, B, x, slots, pos, ch, ns, H_out, q0_out, s);
-        default: return talker_launch_graph<WT_Q4>(t, B, x, slots, pos, ch, ns, H_out, q0_out, s);
-    }
+    return talker_launch_graph(t, B, x, slots, pos, ns, H_out, q0_out, s);
 }
 
 qp_status qp_talker_get_error(qp_talker* t) {
@@ -447,17 +486,7 @@ uint32_t qp_talker_last_device_flags(qp_talker* t) { return t ? t->last_flags : 
 
 void qp_talker_destroy(qp_talker* t) {
     if (!t) return;
-    {
-        DeviceGuard guard(t->device);
-        (void)hipDeviceSynchronize();
-        for (auto& e : t->graphs) {
-            if (e.exec) (void)hipGraphExecDestroy(e.exec);
-            if (e.graph) (void)hipGraphDestroy(e.graph);
-        }
-        if (t->cap_stream) (void)hipStreamDestroy(t->cap_stream);
-        talker_free(t);
-    }
-    delete t;
+    talker_destroy(t);
 }
 
 }  // extern "C"

@@ -97,7 +97,18 @@ struct AttnArgs {
     unsigned* ctr;                    // [B][nkv] arrival counters, left at 0
     uint16_t* ao;                     // [B][qd] bf16 attention output
     unsigned* err;
+    // prepared graphs (grid for max_ctx and a batch bucket): null, or the
+    // call's limits written before the replay, {splits the call's max_len
+    // covers, rows B}; rows at or past B are padding and exit at once
+    const int* live;
 };
+
+__global__ void k_set_live(int* live, int nsplit, int B) {
+    if (threadIdx.x == 0) {
+        live[0] = nsplit;
+        live[1] = B;
+    }
+}
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
@@ -119,11 +130,16 @@ __global__ __launch_bounds__(kThreadsK) void k_attn(AttnArgs a) {
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int lim = a.nsplit;                  // splits the call's max_len covers
+    if (a.live) {
+        if (b >= a.live[1]) return;      // a padding row of the batch bucket
+        lim = a.live[0];
+    }
     int p = a.pos[b], slot = a.slots[b];
     // a row with a position or slot out of range raises the flag, is computed
     // at position 0 of slot 0 and writes nothing into the cache
     bool valid = true;
-    if (p < 0 || p >= a.nsplit * a.ch || p >= a.max_ctx) {
+    if (p < 0 || p >= lim * a.ch || p >= a.max_ctx) {
         if (s == 0 && g == 0 && threadIdx.x == 0) atomicOr(a.err, kErrBadPos);
         p = 0;
         valid = false;

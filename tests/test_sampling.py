@@ -178,6 +178,20 @@ def _check_draws(logits, uniforms, got, T, K, P, label):
     return amb
 
 
+# How many draws may be ambiguous.  Which draws are ambiguous depends only on
+# the fp32 logits the oracle evaluates them on (the host's logits in the
+# sampler tests, the GPU's own logits in the frame tests) and on the
+# uniforms, never on the sampler under test: the count cannot catch a sampler
+# error, which the exact comparison of the unique draws and the validity
+# check of the others do.  It guards that the comparison is not vacuous: at
+# least nine draws in ten must be compared exactly.  (Inputs with exact ties
+# make some draws ambiguous by construction: integer-rounded logits at a low
+# temperature put the top-p cut of 0.5 exactly on a boundary between two tied
+# tokens.)
+def non_vacuity_cap(n_draws):
+    return n_draws // 10
+
+
 PARAMS = [(1.0, 0, 1.0), (0.7, 50, 0.9), (1.3, 0, 0.6), (0.5, 1, 1.0), (2.0, 3000, 0.95), (0.05, 0, 0.5)]
 
 
@@ -202,9 +216,10 @@ def test_gpu_sampler_against_oracle(V):
         torch.cuda.synchronize()
         got = out.cpu().numpy()
         assert ((got >= 0) & (got < V)).all()
-        total_amb += _check_draws(z, u, got, T, K, P, f"V={V} T={T} K={K} P={P}")
-    print(f"[sampler V={V}] ambiguous draws {total_amb} of {rows * len(PARAMS)}")
-    assert total_amb <= rows * len(PARAMS) // 10     # most draws are compared exactly
+        amb = _check_draws(z, u, got, T, K, P, f"V={V} T={T} K={K} P={P}")
+        print(f"[sampler V={V} T={T} K={K} P={P}] ambiguous draws {amb} of {rows}")
+        total_amb += amb
+    assert total_amb <= non_vacuity_cap(rows * len(PARAMS))
 
 
 @pytest.mark.gpu
@@ -369,4 +384,4 @@ def test_sampled_full_size_rows():
     amb = _check_draws(got["logits"].reshape(-1, wl.geom.vocab), U.reshape(-1), got["tokens"].reshape(-1),
                        T, K, P, "b16")
     print(f"[sampled b16] ambiguous draws {amb} of {got['tokens'].size}")
-    assert amb <= got["tokens"].size // 10     # most draws are compared exactly
+    assert amb <= non_vacuity_cap(got["tokens"].size)
