@@ -179,6 +179,28 @@ qp_status qp_run_frames(qp_handle* h, int32_t B, const float* H,
                         const int32_t* q0, int32_t* tokens_out,
                         float* embsum_out, void* stream);
 
+/* qp_run_frames for callers that cannot allocate device memory or must not
+ * touch a handle's scratch between calls (code under stream capture, tight
+ * serving loops, harnesses that forbid allocation): the same frame, on the
+ * small-batch dataflow driver, with that driver's scratch (its exchange
+ * records and a two-request KV cache, 1,646,592 bytes) in a static device
+ * array that each GPU holds until the process ends, set up by the first
+ * qp_create of a dataflow-capable handle on that GPU.  The call allocates
+ * nothing and frees nothing.
+ *   - Only handles of the 1.7B predictor geometry with bf16, Q8_0 or Q4_0
+ *     weights (the dataflow driver), else QP_ERR_INVALID_ARG.
+ *   - 0 <= B <= min(2, max_batch), else QP_ERR_BATCH (the static array holds
+ *     two requests); B = 0 is a no-op.
+ *   - Arguments, outputs, results and the sticky device flag are those of
+ *     qp_run_frames; results equal qp_run_frames' bit for bit.
+ *   - Every call on one GPU, from any handle, shares that GPU's array: calls
+ *     that overlap on one GPU (on different streams, or from different
+ *     threads without ordering) race and give wrong results.  Calls ordered
+ *     on one stream are safe. */
+qp_status qp_run_frames_noalloc(qp_handle* h, int32_t B, const float* H,
+                                const int32_t* q0, int32_t* tokens_out,
+                                float* embsum_out, void* stream);
+
 /* Execution strategy hints for qp_run_frames_ex `flags`. */
 #define QP_FLAG_STEPWISE 0x1u   /* one kernel per phase (no persistent kernel) */
 #define QP_FLAG_GENERIC 0x2u    /* the generic persistent kernel even where a

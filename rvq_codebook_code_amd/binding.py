@@ -38,8 +38,9 @@ QP_FLAG_TILED = 0x4
 WEIGHT_DTYPES = {"f32": 0, "bf16": 1, "q8_0": 2, "q4_0": 3}
 EMB_FORMATS = {"f32": 0, "bf16": 1, "ema": 2}
 
-EXPORTED = ["qp_create", "qp_run_frames", "qp_run_frames_ex", "qp_run_frames_sampled", "qp_sample_logits",
-            "qp_get_error", "qp_last_device_flags", "qp_destroy", "qp_status_string", "qp_last_error"]
+EXPORTED = ["qp_create", "qp_run_frames", "qp_run_frames_ex", "qp_run_frames_noalloc", "qp_run_frames_sampled",
+            "qp_sample_logits", "qp_get_error", "qp_last_device_flags", "qp_destroy", "qp_status_string",
+            "qp_last_error"]
 # include/qp_talker.h
 EXPORTED_TALKER = ["qp_talker_create", "qp_talker_load_history", "qp_talker_step", "qp_talker_get_error",
                    "qp_talker_last_device_flags", "qp_talker_destroy"]
@@ -110,6 +111,8 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     lib.qp_run_frames.restype = i32
     lib.qp_run_frames_ex.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, u32]
     lib.qp_run_frames_ex.restype = i32
+    lib.qp_run_frames_noalloc.argtypes = [vp, i32, vp, vp, vp, vp, vp]
+    lib.qp_run_frames_noalloc.restype = i32
     lib.qp_run_frames_sampled.argtypes = [vp, i32, vp, vp, C.POINTER(QpSampling), vp, vp, vp, vp, vp, vp]
     lib.qp_run_frames_sampled.restype = i32
     lib.qp_sample_logits.argtypes = [vp, i32, i32, C.c_int64, C.POINTER(QpSampling), vp, i32, vp, vp]
@@ -239,6 +242,23 @@ class Predictor:
                                            _dptr(embsum_out), stream, _dptr(force), _dptr(logits_out),
                                            _dptr(taps_out), flags)
         _check(self.lib, st, "qp_run_frames")
+
+    def run_noalloc(self, H, q0, tokens_out, embsum_out, stream=None):
+        """Enqueue one frame through qp_run_frames_noalloc (static device
+        scratch; B <= 2 on the dataflow driver)."""
+        import torch
+        B = H.shape[0]
+        for t in (H, q0, tokens_out, embsum_out):
+            assert t.is_cuda and t.is_contiguous()
+        assert H.dtype == torch.float32 and q0.dtype == torch.int32
+        assert tokens_out.dtype == torch.int32 and embsum_out.dtype == torch.float32
+        assert tuple(H.shape) == (B, self.geom.d_talker) and tuple(q0.shape) == (B,)
+        assert tuple(tokens_out.shape) == (B, N_STEPS) and tuple(embsum_out.shape) == (B, self.geom.d_talker)
+        if stream is None:
+            stream = torch.cuda.current_stream(H.device).cuda_stream
+        st = self.lib.qp_run_frames_noalloc(self.h, B, _dptr(H), _dptr(q0), _dptr(tokens_out), _dptr(embsum_out),
+                                            stream)
+        _check(self.lib, st, "qp_run_frames_noalloc")
 
     def run_sampled(self, H, q0, uniforms, tokens_out, embsum_out, temperature: float, top_k: int = 0,
                     top_p: float = 1.0, force=None, logits_out=None, stream=None):

@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -232,6 +233,28 @@ __global__ __launch_bounds__(256) void k_qkv0(Model m, const float* g, float* Q0
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// static scratch of qp_run_frames_noalloc
+// ---------------------------------------------------------------------------
+
+namespace noalloc {
+namespace S = qp::stream;
+constexpr int kMaxB = 2;                         // requests the scratch holds
+// the dataflow kernel's records (two rows per request) ...
+constexpr size_t kRecs = static_cast<size_t>(2 * kMaxB) * (S::DP + S::NQKV + S::QD + S::F) +
+                         2ull * S::kNwg * kMaxB;
+// ... and its KV cache, [kMaxL][kMaxB][16][NKV][HD] fp32 for keys, then values
+constexpr size_t kKV = static_cast<size_t>(S::kMaxL) * kMaxB * kPositions * S::NKV * S::HD;
+constexpr size_t kBytes = kRecs * 8 + 2 * kKV * 4;   // 1,646,592 B
+static_assert(kRecs * 8 % 256 == 0 && kKV * 4 % 256 == 0, "256-byte aligned parts");
+constexpr int kDevices = 64;
+}  // namespace noalloc
+
+// One copy per GPU, held until the process ends.  In host code this name is a
+// stand-in, not a device address: host code uses the address that
+// hipGetSymbolAddress returns for the current device (noalloc_dev below).
+static __device__ __align__(256) unsigned char scratch[noalloc::kBytes];
 
 // ---------------------------------------------------------------------------
 // host side
@@ -527,6 +550,38 @@ qp_status validate_weights(const qp_weights* w, const qp_geometry* g) {
 void free_all(qp_handle* h) {
     for (void* p : h->allocs) (void)hipFree(p);
     h->allocs.clear();
+}
+
+// Per-device state of the static scratch: its device address (from
+// hipGetSymbolAddress with that device current), and the next record tag of
+// the dataflow frames that run on it (shared by every call on the device, so
+// no stale record can carry a current tag).
+struct NoallocDev {
+    uint64_t* base = nullptr;
+    uint32_t seq = 0;
+};
+std::mutex g_noalloc_mu;
+NoallocDev g_noalloc[noalloc::kDevices];
+
+// Once per device, with the device current (qp_create): look up the scratch's
+// address and clear its records (tag 0 is never current; the KV part needs no
+// clearing, a frame writes every position before reading it).
+qp_status noalloc_setup(int device) {
+    std::lock_guard<std::mutex> lock(g_noalloc_mu);
+    if (device < 0 || device >= noalloc::kDevices) return QP_OK;   // the entry point rejects such devices
+    NoallocDev& d = g_noalloc[device];
+    if (d.base) return QP_OK;
+    void* ptr = nullptr;
+    qp_status st = QP_OK;
+    if (!check_hip(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress (static scratch)", &st))
+        return st;
+    hipLaunchKernelGGL(k_fill64, dim3(64), dim3(256), 0, 0, static_cast<uint64_t*>(ptr), noalloc::kRecs);
+    if (!check_hip(hipGetLastError(), "static scratch clear", &st) ||
+        !check_hip(hipDeviceSynchronize(), "static scratch clear", &st))
+        return st;
+    d.base = static_cast<uint64_t*>(ptr);
+    d.seq = 0;
+    return QP_OK;
 }
 
 // Wait for the device (no replay of the handle's graphs is in flight after
@@ -1237,6 +1292,14 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
         delete h;
         return st;
     }
+    // the static scratch of qp_run_frames_noalloc on this device
+    if (h->stream_ok) {
+        st = noalloc_setup(device);
+        if (st != QP_OK) {
+            destroy_handle(h);
+            return st;
+        }
+    }
     // every graph a later call can replay, built now so that no call
     // captures, instantiates or frees one
     if (h->tiled_ok) {
@@ -1292,6 +1355,75 @@ qp_status qp_run_frames_ex(qp_handle* h, int32_t B, const float* H, const int32_
 qp_status qp_run_frames(qp_handle* h, int32_t B, const float* H, const int32_t* q0, int32_t* tokens_out,
                         float* embsum_out, void* stream) {
     return qp_run_frames_ex(h, B, H, q0, tokens_out, embsum_out, stream, nullptr, nullptr, nullptr, 0u);
+}
+
+qp_status qp_run_frames_noalloc(qp_handle* h, int32_t B, const float* H, const int32_t* q0, int32_t* tokens_out,
+                                float* embsum_out, void* stream) {
+    namespace S = qp::stream;
+    if (!h) return fail(QP_ERR_INVALID_ARG, "handle is NULL");
+    if (!h->stream_ok)
+        return fail(QP_ERR_INVALID_ARG,
+                    "the allocation-free entry point runs the small-batch dataflow kernel: the 1.7B predictor "
+                    "geometry with bf16, Q8_0 or Q4_0 weights only");
+    const int bmax = std::min(noalloc::kMaxB, h->m.max_batch);
+    if (B < 0 || B > bmax)
+        return fail(QP_ERR_BATCH, "B=" + std::to_string(B) + " outside [0, " + std::to_string(bmax) +
+                                      "]: the static scratch holds " + std::to_string(noalloc::kMaxB) +
+                                      " requests (and B may not exceed max_batch)");
+    if (B == 0) return QP_OK;
+    if (!H || !q0 || !tokens_out || !embsum_out) return fail(QP_ERR_INVALID_ARG, "NULL input or output pointer");
+    if (h->device >= noalloc::kDevices) return fail(QP_ERR_INVALID_ARG, "device index beyond the static scratch table");
+    DeviceGuard guard(h->device);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    qp_status st = QP_OK;
+    const uint32_t ppf = static_cast<uint32_t>(S::phases_per_frame(h->m.L));
+    uint64_t* base = nullptr;
+    uint32_t seq0 = 0;
+    {
+        std::lock_guard<std::mutex> lock(g_noalloc_mu);
+        NoallocDev& d = g_noalloc[h->device];
+        if (!d.base) return fail(QP_ERR_HIP, "the static scratch of this device was not set up");
+        if (d.seq > 0xFFFFFFFFu - 2u * ppf) {
+            // the 32-bit tags would wrap: clear the records, restart the tags
+            hipLaunchKernelGGL(k_fill64, dim3(64), dim3(256), 0, s, d.base, noalloc::kRecs);
+            if (!check_hip(hipGetLastError(), "static scratch clear", &st)) return st;
+            d.seq = 0;
+        }
+        base = d.base;
+        seq0 = d.seq;
+        d.seq += ppf;
+    }
+    // the kernel's records and KV cache in the static scratch (the records'
+    // row stride is the kernel's 4 rows; the KV cache holds 2 requests)
+    S::Recs rc{};
+    rc.X = base;
+    rc.QKV = rc.X + 4 * S::DP;
+    rc.AO = rc.QKV + 4 * S::NQKV;
+    rc.H = rc.AO + 4 * S::QD;
+    rc.KEY = rc.H + 4 * S::F;
+    Model mm = h->m;
+    mm.kc = reinterpret_cast<float*>(base + noalloc::kRecs);
+    mm.vc = mm.kc + noalloc::kKV;
+    mm.max_batch = noalloc::kMaxB;
+    RunArgs ra{};
+    ra.B = B;
+    ra.H = H;
+    ra.q0 = q0;
+    ra.tok_out = tokens_out;
+    ra.embsum = embsum_out;
+    ra.seq0 = seq0;
+    void* args[] = {&mm, &ra, &rc};
+    const void* fn;
+    if (h->m.wt == WT_BF16)
+        fn = B == 1 ? reinterpret_cast<const void*>(&S::k_stream<2, WT_BF16>)
+                    : reinterpret_cast<const void*>(&S::k_stream<4, WT_BF16>);
+    else
+        fn = B == 1 ? reinterpret_cast<const void*>(&S::k_stream<2, WT_Q8>)
+                    : reinterpret_cast<const void*>(&S::k_stream<4, WT_Q8>);
+    if (!check_hip(hipLaunchCooperativeKernel(fn, dim3(S::kNwg), dim3(S::kThreadsS), args, 0, s),
+                   "cooperative launch (dataflow kernel, static scratch)", &st))
+        return st;
+    return QP_OK;
 }
 
 namespace {
