@@ -227,6 +227,8 @@ def select_driver(g, B: int, args) -> str:
         return "generic"
     if B <= 2 and has_qkv0_table(g):
         return "dataflow"
+    if B <= 16 and has_qkv0_table(g) and g.weight_dtype == "bf16":
+        return "flow"
     qd = g.n_q_heads * g.head_dim
     nqkv = (g.n_q_heads + 2 * g.n_kv_heads) * g.head_dim
     if (g.weight_dtype in ("bf16", "q8_0", "q4_0") and g.d_talker % 256 == 0 and g.d_model % 256 == 0 and g.d_model <= 4096 and g.d_talker <= 4096 and
@@ -259,6 +261,24 @@ def measured_traffic(workload: str):
     return int(kv["traffic_bytes_per_launch"])
 
 
+def mfma_peak():
+    """The measured dense bf16 matrix-core rate of this GPU (the probe in
+    libqp_probe.so: back-to-back v_mfma_f32_16x16x32_bf16 in every wave of 4
+    workgroups per compute unit), TFLOP/s, or None if the probe is missing."""
+    import ctypes as C
+    path = os.path.join(ROOT, "rvq_codebook_code_amd", "libqp_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = C.CDLL(path)
+    lib.qp_probe_mfma_bf16.argtypes = [C.c_int, C.c_int, C.c_int, C.POINTER(C.c_float), C.POINTER(C.c_double)]
+    lib.qp_probe_mfma_bf16.restype = C.c_int
+    ms, tf = C.c_float(), C.c_double()
+    rc = lib.qp_probe_mfma_bf16(4, 20000, 5, C.byref(ms), C.byref(tf))
+    if rc != 0:
+        raise RuntimeError(f"matrix-core probe failed (HIP error {rc})")
+    return round(tf.value, 1)
+
+
 def calibrate_copy(torch, dev):
     """A plain copy of COPY_BYTES, five times: the reference for scaling the
     FETCH_SIZE / WRITE_SIZE counters (each launch reads and writes exactly
@@ -284,6 +304,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sample", default=None, metavar="T,K,P",
                     help="draw every token (temperature T, top-k K, top-p P) with seeded uniforms instead of the argmax")
+    ap.add_argument("--batch", type=int, default=None,
+                    help="run the workload's weights at this batch size instead of its own (crossover sweeps)")
+    ap.add_argument("--flush-mib", type=int, default=0,
+                    help="before every timed frame copy this many MiB (evicting the MALL); the frame alone is timed")
+    ap.add_argument("--mfma-peak", action="store_true", help="only run the matrix-core peak probe")
     ap.add_argument("--only", action="store_true",
                     help="time the named workload alone (by default the b1 line also times b16 and b128)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -305,11 +330,16 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(torch, dev)
         return
+    if args.mfma_peak:
+        print(json.dumps({"mfma_peak_bf16_tflops": mfma_peak(), "vendor_dense_bf16_tflops": MFMA_BF16_PEAK_TFLOPS}),
+              flush=True)
+        return
     if args.workload in synth.TALKER_WORKLOADS:
         run_talker(args, torch, dev)
         return
     line = measure(args.workload, args, torch, dev, bd)
-    if args.workload == "b1" and not args.only and not args.sample and not (args.stepwise or args.generic):
+    if (args.workload == "b1" and not args.only and not args.sample and not (args.stepwise or args.generic)
+            and args.batch is None and not args.flush_mib):
         # the metric is quoted at B = 1, 16 and 128: the other two batch sizes
         # are timed in the same run, each with its own roofline and oracle
         line["workloads"] = {}
@@ -317,6 +347,13 @@ def main():
             sub = measure(name, args, torch, dev, bd)
             line["workloads"][name] = {k: sub[k] for k in ("value", "unit", "ms_per_step", "dtype", "config",
                                                            "roofline", "cpu_baseline")}
+        # the B = 128 line is graded on the matrix cores: also against this
+        # GPU's measured peak of the instruction the products use
+        peak = mfma_peak()
+        if peak:
+            rf = line["workloads"]["b128"]["roofline"]
+            rf["peak_measured"] = peak
+            rf["frac_of_measured_peak"] = round(rf["achieved"] / peak, 4)
     print(json.dumps(line), flush=True)
 
 
@@ -325,7 +362,7 @@ def measure(name, args, torch, dev, bd):
     return its JSON record."""
     wl = synth.WORKLOADS[name]
     g = wl.geom
-    B = wl.batch
+    B = wl.batch if args.batch is None else args.batch
     W = synth.make_weights(g, wl.weight_seed)
     H, q0 = synth.make_inputs(g, B, wl.frames, wl.input_seed)
     pred = bd.Predictor(W, g, max_batch=B)
@@ -357,8 +394,14 @@ def measure(name, args, torch, dev, bd):
     # one event pair per frame call, on the stream the library launches on:
     # for the single-kernel drivers that brackets exactly one kernel launch
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    flush = None
+    if args.flush_mib:
+        flush = (torch.empty(args.flush_mib << 18, dtype=torch.float32, device=dev).uniform_(),
+                 torch.empty(args.flush_mib << 18, dtype=torch.float32, device=dev))
     torch.cuda.synchronize()
     for i in range(args.steps):
+        if flush is not None:
+            flush[1].copy_(flush[0])      # evicts the frame's weights from the MALL
         ev[i][0].record(stream)
         frame(i)
         ev[i][1].record(stream)
@@ -367,13 +410,16 @@ def measure(name, args, torch, dev, bd):
     launch_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
     if pred.get_error() != 0:
         raise RuntimeError("device flag raised during the timed frames")
+    if flush is not None:
+        # the copies sit between the frames: only the frames are timed
+        ms = launch_ms * args.steps
     ms_per_step = ms / args.steps
     frames_per_s = B * args.steps / (ms / 1e3)
 
     driver = select_driver(g, B, args)
     # the dataflow and batched drivers read layer 0's q/k/v rows of steps
     # 2..15 from the create-time table
-    table = driver in ("dataflow", "tiled") and has_qkv0_table(g)
+    table = driver in ("dataflow", "flow", "tiled") and has_qkv0_table(g)
     nbytes = algorithmic_bytes(g, B, qkv0_table=table)
     nflops = algorithmic_flops(g, B, qkv0_table=table)
     # the unreduced model: every step streams layer 0's q/k/v weights too
@@ -383,7 +429,7 @@ def measure(name, args, torch, dev, bd):
     # (the dataflow driver: exactly one kernel launch; the batched driver: the
     # staging copies and the graph replay of the frame's kernels); the
     # end-to-end fraction uses ms_per_step, gaps between calls included
-    scope = "one kernel launch" if driver in ("dataflow", "generic") else "one frame call (staging + graph replay)"
+    scope = "one kernel launch" if driver in ("dataflow", "flow", "generic") else "one frame call (staging + graph replay)"
     if B >= 128:
         # throughput batch: graded against the bf16 matrix-core peak
         achieved = nflops / (launch_ms / 1e3) / 1e12
@@ -396,7 +442,8 @@ def measure(name, args, torch, dev, bd):
         achieved_gbs = nbytes / (launch_ms / 1e3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-                    "traffic": measured_traffic(wl.name) if driver == "dataflow" else None,
+                    "traffic": (measured_traffic(wl.name)
+                                if driver == "dataflow" and B == wl.batch and not args.flush_mib else None),
                     "frac_end_to_end": round(nbytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                     "frac_unreduced_model": round(nbytes_full / (launch_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                     "algorithmic_bytes_unreduced": nbytes_full, "per": scope}
@@ -409,7 +456,7 @@ def measure(name, args, torch, dev, bd):
     # on the matrix cores and in the dataflow kernel with bf16 weights; the
     # dataflow kernel multiplies Q8_0 / Q4_0 codes with fp32 activations, and
     # the generic path computes in fp32
-    if driver == "tiled" or (driver == "dataflow" and g.weight_dtype == "bf16"):
+    if driver in ("tiled", "flow") or (driver == "dataflow" and g.weight_dtype == "bf16"):
         dtype = "bf16"
     else:
         dtype = "f32"
@@ -426,7 +473,8 @@ def measure(name, args, torch, dev, bd):
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": wl.name, "batch": B, "frames_per_step": 1,
+        "config": {"workload": wl.name if args.batch is None else f"{wl.name} weights at B={B}", "batch": B,
+                   "frames_per_step": 1, "mall_flush_mib_before_each_frame": args.flush_mib or None,
                    "weights": g.weight_dtype, "embeddings": g.emb_format,
                    "predictor": f"dP={g.d_model} L={g.n_layers} heads={g.n_q_heads}/{g.n_kv_heads}x{g.head_dim} "
                                 f"F={g.d_ffn} V={g.vocab} dT={g.d_talker}",

@@ -28,9 +28,10 @@
  *     variable QP_LOG is set; then each failure also writes that text and the
  *     status name to stderr, one line per failure.
  *   - For tests only: QP_TEST_EPOCH0, if set when qp_create runs, is the first
- *     32-bit record tag of the new handle's small-batch dataflow frames (the
- *     tags restart, after every record is cleared, before they would wrap; a
- *     test sets it near that point).  Results do not depend on it.
+ *     32-bit record tag of the new handle's dataflow frames (small and
+ *     moderate batches; the tags restart, after every record is cleared,
+ *     before they would wrap; a test sets it near that point).  Results do
+ *     not depend on it.
  *   - Weight pointers given to qp_create are HOST pointers; the library copies
  *     and repacks everything before returning, so the caller keeps ownership
  *     and may free them afterwards.
@@ -210,10 +211,16 @@ qp_status qp_run_frames_noalloc(qp_handle* h, int32_t B, const float* H,
                                    for bf16, Q8_0 or Q4_0 weights with dT, dP, nq*hd
                                    and F multiples of 256, dP and dT <= 4096, nqkv and V multiples
                                    of 32 (else QP_ERR_INVALID_ARG); excludes
+                                   the other flags                            */
+#define QP_FLAG_FLOW 0x8u       /* the moderate-batch dataflow kernel (1.7B
+                                   predictor geometry with bf16 weights,
+                                   B <= 16, else QP_ERR_INVALID_ARG); excludes
                                    the other flags.
    Without flags the library picks: B <= 2 with bf16, Q8_0 or Q4_0 weights
-   and the 1.7B predictor geometry -> the dataflow kernel; otherwise, where
-   the batched path applies -> it; otherwise the generic persistent kernel. */
+   and the 1.7B predictor geometry -> the small-batch dataflow kernel;
+   3 <= B <= 16 with bf16 weights and that geometry -> the moderate-batch
+   dataflow kernel (matrix-core products); otherwise, where the batched path
+   applies -> it; otherwise the generic persistent kernel. */
 
 /* Same computation with test hooks (any hook may be NULL):
  *   force_tokens int32 [B, 15]  teacher forcing: the token fed back at step

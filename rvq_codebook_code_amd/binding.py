@@ -34,6 +34,7 @@ QP_ERR_DEVICE_FLAG = -8
 QP_FLAG_STEPWISE = 0x1
 QP_FLAG_GENERIC = 0x2
 QP_FLAG_TILED = 0x4
+QP_FLAG_FLOW = 0x8
 
 WEIGHT_DTYPES = {"f32": 0, "bf16": 1, "q8_0": 2, "q4_0": 3}
 EMB_FORMATS = {"f32": 0, "bf16": 1, "ema": 2}
@@ -212,7 +213,7 @@ class Predictor:
         self.h = h
 
     def run(self, H, q0, tokens_out, embsum_out, force=None, logits_out=None, taps_out=None,
-            stepwise: bool = False, generic: bool = False, tiled: bool = False, stream=None):
+            stepwise: bool = False, generic: bool = False, tiled: bool = False, flow: bool = False, stream=None):
         """Enqueue one frame on ``stream`` (default: torch's current stream)."""
         import torch
         B = H.shape[0]
@@ -233,7 +234,7 @@ class Predictor:
         if stream is None:
             stream = torch.cuda.current_stream(H.device).cuda_stream
         flags = ((QP_FLAG_STEPWISE if stepwise else 0) | (QP_FLAG_GENERIC if generic else 0) |
-                 (QP_FLAG_TILED if tiled else 0))
+                 (QP_FLAG_TILED if tiled else 0) | (QP_FLAG_FLOW if flow else 0))
         if force is None and logits_out is None and taps_out is None and flags == 0:
             st = self.lib.qp_run_frames(self.h, B, _dptr(H), _dptr(q0), _dptr(tokens_out),
                                         _dptr(embsum_out), stream)

@@ -1,8 +1,9 @@
 """Compile the HIP library in-tree for gfx950.
 
 ``python -m rvq_codebook_code_amd.build`` (or ``build()``) runs hipcc on
-``csrc/qp.hip`` and writes ``rvq_codebook_code_amd/libqp.so``.  hipcc
-cross-compiles without a GPU.
+``csrc/qp.hip`` and writes ``rvq_codebook_code_amd/libqp.so``, and on
+``csrc/probe_mfma.hip`` (the matrix-core peak probe bench.py can run) for
+``libqp_probe.so``.  hipcc cross-compiles without a GPU.
 """
 from __future__ import annotations
 
@@ -38,9 +39,11 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm toolchain required to build the library)")
 
 
-def build(verbose: bool = False) -> str:
-    src = os.path.join(CSRC, "qp.hip")
-    tmp = LIB + ".tmp"
+PROBE_LIB = os.path.join(PKG, "libqp_probe.so")
+
+
+def _hipcc(src: str, out: str, verbose: bool) -> None:
+    tmp = out + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", src, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -48,7 +51,13 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """The library (libqp.so) and the matrix-core peak probe (libqp_probe.so)."""
+    _hipcc(os.path.join(CSRC, "qp.hip"), LIB, verbose)
+    _hipcc(os.path.join(CSRC, "probe_mfma.hip"), PROBE_LIB, verbose)
     return LIB
 
 

@@ -19,6 +19,7 @@
 #include "qp_phases.h"
 #include "qp_stream.h"
 #include "qp_tiled.h"
+#include "qp_flow.h"
 #include "qp_sample.h"
 
 using namespace qp;
@@ -272,6 +273,12 @@ struct qp_handle {
     qp::stream::Recs recs{};
     size_t nrecs = 0;   // records in the allocation at recs.X
     uint32_t seq = 0;
+    // dataflow kernel with matrix-core products for 3 <= B <= 16 (1.7B
+    // geometry, bf16 weights)
+    bool flow_ok = false;
+    qp::flow::Recs frecs{};
+    uint64_t* frec_base = nullptr;
+    uint32_t fseq = 0;
     // batched matrix-core path
     bool tiled_ok = false;
     bool q4 = false;   // Q4_0 weights: 4-bit fragments on the batched path
@@ -974,10 +981,54 @@ qp_status launch_tiled_graph(qp_handle* h, const RunArgs& a, hipStream_t stream)
     return QP_OK;
 }
 
-template <int WT>
-qp_status launch_frame(qp_handle* h, const RunArgs& a, hipStream_t stream, bool stepwise, bool generic, bool tiled) {
+// The moderate-batch dataflow kernel: one cooperative launch per frame.
+qp_status launch_flow(qp_handle* h, const RunArgs& a, hipStream_t stream) {
+    namespace FL = qp::flow;
     qp_status st = QP_OK;
     const Model& m = h->m;
+    const uint32_t ppf = static_cast<uint32_t>(FL::phases_per_frame(m.L));
+    if (h->fseq > 0xFFFFFFFFu - 2u * ppf) {
+        // the 32-bit phase tags would wrap: clear every record (tag 0 is never
+        // current) so that no record left from long ago can match a new tag
+        hipLaunchKernelGGL(k_fill64, dim3(64), dim3(256), 0, stream, h->frec_base, FL::kRecsTotal);
+        if (!check_hip(hipGetLastError(), "record clear", &st)) return st;
+        h->fseq = 0;
+    }
+    FL::FArgs fa{};
+    for (int l = 0; l < m.L; ++l) {
+        fa.lay[l].qkv = static_cast<const uint8_t*>(h->t_qkv[l].w);
+        fa.lay[l].o = static_cast<const uint8_t*>(h->t_o[l].w);
+        fa.lay[l].gate = static_cast<const uint8_t*>(h->t_gate[l].w);
+        fa.lay[l].up = static_cast<const uint8_t*>(h->t_up[l].w);
+        fa.lay[l].down = static_cast<const uint8_t*>(h->t_down[l].w);
+    }
+    fa.proj = static_cast<const uint8_t*>(h->t_proj.w);
+    for (int k = 0; k < kSteps; ++k) fa.lm[k] = static_cast<const uint8_t*>(h->t_lm[k].w);
+    RunArgs ra = a;
+    ra.seq0 = h->fseq;
+    Model mm = m;
+    FL::Recs rc = h->frecs;
+    void* args[] = {&mm, &ra, &rc, &fa};
+    if (!check_hip(hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&FL::k_flow), dim3(FL::kNwg),
+                                              dim3(FL::kThreadsF), args, 0, stream),
+                   "cooperative launch (moderate-batch dataflow kernel)", &st))
+        return st;
+    h->fseq += ppf;
+    return QP_OK;
+}
+
+template <int WT>
+qp_status launch_frame(qp_handle* h, const RunArgs& a, hipStream_t stream, bool stepwise, bool generic, bool tiled,
+                       bool flow = false) {
+    qp_status st = QP_OK;
+    const Model& m = h->m;
+    if constexpr (WT == WT_BF16) {
+        // 3 <= B <= 16 greedy frames (any B <= 16 under QP_FLAG_FLOW) of the
+        // 1.7B geometry with bf16 weights: the moderate-batch dataflow kernel
+        if (h->flow_ok && !a.uniforms && !stepwise && !generic && !tiled && a.B <= qp::flow::kMaxB &&
+            (flow || a.B >= 3))
+            return launch_flow(h, a, stream);
+    }
     if constexpr (WT == WT_BF16 || WT == WT_Q8) {
         // the batched path for B > 2, and for any B that the dataflow kernel
         // cannot take (Q8_0 and Q4_0 weights, other geometries)
@@ -1267,6 +1318,28 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
             m.qkv0 = qkv0;
         }
     }
+    // records of the moderate-batch dataflow kernel (same geometry, bf16
+    // weights in fragment order)
+    {
+        namespace FL = qp::flow;
+        h->flow_ok = h->stream_ok && h->tiled_ok && wt == WT_BF16;
+        if (h->flow_ok) {
+            uint64_t* r = static_cast<uint64_t*>(up.alloc(FL::kRecsTotal * 8));
+            if (r) {
+                h->frec_base = r;
+                h->frecs.XG = r;
+                h->frecs.SS = h->frecs.XG + static_cast<size_t>(FL::kMaxRows) * (FL::DP / 2);
+                h->frecs.QKV = h->frecs.SS + static_cast<size_t>(FL::kMaxRows) * FL::kNOwn;
+                h->frecs.AO = h->frecs.QKV + static_cast<size_t>(FL::kMaxRows) * FL::NQKV;
+                h->frecs.HH = h->frecs.AO + static_cast<size_t>(FL::kMaxRows) * (FL::QD / 2);
+                h->frecs.KEY = h->frecs.HH + static_cast<size_t>(FL::kMaxRows) * (FL::F / 2);
+                if (hipMemset(r, 0, FL::kRecsTotal * 8) != hipSuccess) {
+                    up.st = QP_ERR_HIP;
+                    up.msg = "hipMemset of the record buffers failed";
+                }
+            }
+        }
+    }
 
     if (up.st != QP_OK) {
         st = fail(up.st, up.msg);
@@ -1311,7 +1384,7 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
     }
     // testing only: the dataflow kernel's first record epoch, so that a test
     // reaches the tag-restart path without running 11 million frames first
-    if (const char* e = std::getenv("QP_TEST_EPOCH0")) h->seq = static_cast<uint32_t>(std::strtoul(e, nullptr, 0));
+    if (const char* e = std::getenv("QP_TEST_EPOCH0")) h->seq = h->fseq = static_cast<uint32_t>(std::strtoul(e, nullptr, 0));
     *out = h;
     return QP_OK;
 }
@@ -1323,13 +1396,20 @@ qp_status qp_run_frames_ex(qp_handle* h, int32_t B, const float* H, const int32_
     if (!h) return fail(QP_ERR_INVALID_ARG, "handle is NULL");
     if (B < 0 || B > h->m.max_batch)
         return fail(QP_ERR_BATCH, "B=" + std::to_string(B) + " outside [0, " + std::to_string(h->m.max_batch) + "]");
-    if (flags & ~(QP_FLAG_STEPWISE | QP_FLAG_GENERIC | QP_FLAG_TILED))
+    if (flags & ~(QP_FLAG_STEPWISE | QP_FLAG_GENERIC | QP_FLAG_TILED | QP_FLAG_FLOW))
         return fail(QP_ERR_INVALID_ARG, "unknown flag bits");
     const bool tiled = (flags & QP_FLAG_TILED) != 0;
+    const bool flow = (flags & QP_FLAG_FLOW) != 0;
     if (tiled && (flags & (QP_FLAG_STEPWISE | QP_FLAG_GENERIC)))
         return fail(QP_ERR_INVALID_ARG, "QP_FLAG_TILED excludes the other driver flags");
+    if (flow && (flags & (QP_FLAG_STEPWISE | QP_FLAG_GENERIC | QP_FLAG_TILED)))
+        return fail(QP_ERR_INVALID_ARG, "QP_FLAG_FLOW excludes the other driver flags");
     if (tiled && !h->tiled_ok)
         return fail(QP_ERR_INVALID_ARG, "the batched matrix-core path does not support this geometry or weight dtype");
+    if (flow && (!h->flow_ok || B > qp::flow::kMaxB))
+        return fail(QP_ERR_INVALID_ARG,
+                    "the moderate-batch dataflow kernel takes the 1.7B predictor geometry with bf16 weights and "
+                    "B <= 16 only");
     if (B == 0) return QP_OK;
     if (!H || !q0 || !tokens_out || !embsum_out) return fail(QP_ERR_INVALID_ARG, "NULL input or output pointer");
     DeviceGuard guard(h->device);
@@ -1347,7 +1427,7 @@ qp_status qp_run_frames_ex(qp_handle* h, int32_t B, const float* H, const int32_
     const bool generic = (flags & QP_FLAG_GENERIC) != 0;
     switch (h->m.wt) {
         case WT_F32: return launch_frame<WT_F32>(h, a, s, stepwise, generic, false);
-        case WT_BF16: return launch_frame<WT_BF16>(h, a, s, stepwise, generic, tiled);
+        case WT_BF16: return launch_frame<WT_BF16>(h, a, s, stepwise, generic, tiled, flow);
         default: return launch_frame<WT_Q8>(h, a, s, stepwise, generic, tiled);
     }
 }

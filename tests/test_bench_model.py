@@ -76,7 +76,11 @@ def test_driver_choice():
     W = synth.WORKLOADS
     assert bench.select_driver(W["b1"].geom, 1, args) == "dataflow"
     assert bench.select_driver(W["b1"].geom, 2, args) == "dataflow"
-    assert bench.select_driver(W["b16"].geom, 16, args) == "tiled"
+    assert bench.select_driver(W["b16"].geom, 16, args) == "flow"
+    assert bench.select_driver(W["b16"].geom, 3, args) == "flow"
+    assert bench.select_driver(W["b16"].geom, 17, args) == "tiled"
+    assert bench.select_driver(W["q8ema"].geom, 16, args) == "tiled"
+    assert bench.select_driver(W["b128"].geom, 128, args) == "tiled"
     assert bench.select_driver(W["q4_b1"].geom, 1, args) == "dataflow"
     assert bench.select_driver(W["q8ema"].geom, 64, args) == "tiled"
     assert bench.select_driver(W["tiny_bf16"].geom, 1, args) == "tiled"

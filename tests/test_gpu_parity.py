@@ -51,7 +51,8 @@ def workload(name):
     return _cache[name]
 
 
-def gpu_frame(pred, H, q0, force=None, logits=True, taps=False, stepwise=False, generic=False, tiled=False):
+def gpu_frame(pred, H, q0, force=None, logits=True, taps=False, stepwise=False, generic=False, tiled=False,
+              flow=False):
     dev = _dev()
     g = pred.geom
     B = H.shape[0]
@@ -64,7 +65,7 @@ def gpu_frame(pred, H, q0, force=None, logits=True, taps=False, stepwise=False, 
     tp = (torch.full((16, g.n_layers, B, g.d_model), float("nan"), dtype=torch.float32, device=dev)
           if taps else None)
     pred.run(Ht, qt, tok, emb, force=ft, logits_out=lg, taps_out=tp, stepwise=stepwise, generic=generic,
-             tiled=tiled)
+             tiled=tiled, flow=flow)
     torch.cuda.synchronize()
     assert pred.get_error() == 0
     out = {"tokens": tok.cpu().numpy(), "embsum": emb.cpu().numpy()}
@@ -75,13 +76,13 @@ def gpu_frame(pred, H, q0, force=None, logits=True, taps=False, stepwise=False, 
     return out
 
 
-def check_against_oracle(name, model, pred, H, q0, rows, stepwise=False, tiled=False):
+def check_against_oracle(name, model, pred, H, q0, rows, stepwise=False, tiled=False, flow=False):
     """Teacher-forced comparison of the sampled ``rows`` of one frame."""
     tol = TOL[model.g.weight_dtype]
     ref = O.run_frames(model, H[rows], q0[rows])
     force = np.zeros((H.shape[0], 15), dtype=np.int32)
     force[rows] = ref["tokens"]
-    got = gpu_frame(pred, H, q0, force=force, stepwise=stepwise, tiled=tiled)
+    got = gpu_frame(pred, H, q0, force=force, stepwise=stepwise, tiled=tiled, flow=flow)
     lg_err = np.abs(got["logits"][rows] - ref["logits"]).max()
     em_err = np.abs(got["embsum"][rows] - ref["embsum"]).max()
     sure = ref["margin"] > MARGIN
@@ -340,6 +341,107 @@ def test_dataflow_kernel_taps_and_repeat():
     again = gpu_frame(pred, H[0], q0[0], force=ref["tokens"].astype(np.int32), taps=True)
     for key in ("tokens", "logits", "embsum", "taps"):
         np.testing.assert_array_equal(again[key], got[key])
+
+
+# ----------------------------------------------------------------------------
+# the moderate-batch dataflow kernel (1.7B geometry, bf16, 3 <= B <= 16)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B", [3, 8, 9, 16])
+def test_flow_kernel_against_oracle_and_batched(B):
+    """Every row of two frames against the oracle (B = 9 and 16: the prefill's
+    2B rows span two 16-row fragments), then the same frames on the batched
+    matrix-core path: the two round the same operands to bf16 and agree to
+    the bf16 bar."""
+    wl, W, model, pred = workload("b16")
+    H, q0 = synth.make_inputs(wl.geom, B, 2, 8100 + B)
+    for f in range(2):
+        ref, got = check_against_oracle(f"flow B={B}", model, pred, H[f], q0[f], np.arange(B))
+        tiled = gpu_frame(pred, H[f], q0[f], force=ref["tokens"].astype(np.int32), tiled=True)
+        lg = np.abs(tiled["logits"] - got["logits"]).max()
+        print(f"[flow B={B} vs batched] logits max-abs {lg:.3g}")
+        assert lg <= TOL["bf16"]
+        assert np.abs(tiled["embsum"] - got["embsum"]).max() <= 1e-5
+
+
+@pytest.mark.parametrize("B", [1, 2])
+def test_flow_kernel_small_batches_by_flag(B):
+    """The same kernel at B = 1 and 2 (QP_FLAG_FLOW; by default those run on
+    the small-batch kernel): one unit per kv head of each request."""
+    wl, W, model, pred = workload("b16")
+    H, q0 = synth.make_inputs(wl.geom, B, 1, 8200 + B)
+    check_against_oracle(f"flow B={B} (flag)", model, pred, H[0], q0[0], np.arange(B), flow=True)
+
+
+def test_flow_kernel_taps_composition_and_repeat():
+    """Per-layer residual taps against the oracle's; a row's results do not
+    depend on the batch it runs in (a permuted subset of a B = 12 frame
+    reproduces its rows bit for bit); repeats are bit for bit."""
+    wl, W, model, pred = workload("b16")
+    H, q0 = synth.make_inputs(wl.geom, 12, 1, 8300)
+    ref = O.run_frames(model, H[0][:5], q0[0][:5], want_taps=True)
+    got = gpu_frame(pred, H[0][:5], q0[0][:5], force=ref["tokens"].astype(np.int32), taps=True)
+    err = np.abs(got["taps"] - ref["taps"]).max()
+    print(f"[flow taps] max-abs {err:.3g}")
+    assert err <= TOL["bf16"]
+    full = gpu_frame(pred, H[0], q0[0])
+    perm = np.array([11, 2, 7, 0])
+    sub = gpu_frame(pred, H[0][perm], q0[0][perm])
+    for key in ("tokens", "logits", "embsum"):
+        np.testing.assert_array_equal(sub[key], full[key][perm])
+    for _ in range(3):
+        rep = gpu_frame(pred, H[0], q0[0])
+        for key in ("tokens", "logits", "embsum"):
+            np.testing.assert_array_equal(rep[key], full[key])
+
+
+def test_flow_kernel_flags():
+    """An out-of-range q0 and an out-of-range forced token raise the sticky
+    flag and are read as token 0; the next call is clean."""
+    wl, W, model, pred = workload("b16")
+    dev = _dev()
+    g = wl.geom
+    B = 6
+    H, q0 = synth.make_inputs(g, B, 1, 8400)
+    bad = q0[0].copy()
+    bad[4] = g.vocab + 7
+    fixed = bad.copy()
+    fixed[4] = 0
+    ref = gpu_frame(pred, H[0], fixed, logits=False)
+    tok = torch.zeros((B, 15), dtype=torch.int32, device=dev)
+    emb = torch.zeros((B, g.d_talker), device=dev)
+    pred.run(torch.from_numpy(H[0]).to(dev), torch.from_numpy(bad).to(dev), tok, emb)
+    torch.cuda.synchronize()
+    assert pred.get_error() == 1
+    assert pred.get_error() == 0
+    np.testing.assert_array_equal(tok.cpu().numpy(), ref["tokens"])
+    np.testing.assert_array_equal(emb.cpu().numpy(), ref["embsum"])
+    force = np.zeros((B, 15), dtype=np.int32)
+    force[2, 6] = -1
+    pred.run(torch.from_numpy(H[0]).to(dev), torch.from_numpy(fixed).to(dev), tok, emb,
+             force=torch.from_numpy(force).to(dev))
+    torch.cuda.synchronize()
+    assert pred.get_error() == 2
+    assert pred.get_error() == 0
+
+
+def test_flow_kernel_record_tags_restart(monkeypatch):
+    """The kernel's 32-bit record tags restart, after its records are
+    cleared, before they would wrap; frames on both sides of the restart
+    equal a fresh handle's bit for bit."""
+    wl, W, model, pred = workload("b16")
+    ppf = 1 + 15 * (5 * wl.geom.n_layers + 1) + 1
+    last = 2**32 - 1 - 2 * ppf
+    monkeypatch.setenv("QP_TEST_EPOCH0", str(last - 50))
+    late = bd.Predictor(W, wl.geom, max_batch=16)
+    monkeypatch.delenv("QP_TEST_EPOCH0")
+    H, q0 = synth.make_inputs(wl.geom, 7, 3, 8500)
+    for f in range(3):
+        a = gpu_frame(pred, H[f], q0[f])
+        b = gpu_frame(late, H[f], q0[f])
+        for key in ("tokens", "logits", "embsum"):
+            np.testing.assert_array_equal(a[key], b[key])
+    late.close()
 
 
 # ----------------------------------------------------------------------------
