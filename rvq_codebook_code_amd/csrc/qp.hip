@@ -1329,7 +1329,7 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
                 h->frec_base = r;
                 h->frecs.XG = r;
                 h->frecs.SS = h->frecs.XG + static_cast<size_t>(FL::kMaxRows) * (FL::DP / 2);
-                h->frecs.QKV = h->frecs.SS + static_cast<size_t>(FL::kMaxRows) * FL::kNOwn;
+                h->frecs.QKV = h->frecs.SS + static_cast<size_t>(FL::kNOwn) * FL::kMaxRows;
                 h->frecs.AO = h->frecs.QKV + static_cast<size_t>(FL::kMaxRows) * FL::NQKV;
                 h->frecs.HH = h->frecs.AO + static_cast<size_t>(FL::kMaxRows) * (FL::QD / 2);
                 h->frecs.KEY = h->frecs.HH + static_cast<size_t>(FL::kMaxRows) * (FL::F / 2);

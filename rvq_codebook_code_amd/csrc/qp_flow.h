@@ -70,13 +70,16 @@ __host__ __device__ constexpr int phases_per_frame(int L) { return 1 + kSteps * 
 // Record buffers (all zero-initialised; tag 0 is never current).
 struct Recs {
     uint64_t* XG;    // [kMaxRows][DP / 2]   bf16 pairs of g_next * x
-    uint64_t* SS;    // [kMaxRows][kNOwn]    sum of x^2 over each owner's 16 columns
+    uint64_t* SS;    // [kNOwn][kMaxRows]    sum of x^2 over each owner's 16 columns; owner-major,
+                     // so that each owner writes its own block (rows of many
+                     // writers sharing a segment made every reader wait longer)
     uint64_t* QKV;   // [kMaxRows][NQKV]     fp32
     uint64_t* AO;    // [kMaxRows][QD / 2]   bf16 pairs of the attention output
     uint64_t* HH;    // [kMaxRows][F / 2]    bf16 pairs of the SwiGLU output
     uint64_t* KEY;   // [kMaxB][kNLm][2]     ordered logit bits, vocabulary index
 };
-constexpr size_t kRecsTotal = static_cast<size_t>(kMaxRows) * (DP / 2 + kNOwn + NQKV + QD / 2 + F / 2) +
+constexpr size_t kRecsTotal = static_cast<size_t>(kMaxRows) * (DP / 2 + NQKV + QD / 2 + F / 2) +
+                              static_cast<size_t>(kNOwn) * kMaxRows +
                               static_cast<size_t>(kMaxB) * kNLm * 2;
 
 // Fragment-ordered bf16 weights ([N/16][K/32][64 lanes][8]) of one launch.
@@ -153,19 +156,31 @@ __device__ __forceinline__ f32x4_t mfma_slice(const uint16_t* stage, int wave, i
 }
 
 // Wait for one staged row: NJ 16-byte loads per lane of bf16-pair records
-// (2 records = 4 values each) into dst (bf16, K = 256 NJ values) and, when
-// ss is set, the row's 64 sums of squares (one record per lane), returned
-// as the fixed-order total.  Bounded wait: a record that never arrives
+// (2 records = 4 values each) into dst (bf16, K = 256 NJ values).  With ss
+// set, the wave also waits for its share of the fragment's sums of squares:
+// owners 4 wave .. 4 wave + 3 (lane / 16), rows ss_row0 + lane % 16 below
+// ss_row0 + ss_rows, into ss_dst[owner][lane % 16] (the row totals are taken
+// after the workgroup barrier).  Bounded wait: a record that never arrives
 // raises the timeout flag and the row keeps whatever arrived.
+// Without a row of its own (have_row false: the fragment's rows end
+// before this wave's) a wave still waits for its share of the sums and
+// zeroes its staged row.
 template <int NJ>
-__device__ __forceinline__ float poll_row(const uint64_t* rec, const uint64_t* ss, uint32_t tag, uint16_t* dst,
-                                          unsigned* err) {
+__device__ __forceinline__ void poll_row(const uint64_t* rec, uint32_t tag, uint16_t* dst, unsigned* err,
+                                         const uint64_t* ss = nullptr, int ss_row0 = 0, int ss_rows = 0,
+                                         float* ss_dst = nullptr, bool have_row = true) {
     const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
     const rsrc_t r = stream::wrsrc(rec, NJ * 1024);
-    const rsrc_t rs = stream::wrsrc(ss ? ss : rec, 512);
-    uint32_t pend = (1u << NJ) - 1u;
-    bool spend = ss != nullptr;
-    float sq = 0.f;
+    const rsrc_t rs = stream::wrsrc(ss ? ss : rec, 0x7FFFFFF0u);
+    const int so = 4 * wave + (lane >> 4);                     // owner of this lane's sum
+    const uint32_t soff = (static_cast<uint32_t>(so) * kMaxRows + ss_row0 + (lane & 15)) * 8u;
+    uint32_t pend = have_row ? (1u << NJ) - 1u : 0u;
+    bool spend = ss != nullptr && (lane & 15) < ss_rows;
+    if (!have_row) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) *reinterpret_cast<uint2*>(dst + 4 * (j * 64 + lane)) = make_uint2(0u, 0u);
+    }
     unsigned spins = 0;
     while (true) {
         decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0u, 0u, 0)) u[NJ];
@@ -173,7 +188,7 @@ __device__ __forceinline__ float poll_row(const uint64_t* rec, const uint64_t* s
         for (int j = 0; j < NJ; ++j)
             if ((pend >> j) & 1u) u[j] = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16u, 1024u * j, kDeviceScope);
         decltype(__builtin_amdgcn_raw_buffer_load_b64(rs, 0u, 0u, 0)) us{};
-        if (spend) us = __builtin_amdgcn_raw_buffer_load_b64(rs, lane * 8u, 0u, kDeviceScope);
+        if (spend) us = __builtin_amdgcn_raw_buffer_load_b64(rs, soff, 0u, kDeviceScope);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             if (((pend >> j) & 1u) && static_cast<uint32_t>(u[j][1]) == tag && static_cast<uint32_t>(u[j][3]) == tag) {
@@ -183,13 +198,12 @@ __device__ __forceinline__ float poll_row(const uint64_t* rec, const uint64_t* s
             }
         }
         if (spend && static_cast<uint32_t>(us[1]) == tag) {
-            sq = __uint_as_float(static_cast<uint32_t>(us[0]));
+            ss_dst[so * 16 + (lane & 15)] = __uint_as_float(static_cast<uint32_t>(us[0]));
             spend = false;
         }
         if (!__any(pend != 0u || spend)) break;
         if (!stream::spin_wait(spins, err)) break;
     }
-    return ss ? wave_sum(sq) : 0.f;
 }
 
 template <int NJ>
@@ -242,6 +256,7 @@ __global__ __launch_bounds__(kThreadsF) void k_flow(Model m, RunArgs a, Recs rc,
     __shared__ __attribute__((aligned(16))) uint16_t stage[16 * kSRow];   // staged operand rows (attention scratch too)
     __shared__ f32x4_t red[2][kW][64];                                   // partial tiles of the 16 waves
     __shared__ float rinv_s[16];
+    __shared__ float ss_s[kNOwn * 16];                                   // [owner][fragment row] sums of x^2
     __shared__ float rope_s[2][kPositions * (HD / 2)];
     __shared__ float qk_s[kMaxL][2][HD];                                 // q_norm, k_norm gains
     __shared__ int fed_s[kMaxB];
@@ -321,6 +336,13 @@ __global__ __launch_bounds__(kThreadsF) void k_flow(Model m, RunArgs a, Recs rc,
         for (int w = 1; w < kW; ++w) t += r[w * 64 * 4];
         return t;
     };
+    // wave w: the RMSNorm scale of fragment row w from the owners' sums
+    // (lane c holds owner c's; the fixed reduction tree), after the barrier
+    // that follows the polls
+    auto row_scale = [&]() {
+        const float sq = wave_sum(ss_s[lane * 16 + wave]);
+        if (lane == 0) rinv_s[wave] = __builtin_amdgcn_rsqf(sq / static_cast<float>(DP) + eps);
+    };
     // owner epilogue (waves 0..3): publish bf16(gain * x) pairs and the
     // 16-column sum of x^2 of this wave's row of fragment rf, if below M
     auto publish_x = [&](int rf, int M, int gj, uint32_t tag) {
@@ -333,7 +355,7 @@ __global__ __launch_bounds__(kThreadsF) void k_flow(Model m, RunArgs a, Recs rc,
         if (row < M) {
             const uint32_t col = 16 * oc + (ln & 15);
             if ((ln & 1) == 0) st_rec64(rbuf(rc.XG), static_cast<uint32_t>(row) * (DP / 2) + col / 2, hb | (nb << 16), tag);
-            if ((ln & 15) == 0) st_rec64(rbuf(rc.SS), static_cast<uint32_t>(row) * kNOwn + oc, __float_as_uint(sq), tag);
+            if ((ln & 15) == 0) st_rec64(rbuf(rc.SS), static_cast<uint32_t>(oc) * kMaxRows + row, __float_as_uint(sq), tag);
         }
     };
     // the tokens of step sp (owners: every request, one wave per request;
@@ -419,15 +441,10 @@ __global__ __launch_bounds__(kThreadsF) void k_flow(Model m, RunArgs a, Recs rc,
                 for (int rf = 0; rf < 2; ++rf) {
                     if (rf >= nrf) break;
                     const int row = 16 * rf + wave;
-                    if (row < M) {
-                        const float sq = poll_row<DP / 256>(rc.XG + static_cast<size_t>(row) * (DP / 2),
-                                                            rc.SS + static_cast<size_t>(row) * kNOwn, tin,
-                                                            stage + wave * kSRow, err);
-                        if (lane == 0) rinv_s[wave] = __builtin_amdgcn_rsqf(sq / static_cast<float>(DP) + eps);
-                    } else {
-                        zero_row<DP / 256>(stage + wave * kSRow);
-                    }
+                    poll_row<DP / 256>(rc.XG + static_cast<size_t>(row) * (DP / 2), tin, stage + wave * kSRow, err,
+                                       rc.SS, 16 * rf, M - 16 * rf, ss_s, row < M);
                     __syncthreads();
+                    if (row < M) row_scale();
                     red[0][wave][lane] = mfma_slice<2>(stage, wave, lane, wb, f32x4_t{0.f, 0.f, 0.f, 0.f});
                     __syncthreads();
                     if (wave < 4) {
@@ -583,8 +600,7 @@ __global__ __launch_bounds__(kThreadsF) void k_flow(Model m, RunArgs a, Recs rc,
                 for (int rf = 0; rf < 2; ++rf) {
                     if (rf >= nrf) break;
                     const int row = 16 * rf + wave;
-                    if (row < M) (void)poll_row<QD / 256>(rc.AO + static_cast<size_t>(row) * (QD / 2), nullptr, tin,
-                                                         stage + wave * kSRow, err);
+                    if (row < M) poll_row<QD / 256>(rc.AO + static_cast<size_t>(row) * (QD / 2), tin, stage + wave * kSRow, err);
                     else zero_row<QD / 256>(stage + wave * kSRow);
                     __syncthreads();
                     red[0][wave][lane] = mfma_slice<4>(stage, wave, lane, wb, f32x4_t{0.f, 0.f, 0.f, 0.f});
@@ -607,15 +623,10 @@ __global__ __launch_bounds__(kThreadsF) void k_flow(Model m, RunArgs a, Recs rc,
                 for (int rf = 0; rf < 2; ++rf) {
                     if (rf >= nrf) break;
                     const int row = 16 * rf + wave;
-                    if (row < M) {
-                        const float sq = poll_row<DP / 256>(rc.XG + static_cast<size_t>(row) * (DP / 2),
-                                                            rc.SS + static_cast<size_t>(row) * kNOwn, tin,
-                                                            stage + wave * kSRow, err);
-                        if (lane == 0) rinv_s[wave] = __builtin_amdgcn_rsqf(sq / static_cast<float>(DP) + eps);
-                    } else {
-                        zero_row<DP / 256>(stage + wave * kSRow);
-                    }
+                    poll_row<DP / 256>(rc.XG + static_cast<size_t>(row) * (DP / 2), tin, stage + wave * kSRow, err,
+                                       rc.SS, 16 * rf, M - 16 * rf, ss_s, row < M);
                     __syncthreads();
+                    if (row < M) row_scale();
                     red[0][wave][lane] = mfma_slice<2>(stage, wave, lane, wb, f32x4_t{0.f, 0.f, 0.f, 0.f});
                     red[1][wave][lane] = mfma_slice<2>(stage, wave, lane, wb + 2, f32x4_t{0.f, 0.f, 0.f, 0.f});
                     __syncthreads();
@@ -648,8 +659,7 @@ __global__ __launch_bounds__(kThreadsF) void k_flow(Model m, RunArgs a, Recs rc,
                 for (int rf = 0; rf < 2; ++rf) {
                     if (rf >= nrf) break;
                     const int row = 16 * rf + wave;
-                    if (row < M) (void)poll_row<F / 256>(rc.HH + static_cast<size_t>(row) * (F / 2), nullptr, tin,
-                                                        stage + wave * kSRow, err);
+                    if (row < M) poll_row<F / 256>(rc.HH + static_cast<size_t>(row) * (F / 2), tin, stage + wave * kSRow, err);
                     else zero_row<F / 256>(stage + wave * kSRow);
                     __syncthreads();
                     red[0][wave][lane] = mfma_slice<6>(stage, wave, lane, wb, f32x4_t{0.f, 0.f, 0.f, 0.f});
@@ -676,15 +686,10 @@ __global__ __launch_bounds__(kThreadsF) void k_flow(Model m, RunArgs a, Recs rc,
             const uint32_t tin = tag_of(ph_layer(L, s, L - 1, T_DOWN));
             const uint32_t tout = tag_of(ph_lm(L, s));
             const int r0 = (s == 1) ? B : 0;
-            if (wave < B) {
-                const float sq = poll_row<DP / 256>(rc.XG + static_cast<size_t>(r0 + wave) * (DP / 2),
-                                                    rc.SS + static_cast<size_t>(r0 + wave) * kNOwn, tin,
-                                                    stage + wave * kSRow, err);
-                if (lane == 0) rinv_s[wave] = __builtin_amdgcn_rsqf(sq / static_cast<float>(DP) + eps);
-            } else {
-                zero_row<DP / 256>(stage + wave * kSRow);
-            }
+            poll_row<DP / 256>(rc.XG + static_cast<size_t>(r0 + wave) * (DP / 2), tin, stage + wave * kSRow, err,
+                               rc.SS, r0, B, ss_s, wave < B);
             __syncthreads();
+            if (wave < B) row_scale();
             red[0][wave][lane] = mfma_slice<2>(stage, wave, lane, wb, f32x4_t{0.f, 0.f, 0.f, 0.f});
             __syncthreads();
             if (wave < 4) {
