@@ -76,7 +76,8 @@ struct Recs {
     uint64_t* QKV;   // [kMaxRows][NQKV]     fp32
     uint64_t* AO;    // [kMaxRows][QD / 2]   bf16 pairs of the attention output
     uint64_t* HH;    // [kMaxRows][F / 2]    bf16 pairs of the SwiGLU output
-    uint64_t* KEY;   // [kMaxB][kNLm][2]     ordered logit bits, vocabulary index
+    uint64_t* KEY;   // [kNLm][kMaxB][2]     ordered logit bits, vocabulary index; fragment-major,
+                     // each lm_head workgroup writing its own block
 };
 constexpr size_t kRecsTotal = static_cast<size_t>(kMaxRows) * (DP / 2 + NQKV + QD / 2 + F / 2) +
                               static_cast<size_t>(kNOwn) * kMaxRows +
@@ -218,7 +219,8 @@ __device__ __forceinline__ void zero_row(uint16_t* dst) {
 __device__ __forceinline__ int poll_token(const uint64_t* key, int b, uint32_t tag, unsigned* err) {
     const int lane = threadIdx.x & 63;
     constexpr int NJ = kNLm / 64;
-    const rsrc_t r = stream::wrsrc(key + static_cast<size_t>(b) * kNLm * 2, kNLm * 16);
+    // fragment f = lane + 64 j: its record pair for request b
+    const rsrc_t r = stream::wrsrc(key + static_cast<size_t>(b) * 2, kNLm * kMaxB * 16);
     uint32_t ord[NJ], idx[NJ];
     uint32_t pend = (1u << NJ) - 1u;
     unsigned spins = 0;
@@ -226,7 +228,8 @@ __device__ __forceinline__ int poll_token(const uint64_t* key, int b, uint32_t t
         decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0u, 0u, 0)) u[NJ];
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
-            if ((pend >> j) & 1u) u[j] = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16u, 1024u * j, kDeviceScope);
+            if ((pend >> j) & 1u)
+                u[j] = __builtin_amdgcn_raw_buffer_load_b128(r, lane * (kMaxB * 16u), j * 64u * kMaxB * 16u, kDeviceScope);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             if (((pend >> j) & 1u) && static_cast<uint32_t>(u[j][1]) == tag && static_cast<uint32_t>(u[j][3]) == tag) {
@@ -705,7 +708,7 @@ __global__ __launch_bounds__(kThreadsF) void k_flow(Model m, RunArgs a, Recs rc,
                     key = k2 > key ? k2 : key;
                 }
                 if ((ln & 15) == 0 && b < B) {
-                    const uint32_t kr = (static_cast<uint32_t>(b) * kNLm + wg) * 2;
+                    const uint32_t kr = (static_cast<uint32_t>(wg) * kMaxB + b) * 2;
                     st_rec64(rbuf(rc.KEY), kr, static_cast<uint32_t>(key >> 32), tout);
                     st_rec64(rbuf(rc.KEY), kr + 1, static_cast<uint32_t>(argmax_index(key)), tout);
                 }
