@@ -225,6 +225,8 @@ def select_driver(g, B: int, args) -> str:
         return "stepwise"
     if args.generic:
         return "generic"
+    if getattr(args, "flow", False):
+        return "flow"
     if B <= 2 and has_qkv0_table(g):
         return "dataflow"
     if B <= 16 and has_qkv0_table(g) and g.weight_dtype == "bf16":
@@ -300,6 +302,8 @@ def main():
     ap.add_argument("--workload", default="b1", choices=sorted(synth.WORKLOADS) + sorted(synth.TALKER_WORKLOADS))
     ap.add_argument("--stepwise", action="store_true", help="one kernel per phase instead of the persistent kernel")
     ap.add_argument("--generic", action="store_true", help="the generic persistent kernel even where a specialised one exists")
+    ap.add_argument("--flow", action="store_true",
+                    help="the moderate-batch dataflow kernel at any B <= 16 (1.7B geometry, bf16 weights)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sample", default=None, metavar="T,K,P",
@@ -338,7 +342,7 @@ def main():
         run_talker(args, torch, dev)
         return
     line = measure(args.workload, args, torch, dev, bd)
-    if (args.workload == "b1" and not args.only and not args.sample and not (args.stepwise or args.generic)
+    if (args.workload == "b1" and not args.only and not args.sample and not (args.stepwise or args.generic or args.flow)
             and args.batch is None and not args.flush_mib):
         # the metric is quoted at B = 1, 16 and 128: the other two batch sizes
         # are timed in the same run, each with its own roofline and oracle
@@ -380,7 +384,8 @@ def measure(name, args, torch, dev, bd):
 
     def frame(i):
         if sampling is None:
-            pred.run(Hd[i % F], qd[i % F], tok, emb, stepwise=args.stepwise, generic=args.generic)
+            pred.run(Hd[i % F], qd[i % F], tok, emb, stepwise=args.stepwise, generic=args.generic,
+                     flow=args.flow)
         else:
             pred.run_sampled(Hd[i % F], qd[i % F], Ud[i % F], tok, emb, *sampling)
 

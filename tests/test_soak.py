@@ -74,6 +74,18 @@ def test_dataflow_kernel_thousand_frames_bitwise(B):
     pred.close()
 
 
+def test_moderate_batch_kernel_thousand_frames_bitwise():
+    """The moderate-batch dataflow kernel at B = 16 (the bench's b16
+    configuration): tokens, logits and embsum of 1,000 frames of one input."""
+    wl = synth.WORKLOADS["b16"]
+    print(f"[soak] moderate-batch dataflow B=16: {FRAMES} frames", flush=True)
+    W = synth.make_weights(wl.geom, wl.weight_seed)
+    pred = bd.Predictor(W, wl.geom, max_batch=wl.batch)
+    tok = _soak(pred, wl.geom, wl.batch, 5350, logits=True)
+    assert len(np.unique(tok)) > 50
+    pred.close()
+
+
 def test_batched_graph_thousand_frames_bitwise():
     """The batched matrix-core path at B = 128 (the bench's configuration):
     1,000 graph replays (no hooks), tokens and embsum bitwise; then 200
