@@ -227,6 +227,8 @@ def select_driver(g, B: int, args) -> str:
         return "generic"
     if getattr(args, "flow", False):
         return "flow"
+    if getattr(args, "tiled", False):
+        return "tiled"
     if B <= 2 and has_qkv0_table(g):
         return "dataflow"
     if B <= 16 and has_qkv0_table(g) and g.weight_dtype == "bf16":
@@ -239,13 +241,18 @@ def select_driver(g, B: int, args) -> str:
     return "generic"
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of the dataflow kernel from the committed counter
+TRAFFIC_FILES = {"dataflow": "k_stream", "flow": "k_flow"}
+
+
+def measured_traffic(driver: str, workload: str):
+    """HBM bytes per launch of a dataflow kernel from the committed counter
     summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy), or None when
-    there is none for this workload or the kernel's sources have changed
-    since the counters were taken."""
+    there is none for this driver and workload or the kernel's sources have
+    changed since the counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"k_stream_{workload}_hbm_traffic.txt")
+    if driver not in TRAFFIC_FILES:
+        return None
+    path = os.path.join(ROOT, "profiles", f"{TRAFFIC_FILES[driver]}_{workload}_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -281,6 +288,29 @@ def mfma_peak():
     return round(tf.value, 1)
 
 
+def exchange_probe():
+    """Microseconds per tagged-record hand-off (libqp_probe.so): records per
+    phase x consumer workgroups x waves per workgroup x loads in flight."""
+    import ctypes as C
+    lib = C.CDLL(os.path.join(ROOT, "rvq_codebook_code_amd", "libqp_probe.so"))
+    lib.qp_probe_exchange.argtypes = [C.c_int] * 6 + [C.POINTER(C.c_float)]
+    lib.qp_probe_exchange.restype = C.c_int
+    out = []
+    for waves, loads in ((4, 8), (4, 16), (8, 8), (16, 8)):
+        for R in (1024, 4096, 8192, 16384, 32768, 49152):
+            for consumers in (64, 256):
+                us = C.c_float()
+                rc = lib.qp_probe_exchange(R, consumers, waves, loads, 200, 3, C.byref(us))
+                if rc == -1:
+                    continue
+                if rc != 0:
+                    raise RuntimeError(f"exchange probe failed ({rc})")
+                out.append({"records": R, "kib_per_consumer": R * 8 // 1024, "consumers": consumers,
+                            "waves": waves, "loads_in_flight": loads, "us_per_phase": round(us.value, 3)})
+                print(json.dumps(out[-1]), flush=True)
+    return out
+
+
 def calibrate_copy(torch, dev):
     """A plain copy of COPY_BYTES, five times: the reference for scaling the
     FETCH_SIZE / WRITE_SIZE counters (each launch reads and writes exactly
@@ -313,6 +343,8 @@ def main():
     ap.add_argument("--flush-mib", type=int, default=0,
                     help="before every timed frame copy this many MiB (evicting the MALL); the frame alone is timed")
     ap.add_argument("--mfma-peak", action="store_true", help="only run the matrix-core peak probe")
+    ap.add_argument("--exchange-probe", action="store_true", help="only run the tagged-record hand-off probe")
+    ap.add_argument("--tiled", action="store_true", help="the batched matrix-core path at any B")
     ap.add_argument("--only", action="store_true",
                     help="time the named workload alone (by default the b1 line also times b16 and b128)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -334,6 +366,9 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(torch, dev)
         return
+    if args.exchange_probe:
+        exchange_probe()
+        return
     if args.mfma_peak:
         print(json.dumps({"mfma_peak_bf16_tflops": mfma_peak(), "vendor_dense_bf16_tflops": MFMA_BF16_PEAK_TFLOPS}),
               flush=True)
@@ -342,7 +377,8 @@ def main():
         run_talker(args, torch, dev)
         return
     line = measure(args.workload, args, torch, dev, bd)
-    if (args.workload == "b1" and not args.only and not args.sample and not (args.stepwise or args.generic or args.flow)
+    if (args.workload == "b1" and not args.only and not args.sample
+            and not (args.stepwise or args.generic or args.flow or args.tiled)
             and args.batch is None and not args.flush_mib):
         # the metric is quoted at B = 1, 16 and 128: the other two batch sizes
         # are timed in the same run, each with its own roofline and oracle
@@ -385,7 +421,7 @@ def measure(name, args, torch, dev, bd):
     def frame(i):
         if sampling is None:
             pred.run(Hd[i % F], qd[i % F], tok, emb, stepwise=args.stepwise, generic=args.generic,
-                     flow=args.flow)
+                     flow=args.flow, tiled=args.tiled)
         else:
             pred.run_sampled(Hd[i % F], qd[i % F], Ud[i % F], tok, emb, *sampling)
 
@@ -447,8 +483,8 @@ def measure(name, args, torch, dev, bd):
         achieved_gbs = nbytes / (launch_ms / 1e3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-                    "traffic": (measured_traffic(wl.name)
-                                if driver == "dataflow" and B == wl.batch and not args.flush_mib else None),
+                    "traffic": (measured_traffic(driver, wl.name)
+                                if B == wl.batch and not args.flush_mib else None),
                     "frac_end_to_end": round(nbytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                     "frac_unreduced_model": round(nbytes_full / (launch_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                     "algorithmic_bytes_unreduced": nbytes_full, "per": scope}

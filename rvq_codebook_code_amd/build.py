@@ -2,8 +2,8 @@
 
 ``python -m rvq_codebook_code_amd.build`` (or ``build()``) runs hipcc on
 ``csrc/qp.hip`` and writes ``rvq_codebook_code_amd/libqp.so``, and on
-``csrc/probe_mfma.hip`` (the matrix-core peak probe bench.py can run) for
-``libqp_probe.so``.  hipcc cross-compiles without a GPU.
+``csrc/probe_mfma.hip`` and ``csrc/probe_exchange.hip`` (the matrix-core
+peak and record hand-off probes bench.py can run) for ``libqp_probe.so``.  hipcc cross-compiles without a GPU.
 """
 from __future__ import annotations
 
@@ -54,10 +54,22 @@ def _hipcc(src: str, out: str, verbose: bool) -> None:
     os.replace(tmp, out)
 
 
+def _hipcc_many(srcs, out: str, verbose: bool) -> None:
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", *srcs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+    os.replace(tmp, out)
+
+
 def build(verbose: bool = False) -> str:
     """The library (libqp.so) and the matrix-core peak probe (libqp_probe.so)."""
     _hipcc(os.path.join(CSRC, "qp.hip"), LIB, verbose)
-    _hipcc(os.path.join(CSRC, "probe_mfma.hip"), PROBE_LIB, verbose)
+    _hipcc_many([os.path.join(CSRC, "probe_mfma.hip"), os.path.join(CSRC, "probe_exchange.hip")], PROBE_LIB, verbose)
     return LIB
 
 
