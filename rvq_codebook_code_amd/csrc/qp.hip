@@ -308,7 +308,7 @@ struct qp_handle {
     int* st_q0 = nullptr;                   // [max_batch]
     int* st_tok = nullptr;                  // [max_batch][15]
     float* st_emb = nullptr;                // [max_batch][dT]
-    uint16_t* t_xg = nullptr;               // [2*max_batch][dP] bf16(g_next * x)
+    uint16_t* t_xg = nullptr;               // bf16(g_next * x), 2*max_batch rows (rounded up to 16) of width dP, fragment order
     float* t_ss = nullptr;                  // [2*max_batch][dP/16] 16-column sums of x^2
     // sampled frames (batched path, V <= 4096)
     bool sample_ok = false;
@@ -688,8 +688,11 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
     const int nb = B < 1024 ? B : 1024;
     // the gain of the first reader of a position's input row
     const float* gain0 = m.L > 0 ? h->layers_host[0].attn_norm : m.out_norm;
+    // the bf16 activations' layout for this batch (qp_tiled.h, act_index)
+    const int frag = B >= T::kFragMinRows ? 1 : 0;
     T::TokArgs ta{};
     ta.B = B;
+    ta.frag = frag;
     ta.dT = m.dT;
     ta.dP = m.dP;
     ta.V = m.V;
@@ -711,6 +714,7 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(T::k_start, dim3(nb), dim3(T::kThreadsT), 0, stream, ta);
     T::AttnArgs aa{};
     aa.B = B;
+    aa.frag = frag;
     aa.nq = m.nq;
     aa.nkv = m.nkv;
     aa.nqkv = m.nqkv;
@@ -724,6 +728,7 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
     aa.rope_sin = m.rope_sin;
     T::GemmArgs g{};
     g.eps = m.eps;
+    g.frag = frag;
     // x[position 0] = W_p . H + b_p
     g.a = a.H;
     g.lda = m.dT;
@@ -750,6 +755,7 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
             if (l > 0 || s == 1 || !m.qkv0) {
                 g = T::GemmArgs{};
                 g.eps = m.eps;
+                g.frag = frag;
                 g.M = M;
                 g.a = h->t_xg;
                 g.lda = m.dP;
@@ -787,6 +793,7 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
             // x += W_o . attention; publishes bf16(ffn_norm * x)
             g = T::GemmArgs{};
             g.eps = m.eps;
+            g.frag = frag;
             g.M = M;
             g.a = ao;
             g.lda = qd;
@@ -802,6 +809,7 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
             // h = silu(W_g . RMSNorm(x)) * (W_u . RMSNorm(x)), bf16
             g = T::GemmArgs{};
             g.eps = m.eps;
+            g.frag = frag;
             g.M = M;
             g.a = h->t_xg;
             g.lda = m.dP;
@@ -816,6 +824,7 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
             // x += W_d . h (and the residual tap); publishes the next reader's operand
             g = T::GemmArgs{};
             g.eps = m.eps;
+            g.frag = frag;
             g.M = M;
             g.a = hb;
             g.lda = m.F;
@@ -838,7 +847,9 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
         const size_t row0 = s == 1 ? static_cast<size_t>(B) : 0;
         g = T::GemmArgs{};
         g.eps = m.eps;
-        g.a = h->t_xg + row0 * m.dP;
+        g.frag = frag;
+        g.a = h->t_xg;
+        g.a_row0 = static_cast<int>(row0);
         g.lda = m.dP;
         g.ss_in = h->t_ss + row0 * nss;
         g.nss = nss;
@@ -1252,10 +1263,11 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
 
     // scratch for max_batch requests
     const size_t rows = 2 * static_cast<size_t>(m.max_batch);
+    const size_t rows16 = (rows + 15) / 16 * 16;   // the batched path's bf16 operands, in whole row fragments
     m.x = static_cast<float*>(up.alloc(rows * m.dP * 4));
     m.qkv = static_cast<float*>(up.alloc(rows * m.nqkv * 4));
-    m.ao = static_cast<float*>(up.alloc(rows * qd * 4));
-    m.hb = static_cast<float*>(up.alloc(rows * m.F * 4));
+    m.ao = static_cast<float*>(up.alloc(std::max(rows * qd * 4, rows16 * qd * 2)));
+    m.hb = static_cast<float*>(up.alloc(std::max(rows * m.F * 4, rows16 * m.F * 2)));
     const size_t kvn = static_cast<size_t>(m.L > 0 ? m.L : 1) * m.max_batch * kPositions * kd;
     m.kc = static_cast<float*>(up.alloc(kvn * 4));
     m.vc = static_cast<float*>(up.alloc(kvn * 4));
@@ -1276,7 +1288,7 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
         h->t_part = static_cast<float*>(up.alloc(h->t_part_floats * 4));
         h->t_nctr = 256;  // split K (the projection of H) only applies below 256 tiles
         h->t_ctr = static_cast<unsigned*>(up.alloc(h->t_nctr * 4));
-        h->t_xg = static_cast<uint16_t*>(up.alloc(rows * m.dP * 2));
+        h->t_xg = static_cast<uint16_t*>(up.alloc(rows16 * m.dP * 2));
         h->st_H = static_cast<float*>(up.alloc(static_cast<size_t>(m.max_batch) * m.dT * 4));
         h->st_q0 = static_cast<int*>(up.alloc(static_cast<size_t>(m.max_batch) * 4));
         h->st_tok = static_cast<int*>(up.alloc(static_cast<size_t>(m.max_batch) * kSteps * 4));

@@ -61,8 +61,8 @@ struct Model {
     // scratch (sized for max_batch)
     float* x;                      // [2*maxB][dP]   residual stream rows
     float* qkv;                    // [2*maxB][nqkv]
-    float* ao;                     // [2*maxB][nq*hd] attention output
-    float* hb;                     // [2*maxB][F]     SwiGLU activations
+    float* ao;                     // [2*maxB][nq*hd] attention output (the batched path: bf16 in fragment order)
+    float* hb;                     // [2*maxB][F]     SwiGLU activations (the batched path: bf16 in fragment order)
     float* kc;                     // [L][maxB][16][nkv][hd]
     float* vc;
     unsigned long long* amax;      // [maxB] packed (logit, index) argmax keys

@@ -28,9 +28,9 @@ struct qp_talker {
     float* x = nullptr;               // [max_batch][d]
     float* ss = nullptr;              // [max_batch][d/16]
     float* qkv = nullptr;             // [max_batch][nqkv]
-    uint16_t* xg = nullptr;           // [max_batch][d]
-    uint16_t* ao = nullptr;           // [max_batch][nq*hd]
-    uint16_t* hb = nullptr;           // [max_batch][F]
+    uint16_t* xg = nullptr;           // max_batch rows (rounded up to 16) of width d, fragment order
+    uint16_t* ao = nullptr;           // ... of width nq*hd, fragment order
+    uint16_t* hb = nullptr;           // ... of width F, fragment order
     unsigned long long* keys = nullptr;  // [max_batch][vocab/16]
     float* apart = nullptr;           // attention partials [max_batch][nq][max_split][hd+2]
     int max_split = 0;
@@ -111,7 +111,9 @@ qp_status talker_launch(qp_talker* t, int B, const float* x, const int* slots, c
     const int R = G.n_q_heads / G.n_kv_heads;
     if (nsplit > t->max_split) return fail(QP_ERR_INVALID_ARG, "attention split table too small");
 
-    K::InArgs ia{d, x, t->x, t->xg, t->ss, L > 0 ? t->layers[0].attn_norm : t->out_norm};
+    // the bf16 activations' layout for this batch (qp::tiled::act_index)
+    const int frag = B >= T::kFragMinRows ? 1 : 0;
+    K::InArgs ia{d, x, t->x, t->xg, t->ss, L > 0 ? t->layers[0].attn_norm : t->out_norm, frag};
     hipLaunchKernelGGL(K::k_input, dim3(B), dim3(K::kThreadsK), 0, stream, ia);
     K::AttnArgs aa{};
     aa.nkv = G.n_kv_heads;
@@ -134,6 +136,7 @@ qp_status talker_launch(qp_talker* t, int B, const float* x, const int* slots, c
     aa.part = t->apart;
     aa.ctr = t->actr;
     aa.ao = t->ao;
+    aa.frag = frag;
     aa.err = t->err;
     aa.live = live;
     T::GemmArgs g{};
@@ -143,6 +146,7 @@ qp_status talker_launch(qp_talker* t, int B, const float* x, const int* slots, c
         // q, k, v = W_qkv . RMSNorm(x)
         g = T::GemmArgs{};
         g.eps = G.rms_eps;
+        g.frag = frag;
         g.M = B;
         g.a = t->xg;
         g.lda = d;
@@ -169,6 +173,7 @@ qp_status talker_launch(qp_talker* t, int B, const float* x, const int* slots, c
         // x += W_o . attention; publishes bf16(ffn_norm * x)
         g = T::GemmArgs{};
         g.eps = G.rms_eps;
+        g.frag = frag;
         g.M = B;
         g.a = t->ao;
         g.lda = qd;
@@ -184,6 +189,7 @@ qp_status talker_launch(qp_talker* t, int B, const float* x, const int* slots, c
         // h = silu(W_g . RMSNorm(x)) * (W_u . RMSNorm(x)), bf16
         g = T::GemmArgs{};
         g.eps = G.rms_eps;
+        g.frag = frag;
         g.M = B;
         g.a = t->xg;
         g.lda = d;
@@ -198,6 +204,7 @@ qp_status talker_launch(qp_talker* t, int B, const float* x, const int* slots, c
         // x += W_d . h; publishes the next reader's operand
         g = T::GemmArgs{};
         g.eps = G.rms_eps;
+        g.frag = frag;
         g.M = B;
         g.a = t->hb;
         g.lda = G.d_ffn;
@@ -214,6 +221,7 @@ qp_status talker_launch(qp_talker* t, int B, const float* x, const int* slots, c
     // codec head . RMSNorm(x): per-tile argmax keys (and the logits)
     g = T::GemmArgs{};
     g.eps = G.rms_eps;
+    g.frag = frag;
     g.M = B;
     g.a = t->xg;
     g.lda = d;
@@ -388,9 +396,11 @@ qp_status qp_talker_create(const qp_talker_weights* w, const qp_talker_geometry*
     t->x = static_cast<float*>(up.alloc(mb * d * 4));
     t->ss = static_cast<float*>(up.alloc(mb * (d / 16) * 4));
     t->qkv = static_cast<float*>(up.alloc(mb * nqkv * 4));
-    t->xg = static_cast<uint16_t*>(up.alloc(mb * d * 2));
-    t->ao = static_cast<uint16_t*>(up.alloc(mb * qd * 2));
-    t->hb = static_cast<uint16_t*>(up.alloc(mb * F * 2));
+    // the products' bf16 operands in fragment order: whole row fragments
+    const size_t mb16 = (mb + 15) / 16 * 16;
+    t->xg = static_cast<uint16_t*>(up.alloc(mb16 * d * 2));
+    t->ao = static_cast<uint16_t*>(up.alloc(mb16 * qd * 2));
+    t->hb = static_cast<uint16_t*>(up.alloc(mb16 * F * 2));
     t->keys = static_cast<unsigned long long*>(up.alloc(mb * (g->vocab / 16) * 8));
     t->max_split = 1;   // split counts are powers of two
     while (t->max_split * kTalkerCh < g->max_ctx) t->max_split *= 2;

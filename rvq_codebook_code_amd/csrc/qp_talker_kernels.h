@@ -49,16 +49,16 @@ struct InArgs {
     int d;
     const float* x_in;     // [B][d] the caller's rows
     float* x;              // [B][d] residual stream
-    uint16_t* xg;          // [B][d] bf16(gain0 * x)
+    uint16_t* xg;          // bf16(gain0 * x), width d (qp::tiled::act_index layout)
     float* ss;             // [B][d/16] 16-column sums of x^2
     const float* gain0;    // layer 0's attn_norm (output_norm without layers)
+    int frag;              // activations in fragment order
 };
 
 __global__ __launch_bounds__(kThreadsK) void k_input(InArgs a) {
     const int b = blockIdx.x;
     const float* src = a.x_in + static_cast<size_t>(b) * a.d;
     float* dst = a.x + static_cast<size_t>(b) * a.d;
-    uint16_t* xg = a.xg + static_cast<size_t>(b) * a.d;
     for (int f = threadIdx.x; f < a.d / 16; f += kThreadsK) {
         float v[16];
 #pragma unroll
@@ -75,8 +75,10 @@ __global__ __launch_bounds__(kThreadsK) void k_input(InArgs a) {
             s = fmaf(v[2 * i + 1], v[2 * i + 1], s);
             pk[i] = qp::tiled::pack_bf16x2(a.gain0[16 * f + 2 * i] * v[2 * i], a.gain0[16 * f + 2 * i + 1] * v[2 * i + 1]);
         }
-        reinterpret_cast<uint4*>(xg + 16 * f)[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-        reinterpret_cast<uint4*>(xg + 16 * f)[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+        // eight consecutive columns from a multiple of 8 are contiguous in either layout
+        *reinterpret_cast<uint4*>(a.xg + qp::tiled::act_index(b, 16 * f, a.d, a.frag)) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        *reinterpret_cast<uint4*>(a.xg + qp::tiled::act_index(b, 16 * f + 8, a.d, a.frag)) =
+            make_uint4(pk[4], pk[5], pk[6], pk[7]);
         a.ss[static_cast<size_t>(b) * (a.d / 16) + f] = s;
     }
 }
@@ -95,7 +97,8 @@ struct AttnArgs {
     uint16_t* vc;
     float* part;                      // [B][nq][nsplit][hd + 2]: max, sum, values
     unsigned* ctr;                    // [B][nkv] arrival counters, left at 0
-    uint16_t* ao;                     // [B][qd] bf16 attention output
+    uint16_t* ao;                     // bf16 attention output, width qd (qp::tiled::act_index layout)
+    int frag;                         // activations in fragment order
     unsigned* err;
     // prepared graphs (grid for max_ctx and a batch bucket): null, or the
     // call's limits written before the replay, {splits the call's max_len
@@ -332,9 +335,10 @@ __global__ __launch_bounds__(kThreadsK) void k_attn(AttnArgs a) {
     if (nsb == 1) {
         if (wave < R) {
             const float rl = 1.0f / st_s[wave][1];
-            uint16_t* dst = a.ao + static_cast<size_t>(b) * a.qd + (g * R + wave) * HD;
 #pragma unroll
-            for (int j = 0; j < J; ++j) dst[lane * J + j] = qp::tiled::to_bf16(o[j] * rl);
+            for (int j = 0; j < J; ++j)
+                a.ao[qp::tiled::act_index(b, (g * R + wave) * HD + lane * J + j, a.qd, a.frag)] =
+                    qp::tiled::to_bf16(o[j] * rl);
         }
         return;
     }
@@ -410,9 +414,9 @@ __global__ __launch_bounds__(kThreadsK) void k_attn(AttnArgs a) {
         }
     }
     const float rl = 1.0f / Ls;
-    uint16_t* dst = a.ao + static_cast<size_t>(b) * a.qd + (g * R + wave) * HD;
 #pragma unroll
-    for (int j = 0; j < J; ++j) dst[lane * J + j] = qp::tiled::to_bf16(O[j] * rl);
+    for (int j = 0; j < J; ++j)
+        a.ao[qp::tiled::act_index(b, (g * R + wave) * HD + lane * J + j, a.qd, a.frag)] = qp::tiled::to_bf16(O[j] * rl);
 }
 
 struct FinArgs {

@@ -15,7 +15,17 @@
 //    are stored contiguously in lane order (1 KiB per fragment for bf16,
 //    512 B of int8 codes plus 16 fp32 block scales for Q8_0).  A wave's
 //    weight load is one contiguous 1 KiB (or 512 B) read.
-//  * Activations enter as bf16.  RMSNorm is applied as
+//  * Activations enter as bf16.  From kFragMinRows rows per position on they
+//    are held in the same fragment order as the weights: a matrix of width K
+//    is [rows/16][K/32][64 lanes][8], lane l holding row l % 16, inputs
+//    8 (l / 16) .. +7 of the 32-wide block (see frag_index).  Every writer of
+//    a product's A operand (the residual and SwiGLU epilogues, attention, the
+//    token steps) then stores in that order, and a wave's load of a 16 x 32
+//    operand block touches 8 whole cache lines instead of 16 half-used ones
+//    (the batched products are bound by each CU's vector-memory path).  With
+//    fewer rows, row-major rows touch fewer lines (one per row), so they stay
+//    row-major.  Buffers hold their rows rounded up to 16.
+//  * RMSNorm is applied as
 //      W . (g * x / rms(x)) = (W . bf16(g * x)) / rms(x)
 //    Whoever writes a residual-stream row also writes bf16(g * x) with the
 //    gain of the row's next reader (ffn_norm after the output projection,
@@ -69,8 +79,11 @@ enum Src : int { SRC_F32 = 0, SRC_BF16 = 1, SRC_BF16_NORM = 2 };
 enum Epi : int { EPI_BIAS = 0, EPI_SCALE = 1, EPI_RESID = 2, EPI_SWIGLU = 3, EPI_ARGMAX = 4 };
 
 struct GemmArgs {
-    const void* a;          // A operand rows [M][lda]: fp32 (SRC_F32) or bf16
+    const void* a;          // A operand: fp32 rows [M][lda] (SRC_F32), or bf16 of width K (act_index),
+                            // logical row m at physical row a_row0 + m
     int lda;
+    int a_row0;
+    int frag;               // the bf16 activations (A operand, xg, outb) are in fragment order
     int M, N, K, KS;        // N = output columns (for SwiGLU: F)
     FMat w0, w1;            // w1: the up matrix of SwiGLU
     // RMSNorm of the A rows (SRC_BF16_NORM): the rows are already g * x in
@@ -81,10 +94,10 @@ struct GemmArgs {
     // epilogue outputs
     float* out;             // fp32 rows [M][ldo] (BIAS, SCALE, RESID)
     int ldo;
-    uint16_t* outb;         // bf16 rows [M][N] (SWIGLU)
+    uint16_t* outb;         // bf16, width N (act_index layout; SWIGLU)
     const float* bias;      // [N] (BIAS)
     // BIAS / RESID also publish the next consumer's operand and row sums:
-    // xg = bf16(g_next * x) [M][ldo], ss_out[m][f] = sum over the 16 columns
+    // xg = bf16(g_next * x) (width ldo, act_index layout), ss_out[m][f] = sum over the 16 columns
     // of fragment f of x^2
     uint16_t* xg;
     const float* g_next;
@@ -113,7 +126,8 @@ struct TokArgs {
     const unsigned long long* keys;   // [B][nkt] lm_head tile keys
     const int* sampled;               // [B] drawn tokens of this step (sampled frames), or null
     float* x;                         // residual rows [2B][dP]
-    uint16_t* xg;                     // bf16(gain0 * x) rows
+    uint16_t* xg;                     // bf16(gain0 * x), width dP (act_index layout)
+    int frag;                         // activations in fragment order
     float* ss;                        // 16-column sums of x^2 [2B][dP/16]
     const float* gain0;               // attn_norm of layer 0 (out_norm without layers)
     unsigned* err;
@@ -135,7 +149,8 @@ struct AttnArgs {
     const float* q_norm;
     const float* rope_cos;            // [16][hd/2]
     const float* rope_sin;
-    uint16_t* ao;                     // [M][nq*hd] bf16 output
+    uint16_t* ao;                     // bf16 output, width nq*hd (act_index layout)
+    int frag;                         // activations in fragment order
     // layer 0 from step 2 on, with the layer-0 q/k/v table: the previous
     // step's token decision (tok.s = that step) happens here instead of in
     // k_next, and the head vectors come from tok.qkv0 [V][nqkv]
@@ -191,6 +206,26 @@ __device__ __forceinline__ float sum16(float v) {
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kDevScope = 16;   // buffer cache policy: device-coherent (sc1)
 
+// Index of element (row p, column n) of a bf16 activation matrix of width K
+// (a multiple of 32) in fragment order: the order in which a product's wave
+// reads its A operand (lane l: row l % 16, columns 8 (l / 16) .. +7 of a
+// 32-wide block), so that its load of one 16 x 32 block is 1 KiB of
+// consecutive bytes.  Eight consecutive columns from a multiple of 8 are
+// contiguous.
+__device__ __forceinline__ size_t frag_index(int p, int n, int K) {
+    return ((static_cast<size_t>(p >> 4) * (K >> 5) + (n >> 5)) * 64 + ((n & 31) >> 3) * 16 + (p & 15)) * 8 +
+           (n & 7);
+}
+
+// The activation layout of a frame: fragment order from kFragMinRows rows
+// per position, else row-major.  A 16 x 32 operand load touches 4 cache
+// lines (up to 8 rows) or 8 in fragment order, and one line per row
+// row-major.
+constexpr int kFragMinRows = 5;
+__device__ __forceinline__ size_t act_index(int p, int n, int K, int frag) {
+    return frag ? frag_index(p, n, K) : static_cast<size_t>(p) * K + n;
+}
+
 // ---------------------------------------------------------------------------
 // [M x K] . [K x N] with a fused prologue (SRC) and epilogue (EPI).
 // grid = (N / (16 CT) (SwiGLU: N / 16), ceil(M / (16 RT)), KS), 64 * NW
@@ -229,6 +264,18 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(GemmArgs g) {
     bool rok[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) rok[rt] = m0 + 16 * rt + arow < g.M;
+    // bf16 operands: this lane's 8 inputs of k-block 0 per row tile, and the
+    // step from one k-block to the next (fragment order: one 512-element
+    // block; row-major: 32 elements)
+    const uint16_t* abase[RT];
+    const int astep = g.frag ? 512 : 32;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int p = g.a_row0 + m0 + 16 * rt + arow;   // physical row
+        abase[rt] = static_cast<const uint16_t*>(g.a) +
+                    (g.frag ? (static_cast<size_t>(p >> 4) * KB * 64 + (lane >> 4) * 16 + (p & 15)) * 8
+                            : static_cast<size_t>(p) * g.K + akoff);
+    }
 
     // RMSNorm row scales of the row tiles this wave finishes, fetched before
     // the products: lane l sums a quarter of row (l % 16)'s tile sums, the
@@ -312,7 +359,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(GemmArgs g) {
                     av[u][rt] = make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w),
                                            pack_bf16x2(x1.x, x1.y), pack_bf16x2(x1.z, x1.w));
                 } else {
-                    const uint16_t* src = static_cast<const uint16_t*>(g.a) + row * g.lda + k;
+                    const uint16_t* src = abase[rt] + static_cast<size_t>(kb + u) * astep;
                     av[u][rt] = rok[rt] ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
                 }
             }
@@ -458,7 +505,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(GemmArgs g) {
                 const int m = m0 + 16 * rt + 4 * (lane >> 4) + i;
                 if (m >= g.M) continue;
                 const float gt = tot[rt][0][i] * rinv[i], ut = tot[rt][1][i] * rinv[i];
-                g.outb[static_cast<size_t>(m) * g.N + n] = to_bf16((gt / (1.0f + expf(-gt))) * ut);
+                g.outb[act_index(m, n, g.N, g.frag)] = to_bf16((gt / (1.0f + expf(-gt))) * ut);
             }
         } else if constexpr (EPI == EPI_SCALE) {
 #pragma unroll
@@ -495,7 +542,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(GemmArgs g) {
                         }
                     }
                     *o = nv;
-                    g.xg[static_cast<size_t>(m) * g.ldo + n] = to_bf16(gn * nv);
+                    g.xg[act_index(m, n, g.ldo, g.frag)] = to_bf16(gn * nv);
                     sq[i] = nv * nv;
                 }
 #pragma unroll
@@ -521,14 +568,14 @@ __device__ __forceinline__ void store_row(const TokArgs& ta, int row, const floa
                                           const float (&gv)[kMaxPer]) {
     const int j = threadIdx.x, np = ta.dP / kThreadsT;
     float* xr = ta.x + static_cast<size_t>(row) * ta.dP;
-    uint16_t* gr = ta.xg + static_cast<size_t>(row) * ta.dP;
+    uint16_t* gr = ta.xg;   // act_index layout
     float* sr = ta.ss + static_cast<size_t>(row) * (ta.dP / 16);
 #pragma unroll
     for (int i = 0; i < kMaxPer; ++i) {
         if (i < np) {
             const int n = j + kThreadsT * i;
             xr[n] = v[i];
-            gr[n] = to_bf16(gv[i] * v[i]);
+            gr[act_index(row, n, ta.dP, ta.frag)] = to_bf16(gv[i] * v[i]);
             float q = v[i] * v[i];
             q += __shfl_xor(q, 1, 64);
             q += __shfl_xor(q, 2, 64);
@@ -804,9 +851,9 @@ __global__ __launch_bounds__(kThreadsT) void k_attn(AttnArgs m) {
 #pragma unroll
                 for (int j = 0; j < J; ++j) o[j] = fmaf(w, Vs[tt][lane + 64 * j], o[j]);
             }
-            uint16_t* orow = m.ao + static_cast<size_t>(r) * (m.nq * HD) + h * HD;
 #pragma unroll
-            for (int j = 0; j < J; ++j) orow[lane + 64 * j] = to_bf16(o[j] / den);
+            for (int j = 0; j < J; ++j)
+                m.ao[act_index(r, h * HD + lane + 64 * j, m.nq * HD, m.frag)] = to_bf16(o[j] / den);
         }
         __syncthreads();
     }
