@@ -563,9 +563,11 @@ constexpr int kMaxPer = 16;
 
 // x, xg = bf16(g * x) and the per-16-column sums of x^2 of residual-stream
 // row `row` from values v (with gains gv) already in registers; a
-// fragment's sum is reduced over the 16 threads that own it.
+// fragment's sum is reduced over the 16 threads that own it.  with_norm =
+// false writes x only (a row whose next reader is a residual add, not a
+// product).
 __device__ __forceinline__ void store_row(const TokArgs& ta, int row, const float (&v)[kMaxPer],
-                                          const float (&gv)[kMaxPer]) {
+                                          const float (&gv)[kMaxPer], bool with_norm = true) {
     const int j = threadIdx.x, np = ta.dP / kThreadsT;
     float* xr = ta.x + static_cast<size_t>(row) * ta.dP;
     uint16_t* gr = ta.xg;   // act_index layout
@@ -575,6 +577,7 @@ __device__ __forceinline__ void store_row(const TokArgs& ta, int row, const floa
         if (i < np) {
             const int n = j + kThreadsT * i;
             xr[n] = v[i];
+            if (!with_norm) continue;
             gr[act_index(row, n, ta.dP, ta.frag)] = to_bf16(gv[i] * v[i]);
             float q = v[i] * v[i];
             q += __shfl_xor(q, 1, 64);
@@ -724,10 +727,7 @@ __global__ __launch_bounds__(kThreadsT) void k_attn(AttnArgs m) {
     float o_es[TOK ? kMaxPer : 1], o_e[TOK ? kMaxPer : 1], o_v[TOK ? kMaxPer : 1], o_gv[TOK ? kMaxPer : 1];
     const int ne = ta.dT / kThreadsT, np = ta.dP / kThreadsT;
     if constexpr (TOK) {
-        if (g == 0) {
-            load_vec(ta.gain0, np, o_gv);
-            load_vec(ta.embsum + static_cast<size_t>(b) * ta.dT, ne, o_es);
-        }
+        if (g == 0) load_vec(ta.embsum + static_cast<size_t>(b) * ta.dT, ne, o_es);
         fed = decide_fed(ta, b, g == 0, red_s, &fed_s);
         if (g == 0) {
             load_emb(ta, fed, o_e);
@@ -772,7 +772,9 @@ __global__ __launch_bounds__(kThreadsT) void k_attn(AttnArgs m) {
 #pragma unroll
             for (int i = 0; i < kMaxPer; ++i)
                 if (i < ne) es_row[threadIdx.x + kThreadsT * i] = o_es[i] + o_e[i];
-            store_row(ta, b, o_v, o_gv);
+            // the row's next reader is layer 0's residual add (its q/k/v
+            // come from the table), so x alone
+            store_row(ta, b, o_v, o_gv, false);
         }
     }
 #pragma unroll
