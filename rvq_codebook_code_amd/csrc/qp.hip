@@ -627,8 +627,10 @@ int tiled_gemm(const Handle* h, qp::tiled::GemmArgs g, hipStream_t stream) {
     // Residual products (N = dP) keep one row tile at any M: with two they
     // need the split-K fixup to fill the chip, and its extra round trips cost
     // more (B = 128 bf16: 4.15 against 4.29 ms per frame-batch; one row tile
-    // for the other products was slower)
-    const int RT = (g.M <= 32 || EPI == T::EPI_RESID) ? 1 : 2;
+    // for the other products was slower).  SwiGLU keeps one row tile up to
+    // 64 rows (with fragment-ordered operands: B = 64 Q8_0 +3 %, no change
+    // at 128 rows)
+    const int RT = (g.M <= 32 || EPI == T::EPI_RESID || (EPI == T::EPI_SWIGLU && g.M <= 64)) ? 1 : 2;
     // one row tile: one 16-column fragment per workgroup (twice the
     // workgroups streaming weights); SwiGLU always pairs gate and up
     const int CT = (RT == 1 && EPI != T::EPI_SWIGLU) ? 1 : 2;
