@@ -570,7 +570,10 @@ __device__ __forceinline__ void store_row(const TokArgs& ta, int row, const floa
                                           const float (&gv)[kMaxPer], bool with_norm = true) {
     const int j = threadIdx.x, np = ta.dP / kThreadsT;
     float* xr = ta.x + static_cast<size_t>(row) * ta.dP;
-    uint16_t* gr = ta.xg;   // act_index layout
+    // element j + 256 i: 256 columns on is eight 32-wide blocks on in
+    // fragment order, 256 elements on row-major
+    uint16_t* gr = ta.xg + act_index(row, j, ta.dP, ta.frag);
+    const int gstep = ta.frag ? 4096 : kThreadsT;
     float* sr = ta.ss + static_cast<size_t>(row) * (ta.dP / 16);
 #pragma unroll
     for (int i = 0; i < kMaxPer; ++i) {
@@ -578,7 +581,7 @@ __device__ __forceinline__ void store_row(const TokArgs& ta, int row, const floa
             const int n = j + kThreadsT * i;
             xr[n] = v[i];
             if (!with_norm) continue;
-            gr[act_index(row, n, ta.dP, ta.frag)] = to_bf16(gv[i] * v[i]);
+            gr[i * gstep] = to_bf16(gv[i] * v[i]);
             float q = v[i] * v[i];
             q += __shfl_xor(q, 1, 64);
             q += __shfl_xor(q, 2, 64);
@@ -687,7 +690,7 @@ __device__ __forceinline__ int decide_fed(const TokArgs& ta, int b, bool writer,
 }
 
 template <int HD, bool TOK>
-__global__ __launch_bounds__(kThreadsT) void k_attn(AttnArgs m) {
+__global__ __launch_bounds__(kThreadsT, HD <= 128 ? 4 : 3) void k_attn(AttnArgs m) {
     constexpr int J = HD / 64;        // elements per lane in the lane + 64 j layout
     constexpr int SL = HD / 4;        // slice of the head per lane in the score
     constexpr int HPT = kPositions * HD / kThreadsT;   // history elements per thread (max)
@@ -853,9 +856,12 @@ __global__ __launch_bounds__(kThreadsT) void k_attn(AttnArgs m) {
 #pragma unroll
                 for (int j = 0; j < J; ++j) o[j] = fmaf(w, Vs[tt][lane + 64 * j], o[j]);
             }
+            // columns lane + 64 j: 64 columns on is two 32-wide blocks on
+            // in fragment order, 64 elements on row-major
+            uint16_t* op = m.ao + act_index(r, h * HD + lane, m.nq * HD, m.frag);
+            const int ostep = m.frag ? 1024 : 64;
 #pragma unroll
-            for (int j = 0; j < J; ++j)
-                m.ao[act_index(r, h * HD + lane + 64 * j, m.nq * HD, m.frag)] = to_bf16(o[j] / den);
+            for (int j = 0; j < J; ++j) op[j * ostep] = to_bf16(o[j] / den);
         }
         __syncthreads();
     }
