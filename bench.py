@@ -70,6 +70,19 @@ def algorithmic_flops(g: synth.Geometry, B: int, qkv0_table: bool = False) -> in
     return 2 * B * total
 
 
+def model_flops(g: synth.Geometry, B: int) -> int:
+    """The frame's whole arithmetic, independent of how a driver reduces it:
+    all 16 positions (the prefill's two and one per later step) through the
+    layers, 15 lm_head rows, the projection of H, and attention's scores and
+    weighted values over the cached positions (2 flops per multiply-add)."""
+    qd = g.n_q_heads * g.head_dim
+    nqkv = (g.n_q_heads + 2 * g.n_kv_heads) * g.head_dim
+    per_layer = nqkv * g.d_model + g.d_model * qd + 2 * g.d_ffn * g.d_model + g.d_model * g.d_ffn
+    attn = g.n_layers * 2 * qd * sum(p + 1 for p in range(16))
+    macs = 16 * g.n_layers * per_layer + 15 * g.vocab * g.d_model + g.d_model * g.d_talker + attn
+    return 2 * B * macs
+
+
 def has_qkv0_table(g: synth.Geometry) -> bool:
     """The library builds the layer-0 q/k/v table for the 1.7B geometry with
     bf16, Q8_0 or Q4_0 weights (the handles the dataflow driver can run)."""
@@ -311,6 +324,81 @@ def exchange_probe():
     return out
 
 
+def timeline(args, torch, dev):
+    """Per-phase timeline of a dataflow frame kernel, from libqp_timeline.so
+    (the same sources built with QP_TIMELINE: thread 0 of every workgroup
+    writes the 100 MHz real-time counter at each phase's start, when its
+    inputs are staged and at its end, into the taps buffer).  Four frames of
+    the workload; the last is analysed over steps 2-15 (one position each).
+    Per phase type: the hand-off (from the last workgroup to end the previous
+    phase to the first one with its inputs staged), the median work (staged
+    inputs to end), and the spread until the last workgroup ends."""
+    import numpy as np
+    from rvq_codebook_code_amd import binding as bd
+    from rvq_codebook_code_amd import build as bb
+    lib = bd.load_library(bb.TIMELINE_LIB)
+    wl = synth.WORKLOADS[args.workload]
+    g = wl.geom
+    B = args.batch or wl.batch
+    W = synth.make_weights(g, wl.weight_seed)
+    pred = bd.Predictor(W, g, max_batch=B)
+    H, q0 = synth.make_inputs(g, B, 4, wl.input_seed)
+    nph = 400
+    buf = torch.zeros(256 * nph * 3, dtype=torch.int64, device=dev)
+    tok = torch.zeros((B, 15), dtype=torch.int32, device=dev)
+    emb = torch.zeros((B, g.d_talker), dtype=torch.float32, device=dev)
+    flags = bd.QP_FLAG_FLOW if args.flow else 0
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    for f in range(4):
+        buf.zero_()
+        Hd = torch.from_numpy(H[f]).to(dev)
+        qd = torch.from_numpy(q0[f]).to(dev)
+        st = lib.qp_run_frames_ex(pred.h, B, Hd.data_ptr(), qd.data_ptr(), tok.data_ptr(), emb.data_ptr(), stream,
+                                  None, None, buf.data_ptr(), flags)
+        if st != 0:
+            raise RuntimeError(f"qp_run_frames_ex failed ({st})")
+        torch.cuda.synchronize()
+    if pred.get_error() != 0:
+        raise RuntimeError("device flags raised during the timeline frames")
+    driver = "flow" if (args.flow or B >= 3) else "dataflow"
+    pred.close()
+    T = buf.cpu().numpy().reshape(256, nph, 3).astype(np.float64)
+    have = T[:, :, 0] > 0
+    t_first = T[have].min()
+    T = np.where(T > 0, (T - t_first) / 100.0, np.nan)          # microseconds
+    L = g.n_layers
+    names = ["qkv", "attn", "o", "up", "down"]
+    per = {n: [] for n in names + ["lm"]}
+    prev_end = None
+    span_phases = 0
+    for ph in range(1, nph):
+        w = np.where(have[:, ph])[0]
+        if len(w) == 0:
+            continue
+        span_phases += 1
+        q = (ph - 1) % (5 * L + 1)
+        s = 1 + (ph - 1) // (5 * L + 1)
+        kind = "lm" if q == 5 * L else names[q % 5]
+        ready = np.nanmin(T[w, ph, 1])
+        end_last = np.nanmax(T[w, ph, 2])
+        if s >= 2 and prev_end is not None:
+            per[kind].append([ready - prev_end, np.nanmedian(T[w, ph, 2] - T[w, ph, 1]),
+                              end_last - np.nanmin(T[w, ph, 2]), end_last - ready])
+        prev_end = end_last
+    span = np.nanmax(T[:, :, 2]) - np.nanmin(T[:, :, 0])
+    out = {"timeline": args.workload, "batch": B, "driver": driver, "frame_span_us": round(float(span), 1),
+           "phases_with_exchange": span_phases, "us_per_phase": round(float(span) / max(span_phases, 1), 3),
+           "per_phase_type_us": {}}
+    for k, v in per.items():
+        if not v:
+            continue
+        a = np.nanmean(np.array(v), axis=0)
+        out["per_phase_type_us"][k] = {"handoff": round(float(a[0]), 2), "work_median": round(float(a[1]), 2),
+                                       "end_spread": round(float(a[2]), 2), "ready_to_last_end": round(float(a[3]), 2),
+                                       "phases": len(v)}
+    print(json.dumps(out), flush=True)
+
+
 def calibrate_copy(torch, dev):
     """A plain copy of COPY_BYTES, five times: the reference for scaling the
     FETCH_SIZE / WRITE_SIZE counters (each launch reads and writes exactly
@@ -344,6 +432,8 @@ def main():
                     help="before every timed frame copy this many MiB (evicting the MALL); the frame alone is timed")
     ap.add_argument("--mfma-peak", action="store_true", help="only run the matrix-core peak probe")
     ap.add_argument("--exchange-probe", action="store_true", help="only run the tagged-record hand-off probe")
+    ap.add_argument("--timeline", action="store_true",
+                    help="per-phase timeline of the workload's dataflow kernel (libqp_timeline.so)")
     ap.add_argument("--tiled", action="store_true", help="the batched matrix-core path at any B")
     ap.add_argument("--only", action="store_true",
                     help="time the named workload alone (by default the b1 line also times b16 and b128)")
@@ -368,6 +458,9 @@ def main():
         return
     if args.exchange_probe:
         exchange_probe()
+        return
+    if args.timeline:
+        timeline(args, torch, dev)
         return
     if args.mfma_peak:
         print(json.dumps({"mfma_peak_bf16_tflops": mfma_peak(), "vendor_dense_bf16_tflops": MFMA_BF16_PEAK_TFLOPS}),
@@ -463,9 +556,10 @@ def measure(name, args, torch, dev, bd):
     table = driver in ("dataflow", "flow", "tiled") and has_qkv0_table(g)
     nbytes = algorithmic_bytes(g, B, qkv0_table=table)
     nflops = algorithmic_flops(g, B, qkv0_table=table)
-    # the unreduced model: every step streams layer 0's q/k/v weights too
+    # the unreduced models: every step streams layer 0's q/k/v weights too;
+    # the flops of the whole frame, the prefill's second row and attention included
     nbytes_full = algorithmic_bytes(g, B, qkv0_table=False)
-    nflops_full = algorithmic_flops(g, B, qkv0_table=False)
+    nflops_full = model_flops(g, B)
     # achieved: per call, over the mean event-pair duration around each call
     # (the dataflow driver: exactly one kernel launch; the batched driver: the
     # staging copies and the graph replay of the frame's kernels); the

@@ -1,9 +1,13 @@
 """Compile the HIP library in-tree for gfx950.
 
 ``python -m rvq_codebook_code_amd.build`` (or ``build()``) runs hipcc on
-``csrc/qp.hip`` and writes ``rvq_codebook_code_amd/libqp.so``, and on
-``csrc/probe_mfma.hip`` and ``csrc/probe_exchange.hip`` (the matrix-core
-peak and record hand-off probes bench.py can run) for ``libqp_probe.so``.  hipcc cross-compiles without a GPU.
+``csrc/qp.hip`` and writes ``rvq_codebook_code_amd/libqp.so``; on the same
+source with ``QP_TIMELINE`` defined for ``libqp_timeline.so`` (the dataflow
+kernels stamp each phase's start, staged inputs and end into the taps buffer;
+``bench.py --timeline`` reads it); and on ``csrc/probe_mfma.hip`` and
+``csrc/probe_exchange.hip`` (the matrix-core peak and record hand-off probes
+bench.py can run) for ``libqp_probe.so``.  The three compile in parallel.
+hipcc cross-compiles without a GPU.
 """
 from __future__ import annotations
 
@@ -40,36 +44,35 @@ def hipcc() -> str:
 
 
 PROBE_LIB = os.path.join(PKG, "libqp_probe.so")
+TIMELINE_LIB = os.path.join(PKG, "libqp_timeline.so")
 
 
-def _hipcc(src: str, out: str, verbose: bool) -> None:
-    tmp = out + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", src, "-o", tmp]
+def _start(srcs, out: str, extra, verbose: bool):
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, f"-I{INCLUDE}", f"-I{CSRC}", *srcs, "-o", out + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
-    os.replace(tmp, out)
-
-
-def _hipcc_many(srcs, out: str, verbose: bool) -> None:
-    tmp = out + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", *srcs, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
-    os.replace(tmp, out)
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
 
 
 def build(verbose: bool = False) -> str:
-    """The library (libqp.so) and the matrix-core peak probe (libqp_probe.so)."""
-    _hipcc(os.path.join(CSRC, "qp.hip"), LIB, verbose)
-    _hipcc_many([os.path.join(CSRC, "probe_mfma.hip"), os.path.join(CSRC, "probe_exchange.hip")], PROBE_LIB, verbose)
+    """The library (libqp.so), its timeline build (libqp_timeline.so) and the
+    probes (libqp_probe.so), compiled in parallel."""
+    jobs = [
+        (LIB, _start([os.path.join(CSRC, "qp.hip")], LIB, [], verbose)),
+        (TIMELINE_LIB, _start([os.path.join(CSRC, "qp.hip")], TIMELINE_LIB, ["-DQP_TIMELINE"], verbose)),
+        (PROBE_LIB, _start([os.path.join(CSRC, "probe_mfma.hip"), os.path.join(CSRC, "probe_exchange.hip")],
+                           PROBE_LIB, [], verbose)),
+    ]
+    failed = []
+    for out, proc in jobs:
+        log, _ = proc.communicate()
+        if proc.returncode != 0:
+            sys.stderr.write(log)
+            failed.append((os.path.basename(out), proc.returncode))
+        else:
+            os.replace(out + ".tmp", out)
+    if failed:
+        raise RuntimeError(f"hipcc failed: {failed}")
     return LIB
 
 

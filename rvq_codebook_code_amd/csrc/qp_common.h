@@ -20,6 +20,27 @@ constexpr int kMaxRowsPerChunk = 4;
 enum WeightType : int { WT_F32 = 0, WT_BF16 = 1, WT_Q8 = 2, WT_Q4 = 3 };
 
 // Device error flag bits (also documented in qp.h).
+// Phase timeline of the dataflow kernels, in a separate build of the same
+// sources (libqp_timeline.so, compiled with QP_TIMELINE): thread 0 of
+// workgroup wg writes the GPU's 100 MHz real-time counter at three points of
+// phase ph (k = 0: the phase starts, 1: its inputs are staged, 2: its
+// stores are issued) into the caller's taps buffer, read as uint64
+// [256][kTimelinePhases][3].  That build writes no residual taps.  The
+// product build compiles none of it.
+constexpr int kTimelinePhases = 400;
+#ifdef QP_TIMELINE
+constexpr bool kWriteTaps = false;
+#define QP_STAMP(taps, wg, ph, k)                                                                         \
+    do {                                                                                                  \
+        if ((taps) && threadIdx.x == 0 && (ph) < ::qp::kTimelinePhases)                                   \
+            reinterpret_cast<unsigned long long*>(taps)[(static_cast<size_t>(wg) * ::qp::kTimelinePhases + \
+                                                         (ph)) * 3 + (k)] = __builtin_amdgcn_s_memrealtime(); \
+    } while (0)
+#else
+constexpr bool kWriteTaps = true;
+#define QP_STAMP(taps, wg, ph, k) ((void)0)
+#endif
+
 constexpr unsigned kErrBadQ0 = 1u;
 constexpr unsigned kErrBadForced = 2u;
 constexpr unsigned kErrBarrierTimeout = 4u;

@@ -12,6 +12,14 @@
 // lane: the per-unit pull of tagged records runs about three times faster
 // than with 4 waves x 8 loads).
 //
+// Waiting: before a phase polls its rows, wave 0 alone waits for the first
+// record of row 0 to carry the phase's tag (one 16-byte load per lane per
+// attempt), the other waves at a barrier; then all sixteen poll their rows in
+// full.  Most workgroups sit out several phases (the owners' O and down,
+// the attention units), and sixteen waves polling whole rows through those
+// waits took fabric bandwidth from the phases in flight (B = 16: 10,240 ->
+// 11,360 frames/s with the gate).
+//
 // Products: [rows x K] . [K x 16] fragments on v_mfma_f32_16x16x32_bf16 over
 // the batched path's fragment-ordered weights (qp_tiled.h), held in
 // registers one active phase ahead; the 16 waves split K and their partial
@@ -205,6 +213,28 @@ __device__ __forceinline__ void poll_row(const uint64_t* rec, uint32_t tag, uint
         if (!__any(pend != 0u || spend)) break;
         if (!stream::spin_wait(spins, err)) break;
     }
+}
+
+// Wave 0 alone waits until some record of row `rec` carries `tag` (one
+// 16-byte load per lane per attempt, its chunks in turn); every wave then
+// meets at the barrier and polls its own row in full.  A workgroup that
+// waits long for a phase thus polls with one wave instead of sixteen, and
+// the fabric is left to the phases in flight.
+template <int NJ>
+__device__ __forceinline__ void gate_row(const uint64_t* rec, uint32_t tag, unsigned* err) {
+    if ((threadIdx.x >> 6) == 0) {
+        const int lane = threadIdx.x & 63;
+        const rsrc_t r = stream::wrsrc(rec, NJ * 1024);
+        uint32_t probe = 0;
+        unsigned spins = 0;
+        while (true) {
+            const auto u = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16u, 1024u * probe, kDeviceScope);
+            if (__any(static_cast<uint32_t>(u[1]) == tag || static_cast<uint32_t>(u[3]) == tag)) break;
+            probe = probe + 1 == NJ ? 0 : probe + 1;
+            if (!stream::spin_wait(spins, err)) break;
+        }
+    }
+    __syncthreads();
 }
 
 template <int NJ>
@@ -440,13 +470,16 @@ __global__ __launch_bounds__(kThreadsF) void k_flow(Model m, RunArgs a, Recs rc,
             if (!(l == 0 && s > 1)) {
                 const uint32_t tin = (l == 0) ? tag_of(0) : tag_of(ph_layer(L, s, l - 1, T_DOWN));
                 const uint32_t tout = tag_of(ph_layer(L, s, l, T_QKV));
+                QP_STAMP(a.taps, wg, ph_layer(L, s, l, T_QKV), 0);
                 #pragma unroll
                 for (int rf = 0; rf < 2; ++rf) {
                     if (rf >= nrf) break;
                     const int row = 16 * rf + wave;
+                    if (rf == 0) gate_row<DP / 256>(rc.XG, tin, err);
                     poll_row<DP / 256>(rc.XG + static_cast<size_t>(row) * (DP / 2), tin, stage + wave * kSRow, err,
                                        rc.SS, 16 * rf, M - 16 * rf, ss_s, row < M);
                     __syncthreads();
+                    if (rf == 0) QP_STAMP(a.taps, wg, ph_layer(L, s, l, T_QKV), 1);
                     if (row < M) row_scale();
                     red[0][wave][lane] = mfma_slice<2>(stage, wave, lane, wb, f32x4_t{0.f, 0.f, 0.f, 0.f});
                     __syncthreads();
@@ -460,12 +493,14 @@ __global__ __launch_bounds__(kThreadsF) void k_flow(Model m, RunArgs a, Recs rc,
                     }
                     __syncthreads();
                 }
+                QP_STAMP(a.taps, wg, ph_layer(L, s, l, T_QKV), 2);
                 stream::sched_fence();
                 if (own) load_o(l); else load_u(l);
                 stream::sched_fence();
             }
             // ================= ATTN(l): units (request ub, kv head ug)
             if (unit) {
+                QP_STAMP(a.taps, wg, ph_layer(L, s, l, T_ATTN), 0);
                 float* sf = reinterpret_cast<float*>(stage);
                 float* hist = sf;                  // K [16][HD], then V [16][HD] at 2048
                 float* nd = sf + 4096;             // head vectors [2 positions][4][HD]
@@ -510,6 +545,7 @@ __global__ __launch_bounds__(kThreadsF) void k_flow(Model m, RunArgs a, Recs rc,
                 }
                 __builtin_amdgcn_s_waitcnt(0);
                 __syncthreads();
+                QP_STAMP(a.taps, wg, ph_layer(L, s, l, T_ATTN), 1);
                 if (wave < 2) {
                     const int h = 2 * ug + wave;
                     const float* gq = qk_s[l][0];
@@ -595,17 +631,21 @@ __global__ __launch_bounds__(kThreadsF) void k_flow(Model m, RunArgs a, Recs rc,
                     }
                 }
                 __syncthreads();
+                QP_STAMP(a.taps, wg, ph_layer(L, s, l, T_ATTN), 2);
             }
             // ================= O(l): owners, x += W_o . attention
             if (own) {
                 const uint32_t tin = tag_of(ph_layer(L, s, l, T_ATTN));
+                QP_STAMP(a.taps, wg, ph_layer(L, s, l, T_O), 0);
                 #pragma unroll
                 for (int rf = 0; rf < 2; ++rf) {
                     if (rf >= nrf) break;
                     const int row = 16 * rf + wave;
+                    if (rf == 0) gate_row<QD / 256>(rc.AO, tin, err);
                     if (row < M) poll_row<QD / 256>(rc.AO + static_cast<size_t>(row) * (QD / 2), tin, stage + wave * kSRow, err);
                     else zero_row<QD / 256>(stage + wave * kSRow);
                     __syncthreads();
+                    if (rf == 0) QP_STAMP(a.taps, wg, ph_layer(L, s, l, T_O), 1);
                     red[0][wave][lane] = mfma_slice<4>(stage, wave, lane, wb, f32x4_t{0.f, 0.f, 0.f, 0.f});
                     __syncthreads();
                     if (wave < 4) {
@@ -614,6 +654,7 @@ __global__ __launch_bounds__(kThreadsF) void k_flow(Model m, RunArgs a, Recs rc,
                     }
                     __syncthreads();
                 }
+                QP_STAMP(a.taps, wg, ph_layer(L, s, l, T_O), 2);
                 stream::sched_fence();
                 load_d(l);
                 stream::sched_fence();
@@ -622,13 +663,16 @@ __global__ __launch_bounds__(kThreadsF) void k_flow(Model m, RunArgs a, Recs rc,
             if (up_role) {
                 const uint32_t tin = tag_of(ph_layer(L, s, l, T_O));
                 const uint32_t tout = tag_of(ph_layer(L, s, l, T_UP));
+                QP_STAMP(a.taps, wg, ph_layer(L, s, l, T_UP), 0);
                 #pragma unroll
                 for (int rf = 0; rf < 2; ++rf) {
                     if (rf >= nrf) break;
                     const int row = 16 * rf + wave;
+                    if (rf == 0) gate_row<DP / 256>(rc.XG, tin, err);
                     poll_row<DP / 256>(rc.XG + static_cast<size_t>(row) * (DP / 2), tin, stage + wave * kSRow, err,
                                        rc.SS, 16 * rf, M - 16 * rf, ss_s, row < M);
                     __syncthreads();
+                    if (rf == 0) QP_STAMP(a.taps, wg, ph_layer(L, s, l, T_UP), 1);
                     if (row < M) row_scale();
                     red[0][wave][lane] = mfma_slice<2>(stage, wave, lane, wb, f32x4_t{0.f, 0.f, 0.f, 0.f});
                     red[1][wave][lane] = mfma_slice<2>(stage, wave, lane, wb + 2, f32x4_t{0.f, 0.f, 0.f, 0.f});
@@ -647,6 +691,7 @@ __global__ __launch_bounds__(kThreadsF) void k_flow(Model m, RunArgs a, Recs rc,
                     }
                     __syncthreads();
                 }
+                QP_STAMP(a.taps, wg, ph_layer(L, s, l, T_UP), 2);
                 stream::sched_fence();
                 if (l + 1 < L) load_q(l + 1);
                 else if (lm_role) load_l(s);
@@ -658,26 +703,30 @@ __global__ __launch_bounds__(kThreadsF) void k_flow(Model m, RunArgs a, Recs rc,
                 const uint32_t tin = tag_of(ph_layer(L, s, l, T_UP));
                 const uint32_t tout = tag_of(ph_layer(L, s, l, T_DOWN));
                 const int gnext = (l + 1 < L) ? 2 * (l + 1) : 2 * kMaxL;   // gain row of the next reader
+                QP_STAMP(a.taps, wg, ph_layer(L, s, l, T_DOWN), 0);
                 #pragma unroll
                 for (int rf = 0; rf < 2; ++rf) {
                     if (rf >= nrf) break;
                     const int row = 16 * rf + wave;
+                    if (rf == 0) gate_row<F / 256>(rc.HH, tin, err);
                     if (row < M) poll_row<F / 256>(rc.HH + static_cast<size_t>(row) * (F / 2), tin, stage + wave * kSRow, err);
                     else zero_row<F / 256>(stage + wave * kSRow);
                     __syncthreads();
+                    if (rf == 0) QP_STAMP(a.taps, wg, ph_layer(L, s, l, T_DOWN), 1);
                     red[0][wave][lane] = mfma_slice<6>(stage, wave, lane, wb, f32x4_t{0.f, 0.f, 0.f, 0.f});
                     __syncthreads();
                     if (wave < 4) {
                         xr[rf] += reduce(0);
                         publish_x(rf, M, gnext, tout);
                         const int r = 16 * rf + erw;
-                        if (a.taps && r < M) {
+                        if (kWriteTaps && a.taps && r < M) {
                             const int pos = row_pos(s, B, r), bb = row_req(s, B, r);
                             a.taps[((static_cast<size_t>(pos) * L + l) * B + bb) * DP + ocol] = xr[rf];
                         }
                     }
                     __syncthreads();
                 }
+                QP_STAMP(a.taps, wg, ph_layer(L, s, l, T_DOWN), 2);
                 stream::sched_fence();
                 if (l + 1 < L) load_q(l + 1);
                 else if (s < kSteps) load_o(0);
@@ -689,9 +738,12 @@ __global__ __launch_bounds__(kThreadsF) void k_flow(Model m, RunArgs a, Recs rc,
             const uint32_t tin = tag_of(ph_layer(L, s, L - 1, T_DOWN));
             const uint32_t tout = tag_of(ph_lm(L, s));
             const int r0 = (s == 1) ? B : 0;
+            QP_STAMP(a.taps, wg, ph_lm(L, s), 0);
+            gate_row<DP / 256>(rc.XG + static_cast<size_t>(r0) * (DP / 2), tin, err);
             poll_row<DP / 256>(rc.XG + static_cast<size_t>(r0 + wave) * (DP / 2), tin, stage + wave * kSRow, err,
                                rc.SS, r0, B, ss_s, wave < B);
             __syncthreads();
+            QP_STAMP(a.taps, wg, ph_lm(L, s), 1);
             if (wave < B) row_scale();
             red[0][wave][lane] = mfma_slice<2>(stage, wave, lane, wb, f32x4_t{0.f, 0.f, 0.f, 0.f});
             __syncthreads();
@@ -714,6 +766,7 @@ __global__ __launch_bounds__(kThreadsF) void k_flow(Model m, RunArgs a, Recs rc,
                 }
             }
             __syncthreads();
+            QP_STAMP(a.taps, wg, ph_lm(L, s), 2);
             stream::sched_fence();
             if (s < kSteps) load_u(0);
             stream::sched_fence();

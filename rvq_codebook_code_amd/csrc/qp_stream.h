@@ -518,6 +518,7 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
             } else {
                 const int par = ph & 1;
                 float* xs = slot[par];
+                QP_STAMP(a.taps, wg, ph, 0);
                 if (l == 0) {
                     if (s == 1) {
                         gather_x(rc.X, B, tag_of(0), par);
@@ -550,6 +551,7 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                     gather_x(rc.X, M, tag_of(ph - 1), par);
                 }
                 __syncthreads();
+                QP_STAMP(a.taps, wg, ph, 1);
                 if (l == 0) {
 #pragma unroll
                     for (int r = 0; r < MR; ++r) xr[r] = (r < M) ? xs[r * DP + 4 * wg + wave] : 0.f;
@@ -573,11 +575,13 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                     for (int q = 0; q < 4; ++q) v = (lane == q) ? acc[q] * rinv : v;
                     if (lane < 4) st_rec(rc.QKV + static_cast<size_t>(r) * NQKV + 16 * wg + 4 * wave + lane, v, tag_of(ph));
                 }
+                QP_STAMP(a.taps, wg, ph, 2);
                 ++ph;
             }
             // ================= ATTN(l) =================
             {
                 const int par = ph & 1;
+                if (wg < B * NKV) QP_STAMP(a.taps, wg, ph, 0);
                 float* hist = slot[par];
                 const bool unit = wg < B * NKV;
                 const int b = wg / NKV, g = wg % NKV;
@@ -615,6 +619,7 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                     __builtin_amdgcn_s_waitcnt(0);
                 }
                 __syncthreads();
+                if (unit) QP_STAMP(a.taps, wg, ph, 1);
                 if (unit && wave < 2) {
                     // one wave per query head; all <= 16 scores at once: key t on
                     // lanes 4t..4t+3, each lane a 32-wide slice of the head
@@ -713,6 +718,7 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                 load_wO(l);
                 if (!unit) load_wU(l);
                 sched_fence();
+                if (unit) QP_STAMP(a.taps, wg, ph, 2);
                 ++ph;
             }
             // ================= O(l) =================
@@ -720,8 +726,10 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                 const int par = ph & 1;
                 float* as = slot[par];
                 const uint32_t tg = tag_of(ph - 1);
+                QP_STAMP(a.taps, wg, ph, 0);
                 for (int r = 0; r < M; ++r) (void)poll_share<QD>(rc.AO + static_cast<size_t>(r) * QD, wave, tg, as + r * QD, err);
                 __syncthreads();
+                QP_STAMP(a.taps, wg, ph, 1);
                 const int n = 4 * wg + wave;
                 for (int r = 0; r < M; ++r) {
                     float acc = 0.f;
@@ -743,14 +751,17 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                 sched_fence();
                 if (wg < B * NKV) load_wU(l);
                 sched_fence();
+                QP_STAMP(a.taps, wg, ph, 2);
                 ++ph;
             }
             // ================= UP(l) =================
             {
                 const int par = ph & 1;
                 float* xs = slot[par];
+                QP_STAMP(a.taps, wg, ph, 0);
                 gather_x(rc.X, M, tag_of(ph - 1), par);
                 __syncthreads();
+                QP_STAMP(a.taps, wg, ph, 1);
                 const float* gf = g_ffn(l);
                 for (int r = 0; r < M; ++r) {
                     float ag[3] = {0.f, 0.f, 0.f}, au[3] = {0.f, 0.f, 0.f};
@@ -782,6 +793,7 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                 sched_fence();
                 load_wD(l);
                 sched_fence();
+                QP_STAMP(a.taps, wg, ph, 2);
                 ++ph;
             }
             // ================= DOWN(l) =================
@@ -789,8 +801,10 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                 const int par = ph & 1;
                 float* hs = slot[par];
                 const uint32_t tg = tag_of(ph - 1);
+                QP_STAMP(a.taps, wg, ph, 0);
                 for (int r = 0; r < M; ++r) (void)poll_share<F>(rc.H + static_cast<size_t>(r) * F, wave, tg, hs + r * F, err);
                 __syncthreads();
+                QP_STAMP(a.taps, wg, ph, 1);
                 const int n = 4 * wg + wave;
                 for (int r = 0; r < M; ++r) {
                     float acc = 0.f;
@@ -809,7 +823,7 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                         if (i == r) { xr[i] += d; nv = xr[i]; }
                     if (lane == 0) {
                         st_rec(rc.X + static_cast<size_t>(r) * DP + n, nv, tag_of(ph));
-                        if (a.taps) {
+                        if (kWriteTaps && a.taps) {
                             const int pos = (s == 1) ? (r >= B ? 1 : 0) : s;
                             const int bb = (s == 1 && r >= B) ? r - B : r;
                             a.taps[((static_cast<size_t>(pos) * L + l) * B + bb) * DP + n] = nv;
@@ -819,6 +833,7 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                 sched_fence();
                 if (l + 1 < L) load_wQ(l + 1); else load_wL(s);
                 sched_fence();
+                QP_STAMP(a.taps, wg, ph, 2);
                 ++ph;
             }
         }
@@ -827,8 +842,10 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
             const int par = ph & 1;
             float* xs = slot[par];
             const int r0 = (s == 1) ? B : 0;
+            QP_STAMP(a.taps, wg, ph, 0);
             gather_x(rc.X + static_cast<size_t>(r0) * DP, B, tag_of(ph - 1), par);
             __syncthreads();
+            QP_STAMP(a.taps, wg, ph, 1);
             const int v0 = 8 * wg + 2 * wave;
 #pragma unroll
             for (int b = 0; b < BM; ++b) {
@@ -874,6 +891,7 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
             sched_fence();
             if (s < kSteps && !t0) load_wQ(0);
             sched_fence();
+            QP_STAMP(a.taps, wg, ph, 2);
             ++ph;
         }
     }

@@ -96,3 +96,14 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_model_flops_of_the_frame():
+    """Whole-frame flops of the 1.7B geometry at B = 128: 16 positions
+    through 5 layers, 15 lm_head rows, W_p once, attention over 1..16 cached
+    positions (2 x 16 heads x 128 x 136 multiply-adds per layer)."""
+    g = synth.WORKLOADS["b128"].geom
+    per_layer = 4096 * 1024 + 1024 * 2048 + 2 * 3072 * 1024 + 1024 * 3072
+    macs = 16 * 5 * per_layer + 15 * 2048 * 1024 + 1024 * 2048 + 5 * 2 * 2048 * 136
+    assert macs == 1_294_630_912
+    assert bench.model_flops(g, 128) == 2 * 128 * macs == 331_425_513_472
