@@ -494,8 +494,12 @@ __global__ __launch_bounds__(kThreadsF) void k_flow(Model m, RunArgs a, Recs rc,
                     __syncthreads();
                 }
                 QP_STAMP(a.taps, wg, ph_layer(L, s, l, T_QKV), 2);
+                // the attention units fetch their gate/up weights after
+                // attention: requested here, they would sit ahead of the
+                // units' polls in the CU's in-order memory queue
                 stream::sched_fence();
-                if (own) load_o(l); else load_u(l);
+                if (own) load_o(l);
+                else if (!unit) load_u(l);
                 stream::sched_fence();
             }
             // ================= ATTN(l): units (request ub, kv head ug)
@@ -632,6 +636,11 @@ __global__ __launch_bounds__(kThreadsF) void k_flow(Model m, RunArgs a, Recs rc,
                 }
                 __syncthreads();
                 QP_STAMP(a.taps, wg, ph_layer(L, s, l, T_ATTN), 2);
+                if (!(l == 0 && s > 1)) {   // layer 0 of later steps: fetched after the last lm_head
+                    stream::sched_fence();
+                    load_u(l);
+                    stream::sched_fence();
+                }
             }
             // ================= O(l): owners, x += W_o . attention
             if (own) {

@@ -181,6 +181,26 @@ __device__ __forceinline__ float poll_share(const uint64_t* row, int wave, uint3
     return wave_sum(ss);
 }
 
+// Wave 0 alone waits until some record of the first NC KiB at rec carries
+// tag (one 16-byte load per lane per attempt, its chunks in turn); then all
+// waves meet at the barrier.
+template <int NC>
+__device__ __forceinline__ void gate_rec(const uint64_t* rec, uint32_t tag, unsigned* err) {
+    if ((threadIdx.x >> 6) == 0) {
+        const int lane = threadIdx.x & 63;
+        const rsrc_t r = wrsrc(rec, NC * 1024);
+        uint32_t probe = 0;
+        unsigned spins = 0;
+        while (true) {
+            const auto u = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16u, 1024u * probe, kDeviceScope);
+            if (__any(static_cast<uint32_t>(u[1]) == tag || static_cast<uint32_t>(u[3]) == tag)) break;
+            probe = probe + 1 == NC ? 0 : probe + 1;
+            if (!spin_wait(spins, err)) break;
+        }
+    }
+    __syncthreads();
+}
+
 // One head vector (HD = 128 tagged records) -> dst[0..128).
 __device__ __forceinline__ void poll_head(const uint64_t* src, uint32_t tag, float* dst, unsigned* err) {
     const int lane = threadIdx.x & 63;
@@ -727,6 +747,7 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                 float* as = slot[par];
                 const uint32_t tg = tag_of(ph - 1);
                 QP_STAMP(a.taps, wg, ph, 0);
+                if (wg >= B * NKV) gate_rec<QD / 128>(rc.AO, tg, err);
                 for (int r = 0; r < M; ++r) (void)poll_share<QD>(rc.AO + static_cast<size_t>(r) * QD, wave, tg, as + r * QD, err);
                 __syncthreads();
                 QP_STAMP(a.taps, wg, ph, 1);
