@@ -399,6 +399,53 @@ def timeline(args, torch, dev):
     print(json.dumps(out), flush=True)
 
 
+def batch_mix(args, torch, dev):
+    """Frames whose batch size changes from call to call, enqueued back to back
+    with no synchronisation (as a scheduler that fills each frame with the
+    requests at hand would), against the same frames at a fixed batch: the
+    handle's prepared graphs serve every batch size without capture or
+    allocation, so a changing B costs only the size of its bucket."""
+    from rvq_codebook_code_amd import binding as bd
+    wl = synth.WORKLOADS[args.workload]
+    g = wl.geom
+    sizes = [int(x) for x in args.batch_mix.split(",")]
+    Bmax = max(sizes)
+    W = synth.make_weights(g, wl.weight_seed)
+    H, q0 = synth.make_inputs(g, Bmax, 4, wl.input_seed)
+    pred = bd.Predictor(W, g, max_batch=Bmax)
+    Hd = torch.from_numpy(H).to(dev)
+    qd = torch.from_numpy(q0).to(dev)
+    tok = torch.zeros((Bmax, 15), dtype=torch.int32, device=dev)
+    emb = torch.zeros((Bmax, g.d_talker), dtype=torch.float32, device=dev)
+
+    def run(seq):
+        for i, B in enumerate(seq):
+            pred.run(Hd[i % 4, :B], qd[i % 4, :B], tok[:B], emb[:B])
+
+    def timed(seq):
+        run(seq[:len(sizes)])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run(seq)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3
+    reps = max(1, args.steps // len(sizes))
+    mixed = sizes * reps
+    ms_mixed = timed(mixed)
+    fixed = {}
+    for B in sorted(set(sizes)):
+        fixed[B] = timed([B] * reps) / reps
+    ms_sum_fixed = sum(fixed[B] for B in sizes) * reps
+    if pred.get_error() != 0:
+        raise RuntimeError("device flags raised during the batch mix")
+    pred.close()
+    print(json.dumps({"batch_mix": sizes, "workload": args.workload, "calls": len(mixed),
+                      "ms_mixed_sequence": round(ms_mixed, 3),
+                      "ms_same_calls_each_size_alone": round(ms_sum_fixed, 3),
+                      "ms_per_call_by_size": {str(B): round(v, 4) for B, v in fixed.items()},
+                      "frames_per_s_mixed": round(sum(mixed) / ms_mixed * 1e3, 1)}), flush=True)
+
+
 def calibrate_copy(torch, dev):
     """A plain copy of COPY_BYTES, five times: the reference for scaling the
     FETCH_SIZE / WRITE_SIZE counters (each launch reads and writes exactly
@@ -432,6 +479,8 @@ def main():
                     help="before every timed frame copy this many MiB (evicting the MALL); the frame alone is timed")
     ap.add_argument("--mfma-peak", action="store_true", help="only run the matrix-core peak probe")
     ap.add_argument("--exchange-probe", action="store_true", help="only run the tagged-record hand-off probe")
+    ap.add_argument("--batch-mix", default=None,
+                    help="comma-separated batch sizes cycled call by call (e.g. 1,3,16,40,128)")
     ap.add_argument("--timeline", action="store_true",
                     help="per-phase timeline of the workload's dataflow kernel (libqp_timeline.so)")
     ap.add_argument("--tiled", action="store_true", help="the batched matrix-core path at any B")
@@ -461,6 +510,9 @@ def main():
         return
     if args.timeline:
         timeline(args, torch, dev)
+        return
+    if args.batch_mix:
+        batch_mix(args, torch, dev)
         return
     if args.mfma_peak:
         print(json.dumps({"mfma_peak_bf16_tflops": mfma_peak(), "vendor_dense_bf16_tflops": MFMA_BF16_PEAK_TFLOPS}),
