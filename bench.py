@@ -362,11 +362,22 @@ def timeline(args, torch, dev):
         raise RuntimeError("device flags raised during the timeline frames")
     driver = "flow" if (args.flow or B >= 3) else "dataflow"
     pred.close()
-    T = buf.cpu().numpy().reshape(256, nph, 3).astype(np.float64)
+    out = {"timeline": args.workload, "batch": B, "driver": driver}
+    out.update(analyze_timeline(buf.cpu().numpy().reshape(256, nph, 3), g.n_layers))
+    print(json.dumps(out), flush=True)
+
+
+def analyze_timeline(stamps, L: int) -> dict:
+    """Per-phase-type statistics of one frame's stamps [workgroups][phases][3]
+    (raw 100 MHz counter values, 0 where a workgroup took no part): phase ph
+    of step s, layer l, type t is 1 + (s - 1) (5 L + 1) + 5 l + t, the lm_head
+    of step s 1 + (s - 1) (5 L + 1) + 5 L.  Steps 2-15 are averaged."""
+    import numpy as np
+    T = stamps.astype(np.float64)
+    nph = T.shape[1]
     have = T[:, :, 0] > 0
     t_first = T[have].min()
     T = np.where(T > 0, (T - t_first) / 100.0, np.nan)          # microseconds
-    L = g.n_layers
     names = ["qkv", "attn", "o", "up", "down"]
     per = {n: [] for n in names + ["lm"]}
     prev_end = None
@@ -386,9 +397,8 @@ def timeline(args, torch, dev):
                               end_last - np.nanmin(T[w, ph, 2]), end_last - ready])
         prev_end = end_last
     span = np.nanmax(T[:, :, 2]) - np.nanmin(T[:, :, 0])
-    out = {"timeline": args.workload, "batch": B, "driver": driver, "frame_span_us": round(float(span), 1),
-           "phases_with_exchange": span_phases, "us_per_phase": round(float(span) / max(span_phases, 1), 3),
-           "per_phase_type_us": {}}
+    out = {"frame_span_us": round(float(span), 1), "phases_with_exchange": span_phases,
+           "us_per_phase": round(float(span) / max(span_phases, 1), 3), "per_phase_type_us": {}}
     for k, v in per.items():
         if not v:
             continue
@@ -396,7 +406,7 @@ def timeline(args, torch, dev):
         out["per_phase_type_us"][k] = {"handoff": round(float(a[0]), 2), "work_median": round(float(a[1]), 2),
                                        "end_spread": round(float(a[2]), 2), "ready_to_last_end": round(float(a[3]), 2),
                                        "phases": len(v)}
-    print(json.dumps(out), flush=True)
+    return out
 
 
 def batch_mix(args, torch, dev):

@@ -107,3 +107,38 @@ def test_model_flops_of_the_frame():
     macs = 16 * 5 * per_layer + 15 * 2048 * 1024 + 1024 * 2048 + 5 * 2 * 2048 * 136
     assert macs == 1_294_630_912
     assert bench.model_flops(g, 128) == 2 * 128 * macs == 331_425_513_472
+
+
+def test_timeline_analysis_on_built_stamps():
+    """A hand-built frame of stamps for one layer: every phase of steps 2..15
+    starts 10 us after the previous one ends, its inputs are staged 1 us (first
+    workgroup) to 2 us (last) after that, and it ends 3 us (first) to 4 us
+    (last) after its start; so each hand-off is 10 + 1 us, the median work 2
+    us, the end spread 1 us and staged-to-last-end 3 us."""
+    import numpy as np
+    L = 1
+    nph = 15 * (5 * L + 1)                       # phases 1..90 of steps 1..15
+    T = np.zeros((4, 400, 3), dtype=np.int64)
+    t = 1000.0                                   # microseconds
+    for ph in range(1, nph + 1):
+        s = 1 + (ph - 1) // (5 * L + 1)
+        q = (ph - 1) % (5 * L + 1)
+        if s >= 2 and q == 0:
+            continue                             # layer 0's q/k/v: no exchange from step 2 on
+        for w in range(4):
+            start = t + 10.0
+            T[w, ph, 0] = int(round(start * 100))
+            T[w, ph, 1] = int(round((start + 1.0 + w / 3.0) * 100))
+            T[w, ph, 2] = int(round((start + 3.0 + w / 3.0) * 100))
+        t = t + 10.0 + 4.0
+    out = bench.analyze_timeline(T, L)
+    per = out["per_phase_type_us"]
+    assert set(per) == {"attn", "o", "up", "down", "lm"}       # q/k/v of layer 0 never stamped after step 1
+    for k, v in per.items():
+        # last producer ended at prev_start + 4; first consumer staged at prev_start + 14 + 1
+        assert abs(v["handoff"] - 11.0) < 1e-6, (k, v)
+        assert abs(v["work_median"] - 2.0) < 1e-6
+        assert abs(v["end_spread"] - 1.0) < 1e-6
+        assert abs(v["ready_to_last_end"] - 3.0) < 1e-6
+        assert v["phases"] == 14
+    assert out["phases_with_exchange"] == nph - 14
