@@ -1327,7 +1327,13 @@ qp_status qp_create(const qp_weights* w, const qp_geometry* g, int32_t device, q
                     up.msg = "hipMemset of the record buffers failed";
                 }
             }
-            // layer 0's q/k/v rows of every table row (k_qkv0, after k_ptab)
+            // layer 0's q/k/v rows of every table row (k_qkv0, after k_ptab);
+            // the batched path's layer-0 attention then also moves each
+            // request to its token, a slice of kTokPer elements per thread
+            // and kv head
+            static_assert(S::DT <= qp::tiled::kTokPer * qp::tiled::kThreadsT * S::NKV &&
+                              S::DP <= qp::tiled::kTokPer * qp::tiled::kThreadsT * S::NKV,
+                          "token move slices exceed the registers set aside for them");
             qkv0 = static_cast<float*>(up.alloc(static_cast<size_t>(kSteps - 1) * m.V * m.nqkv * 4));
             m.qkv0 = qkv0;
         }

@@ -560,14 +560,16 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(GemmArgs g) {
 // (dT and dP are multiples of 256 and at most 4096); callers issue every
 // load before any store so that one memory round trip covers a row.
 constexpr int kMaxPer = 16;
+// elements per thread of a workgroup's slice of the token move (k_attn with
+// the token decision): the layer-0 table, and with it that variant, exists
+// only for geometries whose slices fit (checked where the table is built)
+constexpr int kTokPer = 1;
 
 // x, xg = bf16(g * x) and the per-16-column sums of x^2 of residual-stream
 // row `row` from values v (with gains gv) already in registers; a
-// fragment's sum is reduced over the 16 threads that own it.  with_norm =
-// false writes x only (a row whose next reader is a residual add, not a
-// product).
+// fragment's sum is reduced over the 16 threads that own it.
 __device__ __forceinline__ void store_row(const TokArgs& ta, int row, const float (&v)[kMaxPer],
-                                          const float (&gv)[kMaxPer], bool with_norm = true) {
+                                          const float (&gv)[kMaxPer]) {
     const int j = threadIdx.x, np = ta.dP / kThreadsT;
     float* xr = ta.x + static_cast<size_t>(row) * ta.dP;
     // element j + 256 i: 256 columns on is eight 32-wide blocks on in
@@ -580,7 +582,6 @@ __device__ __forceinline__ void store_row(const TokArgs& ta, int row, const floa
         if (i < np) {
             const int n = j + kThreadsT * i;
             xr[n] = v[i];
-            if (!with_norm) continue;
             gr[i * gstep] = to_bf16(gv[i] * v[i]);
             float q = v[i] * v[i];
             q += __shfl_xor(q, 1, 64);
@@ -722,20 +723,59 @@ __global__ __launch_bounds__(kThreadsT, HD <= 128 ? 4 : 3) void k_attn(AttnArgs 
             hv[i] = m.vc[off];
         }
     }
+    // the history into LDS
+    auto stash_history = [&]() {
+#pragma unroll
+        for (int i = 0; i < HPT; ++i) {
+            const int idx = threadIdx.x + kThreadsT * i;
+            if (idx < pf * HD) {
+                const int t = idx / HD, d = idx - t * HD;
+                Ks[t][d] = hk[i];
+                Vs[t][d] = hv[i];
+            }
+        }
+    };
     // layer 0 with the table: the previous step's token first (the history
-    // loads above are in flight meanwhile); kv head 0's workgroup also moves
-    // the request to the token: embsum += E[t], residual row = P[t]
+    // loads above are in flight meanwhile).  The request's move to the token
+    // (embsum += E[t], residual row = P[t]) is shared by its nkv workgroups,
+    // each taking a contiguous slice of both rows: a single workgroup doing
+    // all of it ended about 6 us after the others at B = 128.
     const TokArgs& ta = m.tok;
     int fed = -1;
-    float o_es[TOK ? kMaxPer : 1], o_e[TOK ? kMaxPer : 1], o_v[TOK ? kMaxPer : 1], o_gv[TOK ? kMaxPer : 1];
-    const int ne = ta.dT / kThreadsT, np = ta.dP / kThreadsT;
+    float o_es[TOK ? kTokPer : 1], o_v[TOK ? kTokPer : 1];
+    uint32_t o_e[TOK ? kTokPer : 1];    // E[t] elements as loaded: bf16 or fp32 bits
+    const int eT = (ta.dT + nkv - 1) / nkv, eP = (ta.dP + nkv - 1) / nkv;   // slice lengths
+    const int cT = g * eT, cP = g * eP;                                     // slice starts
+    // this thread's element i of a slice [c0, c0 + len) of a row of n, or -1
+    auto slot = [&](int i, int len, int c0, int n) {
+        const int e = threadIdx.x + kThreadsT * i;
+        return (e < len && c0 + e < n) ? c0 + e : -1;
+    };
+    float* const es_row = ta.embsum + static_cast<size_t>(b) * ta.dT;
+    // Every load below is issued unconditionally from an in-range address (a
+    // missing element reads element 0 and is not stored) and converted only
+    // where it is used: with a branch or a conversion beside each load the
+    // compiler waited for every load before issuing the next.
     if constexpr (TOK) {
-        if (g == 0) load_vec(ta.embsum + static_cast<size_t>(b) * ta.dT, ne, o_es);
+#pragma unroll
+        for (int i = 0; i < kTokPer; ++i) o_es[i] = es_row[max(slot(i, eT, cT, ta.dT), 0)];
         fed = decide_fed(ta, b, g == 0, red_s, &fed_s);
-        if (g == 0) {
-            load_emb(ta, fed, o_e);
-            load_vec(ta.ptab + static_cast<size_t>(fed) * ta.dP, np, o_v);
+        // the history arrived before the keys (a wave's loads return in
+        // order): into LDS now, freeing its registers for the loads below
+        stash_history();
+        const size_t erow = static_cast<size_t>(fed) * ta.dT;
+        if (ta.emb_bf16) {
+            const uint16_t* E = static_cast<const uint16_t*>(ta.emb) + erow;
+#pragma unroll
+            for (int i = 0; i < kTokPer; ++i) o_e[i] = E[max(slot(i, eT, cT, ta.dT), 0)];
+        } else {
+            const uint32_t* E = static_cast<const uint32_t*>(ta.emb) + erow;
+#pragma unroll
+            for (int i = 0; i < kTokPer; ++i) o_e[i] = E[max(slot(i, eT, cT, ta.dT), 0)];
         }
+        const float* prow = ta.ptab + static_cast<size_t>(fed) * ta.dP;
+#pragma unroll
+        for (int i = 0; i < kTokPer; ++i) o_v[i] = prow[max(slot(i, eP, cP, ta.dP), 0)];
     }
     // the step's q/k/v row of position pi: from the table when fed >= 0
     auto qkv_row = [&](int pi) {
@@ -767,28 +807,21 @@ __global__ __launch_bounds__(kThreadsT, HD <= 128 ? 4 : 3) void k_attn(AttnArgs 
             for (int j = 0; j < J; ++j) qin[pi][j] = row[(g * grp + wave) * HD + lane + 64 * j];
         }
     }
-    // the request's move to the token (its loads were issued before the head
-    // vectors', so this waits for nothing the attention does not need)
+    // this workgroup's share of the request's move to the token (its loads
+    // were issued before the head vectors', so this waits for nothing the
+    // attention does not need); the residual row's next reader is layer 0's
+    // residual add (its q/k/v come from the table), so x alone
     if constexpr (TOK) {
-        if (g == 0) {
-            float* es_row = ta.embsum + static_cast<size_t>(b) * ta.dT;
+        float* x_row = ta.x + static_cast<size_t>(b) * ta.dP;
 #pragma unroll
-            for (int i = 0; i < kMaxPer; ++i)
-                if (i < ne) es_row[threadIdx.x + kThreadsT * i] = o_es[i] + o_e[i];
-            // the row's next reader is layer 0's residual add (its q/k/v
-            // come from the table), so x alone
-            store_row(ta, b, o_v, o_gv, false);
+        for (int i = 0; i < kTokPer; ++i) {
+            const int jt = slot(i, eT, cT, ta.dT), jp = slot(i, eP, cP, ta.dP);
+            const float e = __uint_as_float(ta.emb_bf16 ? o_e[i] << 16 : o_e[i]);
+            if (jt >= 0) es_row[jt] = o_es[i] + e;
+            if (jp >= 0) x_row[jp] = o_v[i];
         }
     }
-#pragma unroll
-    for (int i = 0; i < HPT; ++i) {
-        const int idx = threadIdx.x + kThreadsT * i;
-        if (idx < pf * HD) {
-            const int t = idx / HD, d = idx - t * HD;
-            Ks[t][d] = hk[i];
-            Vs[t][d] = hv[i];
-        }
-    }
+    if constexpr (!TOK) stash_history();
 
     for (int pi = 0; pi < npos; ++pi) {
         const int p = pf + pi;
