@@ -343,6 +343,8 @@ def timeline(args, torch, dev):
     W = synth.make_weights(g, wl.weight_seed)
     pred = bd.Predictor(W, g, max_batch=B)
     H, q0 = synth.make_inputs(g, B, 4, wl.input_seed)
+    if select_driver(g, B, args) == "tiled":
+        return kernel_timeline(args, torch, dev, lib, pred, H, q0, B)
     nph = 400
     buf = torch.zeros(256 * nph * 3, dtype=torch.int64, device=dev)
     tok = torch.zeros((B, 15), dtype=torch.int32, device=dev)
@@ -365,6 +367,82 @@ def timeline(args, torch, dev):
     out = {"timeline": args.workload, "batch": B, "driver": driver}
     out.update(analyze_timeline(buf.cpu().numpy().reshape(256, nph, 3), g.n_layers))
     print(json.dumps(out), flush=True)
+
+
+TL_NAMES = {1: "proj", 2: "qkv", 3: "attn", 4: "attn_tok", 5: "o", 6: "swiglu", 7: "down", 8: "lm", 9: "start",
+            10: "next"}
+TL_LAUNCHES, TL_WGS = 448, 1024
+
+
+def kernel_timeline(args, torch, dev, lib, pred, H, q0, B):
+    """Kernel timeline of the batched path (libqp_timeline.so): four frames
+    through the prepared graph, as the bench runs them; thread 0 of every
+    workgroup stamps each kernel's start, the end of a product's K loop and
+    its end.  The last frame is summarised per kernel role."""
+    import ctypes as C
+    import numpy as np
+    g = pred.geom
+    tok = torch.zeros((B, 15), dtype=torch.int32, device=dev)
+    emb = torch.zeros((B, g.d_talker), dtype=torch.float32, device=dev)
+    for f in range(4):
+        pred.run(torch.from_numpy(H[f]).to(dev), torch.from_numpy(q0[f]).to(dev), tok, emb, tiled=args.tiled)
+    torch.cuda.synchronize()
+    if pred.get_error() != 0:
+        raise RuntimeError("device flags raised during the timeline frames")
+    stamps = np.zeros(TL_LAUNCHES * TL_WGS * 3, dtype=np.uint64)
+    kinds = (C.c_int * TL_LAUNCHES)()
+    lib.qp_timeline_tiled.argtypes = [C.c_void_p, C.c_size_t, C.POINTER(C.c_int), C.c_int]
+    lib.qp_timeline_tiled.restype = C.c_int
+    n = lib.qp_timeline_tiled(stamps.ctypes.data, stamps.nbytes, kinds, TL_LAUNCHES)
+    if n < 0:
+        raise RuntimeError("qp_timeline_tiled failed")
+    pred.close()
+    out = {"timeline": args.workload, "batch": B, "driver": "tiled"}
+    out.update(analyze_kernel_timeline(stamps.reshape(TL_LAUNCHES, TL_WGS, 3)[:n], list(kinds)[:n]))
+    print(json.dumps(out), flush=True)
+
+
+def analyze_kernel_timeline(stamps, kinds) -> dict:
+    """Per-role statistics of one frame's kernel stamps [launches][workgroups][3]
+    (raw 100 MHz counter values; k = 0 start, 1 end of a product's K loop,
+    2 end; 0 where no workgroup wrote).  A launch's span runs from its first
+    workgroup's start to its last one's end, its gap from the previous
+    launch's last end to its first start.  Workgroups that started before the
+    frame's first launch (left from an earlier frame of another shape) are
+    ignored."""
+    import numpy as np
+    T = stamps.astype(np.float64)
+    first = T[0, :, 0]
+    t0 = first[first > 0].min()
+    per = {}
+    prev_end = None
+    tot_span = tot_gap = 0.0
+    for i in range(T.shape[0]):
+        w = T[i][(T[i, :, 0] >= t0) & (T[i, :, 2] > 0)]
+        if len(w) == 0:
+            continue
+        start, end = w[:, 0].min(), w[:, 2].max()
+        rec = per.setdefault(TL_NAMES.get(kinds[i], str(kinds[i])), {"span": [], "gap": [], "ramp": [], "wg": [],
+                                                                      "loop": []})
+        rec["span"].append((end - start) / 100.0)
+        rec["ramp"].append((w[:, 0].max() - start) / 100.0)
+        rec["wg"].append(float(np.median(w[:, 2] - w[:, 0])) / 100.0)
+        if (w[:, 1] > 0).all():
+            rec["loop"].append(float(np.median(w[:, 1] - w[:, 0])) / 100.0)
+        tot_span += (end - start) / 100.0
+        if prev_end is not None:
+            rec["gap"].append((start - prev_end) / 100.0)
+            tot_gap += (start - prev_end) / 100.0
+        prev_end = end
+    frame = (prev_end - t0) / 100.0
+    out = {"frame_span_us": round(frame, 1), "kernels": int(sum(len(r["span"]) for r in per.values())),
+           "kernel_time_us": round(tot_span, 1), "gap_time_us": round(tot_gap, 1), "per_kernel_us": {}}
+    for k, r in per.items():
+        m = lambda v: round(float(np.mean(v)), 2) if v else None
+        out["per_kernel_us"][k] = {"launches": len(r["span"]), "span": m(r["span"]), "gap_before": m(r["gap"]),
+                                   "start_ramp": m(r["ramp"]), "workgroup_median": m(r["wg"]),
+                                   "k_loop_median": m(r["loop"]), "total": round(float(np.sum(r["span"])), 1)}
+    return out
 
 
 def analyze_timeline(stamps, L: int) -> dict:
@@ -456,6 +534,37 @@ def batch_mix(args, torch, dev):
                       "frames_per_s_mixed": round(sum(mixed) / ms_mixed * 1e3, 1)}), flush=True)
 
 
+LIBRARY_GEMM_SHAPES = ("qkv", "o", "gateup", "down")
+
+
+def library_gemm(args, torch, dev):
+    """The vendor library (torch.mm, hipBLASLt on this image) on one of the
+    1.7B-shaped predictor's bf16 products, [B x K] . [K x N], for comparison
+    with the batched path's kernels under a kernel trace: q/k/v [1024 x 4096],
+    output projection [2048 x 1024], gate and up as one [1024 x 6144] product,
+    down [3072 x 1024].  Eight weight copies are used in turn (64-96 MiB, so
+    they are not all L2-resident), 400 calls back to back after 20 warm-up
+    calls; the JSON line gives the host-side time per call."""
+    shapes = {"qkv": (1024, 4096), "o": (2048, 1024), "gateup": (1024, 6144), "down": (3072, 1024)}
+    K, N = shapes[args.library_gemm]
+    M = args.batch or 128
+    gen = torch.Generator(device=dev).manual_seed(7)
+    A = torch.randn(M, K, device=dev, dtype=torch.bfloat16, generator=gen)
+    Ws = [torch.randn(K, N, device=dev, dtype=torch.bfloat16, generator=gen) for _ in range(8)]
+    out = torch.empty(M, N, device=dev, dtype=torch.bfloat16)
+    for i in range(20):
+        torch.mm(A, Ws[i % 8], out=out)
+    torch.cuda.synchronize()
+    n = 400
+    t0 = time.perf_counter()
+    for i in range(n):
+        torch.mm(A, Ws[i % 8], out=out)
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) / n * 1e6
+    print(json.dumps({"library_gemm": args.library_gemm, "M": M, "K": K, "N": N, "calls": n,
+                      "host_us_per_call": round(us, 2)}), flush=True)
+
+
 def calibrate_copy(torch, dev):
     """A plain copy of COPY_BYTES, five times: the reference for scaling the
     FETCH_SIZE / WRITE_SIZE counters (each launch reads and writes exactly
@@ -492,8 +601,11 @@ def main():
     ap.add_argument("--batch-mix", default=None,
                     help="comma-separated batch sizes cycled call by call (e.g. 1,3,16,40,128)")
     ap.add_argument("--timeline", action="store_true",
-                    help="per-phase timeline of the workload's dataflow kernel (libqp_timeline.so)")
+                    help="per-phase timeline of the workload's dataflow kernel, or the kernel timeline of "
+                         "the batched path (libqp_timeline.so)")
     ap.add_argument("--tiled", action="store_true", help="the batched matrix-core path at any B")
+    ap.add_argument("--library-gemm", choices=LIBRARY_GEMM_SHAPES,
+                    help="torch.mm (the vendor library) on one of the predictor's product shapes at --batch rows")
     ap.add_argument("--only", action="store_true",
                     help="time the named workload alone (by default the b1 line also times b16 and b128)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -520,6 +632,9 @@ def main():
         return
     if args.timeline:
         timeline(args, torch, dev)
+        return
+    if args.library_gemm:
+        library_gemm(args, torch, dev)
         return
     if args.batch_mix:
         batch_mix(args, torch, dev)

@@ -615,6 +615,25 @@ namespace {
 
 // --- batched matrix-core path ---------------------------------------------
 
+// Launch indices of a frame's kernels for the timeline build (QP_TSTAMP):
+// launch_tiled numbers its launches from 0 in order and records each one's
+// role; every other build numbers nothing.  Host-side state of that
+// measurement build only, not safe for concurrent captures.
+enum TlKind : int { TL_PROJ = 1, TL_QKV, TL_ATTN, TL_ATTN_TOK, TL_O, TL_SWIGLU, TL_DOWN, TL_LM, TL_START, TL_NEXT };
+#ifdef QP_TIMELINE
+int g_tl_next = 0;
+int g_tl_kind[qp::kTiledLaunches];
+void tl_reset() { g_tl_next = 0; }
+int tl_index(int kind) {
+    const int i = g_tl_next++;
+    if (i < qp::kTiledLaunches) g_tl_kind[i] = kind;
+    return i;
+}
+#else
+void tl_reset() {}
+int tl_index(int) { return -1; }
+#endif
+
 // Launches one product; returns the number of column tiles (gridDim.x).
 // h: any handle with the split-K scratch (t_part, t_part_floats, t_ctr, t_nctr).
 template <int WT, int SRC, int EPI, class Handle>
@@ -713,7 +732,10 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
     ta.ptab = m.ptab;
     ta.qkv = m.qkv;
     ta.nqkv = m.nqkv;
+    tl_reset();
+    ta.tl = tl_index(TL_START);
     hipLaunchKernelGGL(T::k_start, dim3(nb), dim3(T::kThreadsT), 0, stream, ta);
+    ta.tl = -1;
     T::AttnArgs aa{};
     aa.B = B;
     aa.frag = frag;
@@ -744,6 +766,7 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
     g.xg = h->t_xg;
     g.g_next = gain0;
     g.ss_out = h->t_ss;
+    g.tl = tl_index(TL_PROJ);
     tiled_gemm<WT, T::SRC_F32, T::EPI_BIAS>(h, g, stream);
     uint16_t* ao = reinterpret_cast<uint16_t*>(m.ao);
     uint16_t* hb = reinterpret_cast<uint16_t*>(m.hb);
@@ -768,6 +791,7 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
                 g.w0 = h->t_qkv[l];
                 g.out = m.qkv;
                 g.ldo = m.nqkv;
+                g.tl = tl_index(TL_QKV);
                 tiled_gemm<WT, T::SRC_BF16_NORM, T::EPI_SCALE>(h, g, stream);
             }
             // attention (layer 0 from step 2 on, with the table: also the
@@ -775,6 +799,7 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
             aa.s = s;
             aa.l = l;
             aa.tok_on = (l == 0 && s > 1 && m.qkv0) ? 1 : 0;
+            aa.tl = tl_index(aa.tok_on ? TL_ATTN_TOK : TL_ATTN);
             aa.k_norm = L.k_norm;
             aa.q_norm = L.q_norm;
             aa.ao = ao;
@@ -807,6 +832,7 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
             g.xg = h->t_xg;
             g.g_next = L.ffn_norm;
             g.ss_out = h->t_ss;
+            g.tl = tl_index(TL_O);
             tiled_gemm<WT, T::SRC_BF16, T::EPI_RESID>(h, g, stream);
             // h = silu(W_g . RMSNorm(x)) * (W_u . RMSNorm(x)), bf16
             g = T::GemmArgs{};
@@ -822,6 +848,7 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
             g.w0 = h->t_gate[l];
             g.w1 = h->t_up[l];
             g.outb = hb;
+            g.tl = tl_index(TL_SWIGLU);
             tiled_gemm<WT, T::SRC_BF16_NORM, T::EPI_SWIGLU>(h, g, stream);
             // x += W_d . h (and the residual tap); publishes the next reader's operand
             g = T::GemmArgs{};
@@ -843,6 +870,7 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
             g.tap_l = l;
             g.tap_L = m.L;
             g.tap_B = B;
+            g.tl = tl_index(TL_DOWN);
             tiled_gemm<WT, T::SRC_BF16, T::EPI_RESID>(h, g, stream);
         }
         // lm_head[s-1] . RMSNorm(x at position s) -> per-tile argmax keys
@@ -867,6 +895,7 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
             g.logits = h->t_logits;
             g.logit_ld = m.V;
         }
+        g.tl = tl_index(TL_LM);
         ta.nkt = tiled_gemm<WT, T::SRC_BF16_NORM, T::EPI_ARGMAX>(h, g, stream);
         if (a.uniforms) {
             // the step's token drawn from its logits with the caller's uniform
@@ -884,7 +913,9 @@ qp_status launch_tiled(qp_handle* h, const RunArgs& a, hipStream_t stream) {
             // reads its q/k/v rows from the table: no k_next launch
             aa.tok = ta;
         } else {
+            ta.tl = tl_index(TL_NEXT);
             hipLaunchKernelGGL(T::k_next, dim3(nb), dim3(T::kThreadsT), 0, stream, ta);
+            ta.tl = -1;
         }
     }
     if (!check_hip(hipGetLastError(), "batched path kernel launch", &st)) return st;
@@ -1634,3 +1665,19 @@ void qp_destroy(qp_handle* h) {
 
 // the Talker decode step (include/qp_talker.h)
 #include "qp_talker_host.h"
+
+#ifdef QP_TIMELINE
+// Timeline build only (QP_TSTAMP): copies the batched path's kernel stamps,
+// uint64 [kTiledLaunches][kTiledWgs][3] (at most `bytes` of them), and the
+// role (TlKind) of each launch of the frame last captured or launched (at
+// most `cap`); returns the number of launches in that frame, or -1 if the
+// copy fails.
+extern "C" int qp_timeline_tiled(void* stamps, size_t bytes, int* kinds, int cap) {
+    const size_t n = std::min(bytes, sizeof(qp::g_tiled_stamps));
+    if (hipDeviceSynchronize() != hipSuccess) return -1;
+    if (hipMemcpyFromSymbol(stamps, HIP_SYMBOL(qp::g_tiled_stamps), n, 0, hipMemcpyDeviceToHost) != hipSuccess)
+        return -1;
+    for (int i = 0; i < cap && i < qp::kTiledLaunches; ++i) kinds[i] = g_tl_kind[i];
+    return g_tl_next;
+}
+#endif

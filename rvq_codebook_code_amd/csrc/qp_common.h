@@ -41,6 +41,29 @@ constexpr bool kWriteTaps = true;
 #define QP_STAMP(taps, wg, ph, k) ((void)0)
 #endif
 
+// Kernel timeline of the batched path, in the same timeline build: every
+// kernel launch of a frame carries its index (tl, -1 elsewhere), and thread
+// 0 of each workgroup (linear id below kTiledWgs) writes the real-time
+// counter at its start (k = 0), at the end of a product's K loop (k = 1) and
+// at its end (k = 2) into a device array of [kTiledLaunches][kTiledWgs][3],
+// read back with qp_timeline_tiled.  The graph replays of a frame overwrite
+// it; the product build compiles none of it.
+constexpr int kTiledLaunches = 448, kTiledWgs = 1024;
+#ifdef QP_TIMELINE
+__device__ unsigned long long g_tiled_stamps[kTiledLaunches * kTiledWgs * 3];
+#define QP_TSTAMP(tl, k)                                                                                     \
+    do {                                                                                                     \
+        if (threadIdx.x == 0 && (tl) >= 0 && (tl) < ::qp::kTiledLaunches) {                                  \
+            const int lin_ = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);                 \
+            if (lin_ < ::qp::kTiledWgs)                                                                      \
+                ::qp::g_tiled_stamps[(static_cast<size_t>(tl) * ::qp::kTiledWgs + lin_) * 3 + (k)] =         \
+                    __builtin_amdgcn_s_memrealtime();                                                        \
+        }                                                                                                    \
+    } while (0)
+#else
+#define QP_TSTAMP(tl, k) ((void)0)
+#endif
+
 constexpr unsigned kErrBadQ0 = 1u;
 constexpr unsigned kErrBadForced = 2u;
 constexpr unsigned kErrBarrierTimeout = 4u;

@@ -110,6 +110,7 @@ struct GemmArgs {
     float* part;            // split-K partial tiles
     uint32_t part_bytes;
     unsigned* ctr;          // split-K arrival counters, one per tile, left at 0
+    int tl = -1;            // launch index in the frame (timeline build)
 };
 
 // Arguments of the token-step kernels, resolved on the host per launch and
@@ -137,6 +138,7 @@ struct TokArgs {
     const float* qkv0;
     float* qkv;
     int nqkv;
+    int tl = -1;                      // launch index in the frame (timeline build)
 };
 
 struct AttnArgs {
@@ -156,6 +158,7 @@ struct AttnArgs {
     // k_next, and the head vectors come from tok.qkv0 [V][nqkv]
     int tok_on;
     TokArgs tok;
+    int tl = -1;                      // launch index in the frame (timeline build)
 };
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -238,6 +241,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(GemmArgs g) {
     __shared__ f32x4_t red[NW][RT][CT][64];
     __shared__ int last_s;
 
+    QP_TSTAMP(g.tl, 0);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int bx = blockIdx.x, by = blockIdx.y, kz = blockIdx.z;
@@ -401,6 +405,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(GemmArgs g) {
     for (; kb + 4 <= kb1; kb += 4) batch(kb, std::integral_constant<int, 4>{});
     for (; kb < kb1; kb += 2) batch(kb, std::integral_constant<int, 2>{});
 
+    QP_TSTAMP(g.tl, 1);
     // ---- reduce the four waves' K ranges, in wave order ----
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
@@ -449,7 +454,10 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(GemmArgs g) {
             last_s = last;
         }
         __syncthreads();
-        if (!last_s) return;
+        if (!last_s) {
+            QP_TSTAMP(g.tl, 2);
+            return;
+        }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             if (rt % NW != wave) continue;
@@ -554,6 +562,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(GemmArgs g) {
             }
         }
     }
+    QP_TSTAMP(g.tl, 2);
 }
 
 // Row helpers of the token steps.  Thread j owns elements j, j + 256, ...
@@ -701,6 +710,7 @@ __global__ __launch_bounds__(kThreadsT, HD <= 128 ? 4 : 3) void k_attn(AttnArgs 
     __shared__ float es[4][kPositions];
     __shared__ uint64_t red_s[kThreadsT / 64];
     __shared__ int fed_s;
+    QP_TSTAMP(m.tl, 0);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int B = m.B, s = m.s, l = m.l;
@@ -898,12 +908,14 @@ __global__ __launch_bounds__(kThreadsT, HD <= 128 ? 4 : 3) void k_attn(AttnArgs 
         }
         __syncthreads();
     }
+    QP_TSTAMP(m.tl, 2);
 }
 
 // Frame start, per request: check q0, x[pos 1] = P_0[q0], embsum = E_0[q0].
 // (x[pos 0] = W_p . H + b_p is a product of its own.)
 __global__ __launch_bounds__(kThreadsT) void k_start(TokArgs ta) {
     __shared__ int tok_s;
+    QP_TSTAMP(ta.tl, 0);
     const int B = ta.B, ne = ta.dT / kThreadsT, np = ta.dP / kThreadsT;
     float gv[kMaxPer], v[kMaxPer], e[kMaxPer];
     load_vec(ta.gain0, np, gv);
@@ -927,6 +939,7 @@ __global__ __launch_bounds__(kThreadsT) void k_start(TokArgs ta) {
         for (int i = 0; i < kMaxPer; ++i)
             if (i < ne) es[threadIdx.x + kThreadsT * i] = e[i];
     }
+    QP_TSTAMP(ta.tl, 2);
 }
 
 // Step s's token per request from the lm_head tiles' keys; the fed-back
@@ -936,6 +949,7 @@ __global__ __launch_bounds__(kThreadsT) void k_start(TokArgs ta) {
 __global__ __launch_bounds__(kThreadsT) void k_next(TokArgs ta) {
     __shared__ uint64_t red[kThreadsT / 64];
     __shared__ int fed_s;
+    QP_TSTAMP(ta.tl, 0);
     const int B = ta.B;
     const int ne = ta.dT / kThreadsT, np = ta.dP / kThreadsT;
     float gv[kMaxPer], o[kMaxPer], v[kMaxPer], e[kMaxPer];
@@ -956,6 +970,7 @@ __global__ __launch_bounds__(kThreadsT) void k_next(TokArgs ta) {
             if (i < ne) es[threadIdx.x + kThreadsT * i] = o[i] + e[i];
         if (ta.ptab) store_row(ta, b, v, gv);
     }
+    QP_TSTAMP(ta.tl, 2);
 }
 
 }  // namespace tiled

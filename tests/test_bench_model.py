@@ -12,6 +12,8 @@ import os
 import subprocess
 import sys
 
+import numpy as np
+
 import bench
 from rvq_codebook_code_amd import synth
 
@@ -142,3 +144,30 @@ def test_timeline_analysis_on_built_stamps():
         assert abs(v["ready_to_last_end"] - 3.0) < 1e-6
         assert v["phases"] == 14
     assert out["phases_with_exchange"] == nph - 14
+
+
+def test_kernel_timeline_analysis_on_built_stamps():
+    """The batched path's kernel timeline on hand-built stamps (100 MHz
+    counter values): three launches, one stale workgroup left from before the
+    frame, gaps and spans worked out by hand."""
+    S = np.zeros((3, 8, 3), dtype=np.uint64)
+    S[0, 0] = (1000, 0, 1500)                       # k_start: no K loop
+    S[0, 1] = (1010, 0, 1520)
+    S[1, 0] = (1700, 2000, 2300)                    # q/k/v product
+    S[1, 1] = (1720, 2010, 2310)
+    S[1, 2] = (1730, 2050, 2400)
+    S[2, 0] = (500, 0, 900)                         # stale: before the frame
+    S[2, 1] = (2600, 0, 3000)                       # attention
+    S[2, 2] = (2650, 0, 3100)
+    out = bench.analyze_kernel_timeline(S, [9, 2, 3])
+    assert out["frame_span_us"] == 21.0
+    assert out["kernels"] == 3
+    assert out["kernel_time_us"] == 17.2
+    assert out["gap_time_us"] == 3.8
+    k = out["per_kernel_us"]
+    assert k["start"] == {"launches": 1, "span": 5.2, "gap_before": None, "start_ramp": 0.1,
+                          "workgroup_median": 5.05, "k_loop_median": None, "total": 5.2}
+    assert k["qkv"] == {"launches": 1, "span": 7.0, "gap_before": 1.8, "start_ramp": 0.3,
+                        "workgroup_median": 6.0, "k_loop_median": 3.0, "total": 7.0}
+    assert k["attn"] == {"launches": 1, "span": 5.0, "gap_before": 2.0, "start_ramp": 0.5,
+                         "workgroup_median": 4.25, "k_loop_median": None, "total": 5.0}
