@@ -539,12 +539,13 @@ LIBRARY_GEMM_SHAPES = ("qkv", "o", "gateup", "down")
 
 def library_gemm(args, torch, dev):
     """The vendor library (torch.mm, hipBLASLt on this image) on one of the
-    1.7B-shaped predictor's bf16 products, [B x K] . [K x N], for comparison
-    with the batched path's kernels under a kernel trace: q/k/v [1024 x 4096],
-    output projection [2048 x 1024], gate and up as one [1024 x 6144] product,
-    down [3072 x 1024].  Eight weight copies are used in turn (64-96 MiB, so
-    they are not all L2-resident), 400 calls back to back after 20 warm-up
-    calls; the JSON line gives the host-side time per call."""
+    1.7B-shaped predictor's bf16 products, [B x K] . [K x N], in the regime the
+    batched path's frames run in: 100 products captured in one graph and
+    replayed back to back.  Shapes: q/k/v [1024 x 4096], output projection
+    [2048 x 1024], gate and up as one [1024 x 6144] product, down
+    [3072 x 1024].  Eight weight copies are used in turn (64-96 MiB, more than
+    the L2s hold).  The JSON line gives the time per product over 20 replays
+    (kernel and the gap before the next one); the outputs are not used."""
     shapes = {"qkv": (1024, 4096), "o": (2048, 1024), "gateup": (1024, 6144), "down": (3072, 1024)}
     K, N = shapes[args.library_gemm]
     M = args.batch or 128
@@ -552,17 +553,32 @@ def library_gemm(args, torch, dev):
     A = torch.randn(M, K, device=dev, dtype=torch.bfloat16, generator=gen)
     Ws = [torch.randn(K, N, device=dev, dtype=torch.bfloat16, generator=gen) for _ in range(8)]
     out = torch.empty(M, N, device=dev, dtype=torch.bfloat16)
-    for i in range(20):
-        torch.mm(A, Ws[i % 8], out=out)
+    per_graph = 100
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        for i in range(20):
+            torch.mm(A, Ws[i % 8], out=out)
+    torch.cuda.current_stream(dev).wait_stream(side)
     torch.cuda.synchronize()
-    n = 400
-    t0 = time.perf_counter()
-    for i in range(n):
-        torch.mm(A, Ws[i % 8], out=out)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(per_graph):
+            torch.mm(A, Ws[i % 8], out=out)
+    for _ in range(3):
+        graph.replay()
     torch.cuda.synchronize()
-    us = (time.perf_counter() - t0) / n * 1e6
-    print(json.dumps({"library_gemm": args.library_gemm, "M": M, "K": K, "N": N, "calls": n,
-                      "host_us_per_call": round(us, 2)}), flush=True)
+    reps = 20
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * per_graph)
+    print(json.dumps({"library_gemm": args.library_gemm, "M": M, "K": K, "N": N, "products_per_graph": per_graph,
+                      "replays": reps, "us_per_product_in_graph": round(us, 3),
+                      "tflops": round(2.0 * M * K * N / us / 1e6, 2)}), flush=True)
 
 
 def calibrate_copy(torch, dev):
