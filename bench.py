@@ -324,6 +324,30 @@ def exchange_probe():
     return out
 
 
+def boundary_probe():
+    """Microseconds per kernel of back-to-back launches of a trivial kernel
+    (libqp_probe.so): in one replayed graph or on a stream, with no work or
+    writing / reading a buffer, over 200 launches of 256-thread workgroups."""
+    import ctypes as C
+    lib = C.CDLL(os.path.join(ROOT, "rvq_codebook_code_amd", "libqp_probe.so"))
+    lib.qp_probe_boundary.argtypes = [C.c_int, C.c_int, C.c_size_t, C.c_int, C.c_int, C.c_int, C.POINTER(C.c_float)]
+    lib.qp_probe_boundary.restype = C.c_int
+    names = {0: "no work", 1: "writes", 2: "reads"}
+    out = []
+    cases = [(0, b, 0) for b in (256, 512, 1024)] + [(1, 512, n) for n in (1 << 16, 1 << 18, 1 << 20, 1 << 22)] + \
+            [(2, 512, n) for n in (1 << 20, 1 << 23)]
+    for graph in (1, 0):
+        for kind, blocks, n in cases:
+            us = C.c_float()
+            rc = lib.qp_probe_boundary(kind, blocks, n, 200, graph, 5, C.byref(us))
+            if rc != 0:
+                raise RuntimeError(f"boundary probe failed ({rc})")
+            out.append({"launch": "graph" if graph else "stream", "kernel": names[kind], "workgroups": blocks,
+                        "kib": n * 4 // 1024, "us_per_kernel": round(us.value, 3)})
+            print(json.dumps(out[-1]), flush=True)
+    return out
+
+
 def timeline(args, torch, dev):
     """Per-phase timeline of a dataflow frame kernel, from libqp_timeline.so
     (the same sources built with QP_TIMELINE: thread 0 of every workgroup
@@ -614,6 +638,7 @@ def main():
                     help="before every timed frame copy this many MiB (evicting the MALL); the frame alone is timed")
     ap.add_argument("--mfma-peak", action="store_true", help="only run the matrix-core peak probe")
     ap.add_argument("--exchange-probe", action="store_true", help="only run the tagged-record hand-off probe")
+    ap.add_argument("--boundary-probe", action="store_true", help="only run the kernel-boundary probe")
     ap.add_argument("--batch-mix", default=None,
                     help="comma-separated batch sizes cycled call by call (e.g. 1,3,16,40,128)")
     ap.add_argument("--timeline", action="store_true",
@@ -645,6 +670,9 @@ def main():
         return
     if args.exchange_probe:
         exchange_probe()
+        return
+    if args.boundary_probe:
+        boundary_probe()
         return
     if args.timeline:
         timeline(args, torch, dev)

@@ -3,10 +3,12 @@
 ``python -m rvq_codebook_code_amd.build`` (or ``build()``) runs hipcc on
 ``csrc/qp.hip`` and writes ``rvq_codebook_code_amd/libqp.so``; on the same
 source with ``QP_TIMELINE`` defined for ``libqp_timeline.so`` (the dataflow
-kernels stamp each phase's start, staged inputs and end into the taps buffer;
-``bench.py --timeline`` reads it); and on ``csrc/probe_mfma.hip`` and
-``csrc/probe_exchange.hip`` (the matrix-core peak and record hand-off probes
-bench.py can run) for ``libqp_probe.so``.  The three compile in parallel.
+kernels stamp each phase's start, staged inputs and end into the taps buffer,
+the batched path's kernels their start, K-loop end and end into a device
+array; ``bench.py --timeline`` reads them); and on ``csrc/probe_mfma.hip``,
+``csrc/probe_exchange.hip`` and ``csrc/probe_boundary.hip`` (the matrix-core
+peak, record hand-off and kernel-boundary probes bench.py can run) for
+``libqp_probe.so``.  The three compile in parallel.
 hipcc cross-compiles without a GPU.
 """
 from __future__ import annotations
@@ -60,7 +62,8 @@ def build(verbose: bool = False) -> str:
     jobs = [
         (LIB, _start([os.path.join(CSRC, "qp.hip")], LIB, [], verbose)),
         (TIMELINE_LIB, _start([os.path.join(CSRC, "qp.hip")], TIMELINE_LIB, ["-DQP_TIMELINE"], verbose)),
-        (PROBE_LIB, _start([os.path.join(CSRC, "probe_mfma.hip"), os.path.join(CSRC, "probe_exchange.hip")],
+        (PROBE_LIB, _start([os.path.join(CSRC, "probe_mfma.hip"), os.path.join(CSRC, "probe_exchange.hip"),
+                            os.path.join(CSRC, "probe_boundary.hip")],
                            PROBE_LIB, [], verbose)),
     ]
     failed = []
