@@ -401,8 +401,8 @@ TL_LAUNCHES, TL_WGS = 448, 1024
 def kernel_timeline(args, torch, dev, lib, pred, H, q0, B):
     """Kernel timeline of the batched path (libqp_timeline.so): four frames
     through the prepared graph, as the bench runs them; thread 0 of every
-    workgroup stamps each kernel's start, the end of a product's K loop and
-    its end.  The last frame is summarised per kernel role."""
+    workgroup stamps each kernel's start, the end of a product's K loop (or
+    an attention's staged inputs) and its end.  The last frame is summarised per kernel role."""
     import ctypes as C
     import numpy as np
     g = pred.geom
@@ -428,12 +428,12 @@ def kernel_timeline(args, torch, dev, lib, pred, H, q0, B):
 
 def analyze_kernel_timeline(stamps, kinds) -> dict:
     """Per-role statistics of one frame's kernel stamps [launches][workgroups][3]
-    (raw 100 MHz counter values; k = 0 start, 1 end of a product's K loop,
-    2 end; 0 where no workgroup wrote).  A launch's span runs from its first
-    workgroup's start to its last one's end, its gap from the previous
-    launch's last end to its first start.  Workgroups that started before the
-    frame's first launch (left from an earlier frame of another shape) are
-    ignored."""
+    (raw 100 MHz counter values; k = 0 start, 1 end of a product's K loop or
+    an attention's staged inputs (k1), 2 end; 0 where no workgroup wrote).  A
+    launch's span runs from its first workgroup's start to its last one's end,
+    its gap from the previous launch's last end to its first start.
+    Workgroups that started before the frame's first launch (left from an
+    earlier frame of another shape) are ignored."""
     import numpy as np
     T = stamps.astype(np.float64)
     first = T[0, :, 0]
@@ -465,7 +465,7 @@ def analyze_kernel_timeline(stamps, kinds) -> dict:
         m = lambda v: round(float(np.mean(v)), 2) if v else None
         out["per_kernel_us"][k] = {"launches": len(r["span"]), "span": m(r["span"]), "gap_before": m(r["gap"]),
                                    "start_ramp": m(r["ramp"]), "workgroup_median": m(r["wg"]),
-                                   "k_loop_median": m(r["loop"]), "total": round(float(np.sum(r["span"])), 1)}
+                                   "k1_median": m(r["loop"]), "total": round(float(np.sum(r["span"])), 1)}
     return out
 
 

@@ -44,10 +44,11 @@ constexpr bool kWriteTaps = true;
 // Kernel timeline of the batched path, in the same timeline build: every
 // kernel launch of a frame carries its index (tl, -1 elsewhere), and thread
 // 0 of each workgroup (linear id below kTiledWgs) writes the real-time
-// counter at its start (k = 0), at the end of a product's K loop (k = 1) and
-// at its end (k = 2) into a device array of [kTiledLaunches][kTiledWgs][3],
-// read back with qp_timeline_tiled.  The graph replays of a frame overwrite
-// it; the product build compiles none of it.
+// counter at its start (k = 0), at the end of a product's K loop or once an
+// attention's inputs are in LDS (k = 1) and at its end (k = 2) into a device
+// array of [kTiledLaunches][kTiledWgs][3], read back with qp_timeline_tiled.
+// The graph replays of a frame overwrite it; the product build compiles none
+// of it.
 constexpr int kTiledLaunches = 448, kTiledWgs = 1024;
 #ifdef QP_TIMELINE
 __device__ unsigned long long g_tiled_stamps[kTiledLaunches * kTiledWgs * 3];

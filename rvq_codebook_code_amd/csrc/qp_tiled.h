@@ -853,6 +853,7 @@ __global__ __launch_bounds__(kThreadsT, HD <= 128 ? 4 : 3) void k_attn(AttnArgs 
             }
         }
         __syncthreads();
+        if (pi == 0) QP_TSTAMP(m.tl, 1);
         for (int i = wave; i < grp; i += 4) {
             const int h = g * grp + i;
             float qv[J], q[J];

@@ -166,8 +166,8 @@ def test_kernel_timeline_analysis_on_built_stamps():
     assert out["gap_time_us"] == 3.8
     k = out["per_kernel_us"]
     assert k["start"] == {"launches": 1, "span": 5.2, "gap_before": None, "start_ramp": 0.1,
-                          "workgroup_median": 5.05, "k_loop_median": None, "total": 5.2}
+                          "workgroup_median": 5.05, "k1_median": None, "total": 5.2}
     assert k["qkv"] == {"launches": 1, "span": 7.0, "gap_before": 1.8, "start_ramp": 0.3,
-                        "workgroup_median": 6.0, "k_loop_median": 3.0, "total": 7.0}
+                        "workgroup_median": 6.0, "k1_median": 3.0, "total": 7.0}
     assert k["attn"] == {"launches": 1, "span": 5.0, "gap_before": 2.0, "start_ramp": 0.5,
-                         "workgroup_median": 4.25, "k_loop_median": None, "total": 5.0}
+                         "workgroup_median": 4.25, "k1_median": None, "total": 5.0}
