@@ -208,12 +208,17 @@ def cpu_baseline(wl, W, H, q0, budget_s: float, sampling=None, U=None):
     model = O.OracleModel(W, wl.geom)
     B = H.shape[1]
     n = 0
+    outs = []
     t0 = time.perf_counter()
     while True:
         if sampling is None:
-            O.run_frames(model, H[n % H.shape[0]], q0[n % H.shape[0]])
+            r = O.run_frames(model, H[n % H.shape[0]], q0[n % H.shape[0]])
         else:
-            O.run_frames(model, H[n % H.shape[0]], q0[n % H.shape[0]], sampling=sampling, uniforms=U[n % H.shape[0]])
+            r = O.run_frames(model, H[n % H.shape[0]], q0[n % H.shape[0]], sampling=sampling, uniforms=U[n % H.shape[0]])
+        # sampled frames: a draw is decisive when its uniform is not within
+        # 1e-5 (relative) of a boundary of the cumulative distribution
+        outs.append((r["tokens"], r["margin"], DECISIVE_MARGIN) if sampling is None
+                    else (r["tokens"], r["sample_margin"], SAMPLE_DECISIVE_MARGIN))
         n += 1
         el = time.perf_counter() - t0
         if el >= budget_s or n >= H.shape[0]:
@@ -221,7 +226,33 @@ def cpu_baseline(wl, W, H, q0, budget_s: float, sampling=None, U=None):
     return {"value": round(n * B / el, 3), "unit": "frames/s", "cores": int(threads),
             "kind": "oracle", "host": host,
             "sample": f"{n} frame(s) of {B} request(s) of the {wl.name} workload"
-                      f"{' (sampled)' if sampling else ''}, fp64 NumPy, {el:.1f} s"}
+                      f"{' (sampled)' if sampling else ''}, fp64 NumPy, {el:.1f} s"}, outs
+
+
+# a step is decisive when the oracle's top-2 logit margin exceeds this (the
+# bar under which greedy tokens must match bit for bit); for a sampled draw,
+# when its relative margin to the nearest boundary exceeds the second
+DECISIVE_MARGIN = 0.05
+SAMPLE_DECISIVE_MARGIN = 1e-5
+
+
+def free_run_agreement(gpu_tokens, oracle_outs):
+    """Token agreement of free-running GPU frames with the oracle's free run
+    of the same frames: over all tokens, and per row up to its first step
+    that is not decisive (where the two must agree)."""
+    import numpy as np
+    tot = same = rows = rows_ok = 0
+    for g, (t, mg, thr) in zip(gpu_tokens, oracle_outs):
+        g = np.asarray(g, dtype=np.int64)
+        tot += g.size
+        same += int((g == t).sum())
+        for b in range(g.shape[0]):
+            nd = np.nonzero(mg[b] <= thr)[0]
+            k = int(nd[0]) if nd.size else g.shape[1]
+            rows += 1
+            rows_ok += int(np.array_equal(g[b, :k], t[b, :k]))
+    return {"frames": len(oracle_outs), "tokens": tot, "token_agreement": round(same / max(tot, 1), 4),
+            "rows_equal_to_first_non_decisive_step": f"{rows_ok}/{rows}"}
 
 
 COPY_BYTES = 1 << 30
@@ -700,7 +731,7 @@ def main():
         for name in ("b16", "b128"):
             sub = measure(name, args, torch, dev, bd)
             line["workloads"][name] = {k: sub[k] for k in ("value", "unit", "ms_per_step", "dtype", "config",
-                                                           "roofline", "cpu_baseline")}
+                                                           "roofline", "cpu_baseline", "free_run_vs_oracle")}
         # the B = 128 line is graded on the matrix cores: also against this
         # GPU's measured peak of the instruction the products use
         peak = mfma_peak()
@@ -805,8 +836,15 @@ def measure(name, args, torch, dev, bd):
                     "algorithmic_bytes_unreduced": nbytes_full, "per": scope}
 
     cpu = None
+    free_run = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, W, H, q0, args.cpu_budget, sampling, U if sampling else None)
+        cpu, outs = cpu_baseline(wl, W, H, q0, args.cpu_budget, sampling, U if sampling else None)
+        # the same frames again on the GPU, untimed, for their tokens
+        got = []
+        for i in range(len(outs)):
+            frame(i)
+            got.append(tok.cpu().numpy().copy())
+        free_run = free_run_agreement(got, outs)
 
     # arithmetic type of the products: bf16 operands with fp32 accumulation
     # on the matrix cores and in the dataflow kernel with bf16 weights; the
@@ -844,6 +882,7 @@ def measure(name, args, torch, dev, bd):
                    "algorithmic_flops_per_step": nflops},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "free_run_vs_oracle": free_run,
     }
     # every launch has finished before the handle is destroyed
     torch.cuda.synchronize()

@@ -525,14 +525,7 @@ __global__ __launch_bounds__(kThreadsF) void k_flow(Model m, RunArgs a, Recs rc,
                     fed = fed_s[0];
                 }
                 // history: keys and values of positions < pf, LDS-direct loads
-                if (wave >= 8) {
-                    for (int i = wave - 8; i < 4 * pf; i += kW - 8) {
-                        const int tt = i >> 2, part = i & 3;
-                        const size_t off = kvb + (static_cast<size_t>(tt) * NKV + ug) * HD + (part & 1) * 64;
-                        float* dst = (part < 2 ? hist : hist + 2048) + tt * HD + (part & 1) * 64;
-                        stream::dma64((part < 2 ? m.kc : m.vc) + off, dst);
-                    }
-                }
+                if (wave >= 8) stream::hist_dma(m.kc, m.vc, kvb, ug, pf, hist, wave, 8, kW - 8);
                 // head vectors: wave 4 pi + v takes vector v (q 2g, q 2g+1, k g, v g) of position pi
                 if (wave < 4 * npos) {
                     const int pi = wave >> 2, v = wave & 3;

@@ -266,6 +266,27 @@ __device__ __forceinline__ void dma64(const float* src, float* dst) {
     __builtin_amdgcn_global_load_lds((gbl_void_t*)(src + lane), (lds_void_t*)(dst), 4, 0, kDeviceScope);
 }
 
+// The cached keys and values of positions 0 .. pf-1 of one (request, kv head)
+// (rows of HD floats, position stride NKV * HD in the cache) into LDS: keys
+// at hist[t * HD], values at hist[2048 + t * HD].  16 bytes per lane, so one
+// load moves two positions' rows (lanes 32..63 the second); the loads are
+// dealt round-robin over the nw waves from wave w0.  With pf odd, the last
+// load's upper half re-reads row pf - 1 into row pf, which the caller
+// overwrites with the current position after its barrier.
+__device__ __forceinline__ void hist_dma(const float* kc, const float* vc, size_t kvb, int g, int pf, float* hist,
+                                         int wave, int w0, int nw) {
+    const int lane = threadIdx.x & 63;
+    const int np = (pf + 1) >> 1;             // loads per matrix
+    for (int i = wave - w0; i < 2 * np; i += nw) {
+        if (i < 0) continue;
+        const int j = i < np ? i : i - np;     // position pair
+        const int tt = min(2 * j + (lane >> 5), pf - 1);
+        const float* src = (i < np ? kc : vc) + kvb + (static_cast<size_t>(tt) * NKV + g) * HD + (lane & 31) * 4;
+        float* dst = hist + (i < np ? 0 : 2048) + 2 * j * HD;
+        __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)dst, 16, 0, kDeviceScope);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // compute side helpers
 // ---------------------------------------------------------------------------
@@ -596,6 +617,15 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                     if (lane < 4) st_rec(rc.QKV + static_cast<size_t>(r) * NQKV + 16 * wg + 4 * wave + lane, v, tag_of(ph));
                 }
                 QP_STAMP(a.taps, wg, ph, 2);
+                if (wg < B * NKV && s > 1) {
+                    // the attention unit's history, requested behind its
+                    // q/k/v stores: it lands while the other producers'
+                    // records are awaited.  The slot is attention's; its
+                    // last reader (the previous phase) finished before this
+                    // phase's staging barrier.
+                    const size_t kvb = ((static_cast<size_t>(l) * m.max_batch + wg / NKV) * kPositions) * NKV * HD;
+                    hist_dma(m.kc, m.vc, kvb, wg % NKV, s, slot[par ^ 1], wave, 0, kW);
+                }
                 ++ph;
             }
             // ================= ATTN(l) =================
@@ -609,16 +639,10 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                 const int npos = (s == 1) ? 2 : 1;
                 const size_t kvb = ((static_cast<size_t>(l) * m.max_batch + b) * kPositions) * NKV * HD;
                 if (unit) {
-                    // cached keys/values of earlier positions: LDS-direct loads
-                    if (wave == 0) {
-                        for (int tt = 0; tt < pf; ++tt) {
-                            const size_t off = kvb + (static_cast<size_t>(tt) * NKV + g) * HD;
-                            dma64(m.kc + off, hist + tt * HD);
-                            dma64(m.kc + off + 64, hist + tt * HD + 64);
-                            dma64(m.vc + off, hist + 2048 + tt * HD);
-                            dma64(m.vc + off + 64, hist + 2048 + tt * HD + 64);
-                        }
-                    }
+                    // cached keys/values of earlier positions: LDS-direct
+                    // loads; after a q/k/v phase of its own the unit requested
+                    // them already (at its end)
+                    if (l == 0 && s > 1 && t0) hist_dma(m.kc, m.vc, kvb, g, pf, hist, wave, 0, kW);
                     // new head vectors: wave w takes q 2g, q 2g+1, k g, v g
                     const int col = wave < 2 ? (2 * g + wave) * HD : (wave == 2 ? (NQ + g) * HD : (NQ + NKV + g) * HD);
                     if (l == 0 && s > 1 && t0) {

@@ -171,3 +171,25 @@ def test_kernel_timeline_analysis_on_built_stamps():
                         "workgroup_median": 6.0, "k1_median": 3.0, "total": 7.0}
     assert k["attn"] == {"launches": 1, "span": 5.0, "gap_before": 2.0, "start_ramp": 0.5,
                          "workgroup_median": 4.25, "k1_median": None, "total": 5.0}
+
+
+def test_free_run_agreement_counts_tokens_and_decisive_prefixes():
+    """Hand-built frames: row 0 equal everywhere; row 1 differs only after its
+    first non-decisive step (counts as equal up to it); row 2 differs at a
+    decisive step before that."""
+    t = np.arange(45, dtype=np.int64).reshape(3, 15)
+    mg = np.ones((3, 15))
+    mg[1, 7] = 0.01
+    mg[2, 9] = 0.01
+    g = t.copy()
+    g[1, 10] += 1
+    g[2, 3] += 1
+    r = bench.free_run_agreement([g], [(t, mg, bench.DECISIVE_MARGIN)])
+    assert r["frames"] == 1 and r["tokens"] == 45
+    assert r["token_agreement"] == round(43 / 45, 4)
+    assert r["rows_equal_to_first_non_decisive_step"] == "2/3"
+    # a margin exactly at the bar is not decisive
+    mg2 = np.ones((3, 15))
+    mg2[2, 3] = bench.DECISIVE_MARGIN
+    r2 = bench.free_run_agreement([g], [(t, mg2, bench.DECISIVE_MARGIN)])
+    assert r2["rows_equal_to_first_non_decisive_step"] == "2/3"   # row 1 still differs at step 10
