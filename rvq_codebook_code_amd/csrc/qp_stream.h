@@ -541,7 +541,14 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
             // ================= QKV(l) =================
             if (l == 0 && s > 1 && t0) {
                 // the input row is P_{s-1}[fed], whose q/k/v rows are in the
-                // table: decide the tokens and take this wave's residual element
+                // table: decide the tokens and take this wave's residual
+                // element.  The attention units first request their layer-0
+                // history, which does not depend on the token (attention's
+                // slot: its last reader, the lm_head phase, ended at a barrier).
+                if (wg < B * NKV) {
+                    const size_t kvb = (static_cast<size_t>(wg / NKV) * kPositions) * NKV * HD;
+                    hist_dma(m.kc, m.vc, kvb, wg % NKV, s, slot[(ph + 1) & 1], wave, 0, kW);
+                }
                 decide(s - 1, ph_lm(L, s - 1));
                 if (wave == 3 && eb < B) {
                     int fb = fed[0];
@@ -639,10 +646,10 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                 const int npos = (s == 1) ? 2 : 1;
                 const size_t kvb = ((static_cast<size_t>(l) * m.max_batch + b) * kPositions) * NKV * HD;
                 if (unit) {
-                    // cached keys/values of earlier positions: LDS-direct
-                    // loads; after a q/k/v phase of its own the unit requested
-                    // them already (at its end)
-                    if (l == 0 && s > 1 && t0) hist_dma(m.kc, m.vc, kvb, g, pf, hist, wave, 0, kW);
+                    // cached keys/values of earlier positions (LDS-direct
+                    // loads) were requested by the unit already: at the end
+                    // of its q/k/v phase, or (layer 0 from the table) ahead
+                    // of the token decision
                     // new head vectors: wave w takes q 2g, q 2g+1, k g, v g
                     const int col = wave < 2 ? (2 * g + wave) * HD : (wave == 2 ? (NQ + g) * HD : (NQ + NKV + g) * HD);
                     if (l == 0 && s > 1 && t0) {
