@@ -526,8 +526,13 @@ __global__ __launch_bounds__(kThreadsF) void k_flow(Model m, RunArgs a, Recs rc,
                 }
                 // history: keys and values of positions < pf, LDS-direct loads
                 if (wave >= 8) stream::hist_dma(m.kc, m.vc, kvb, ug, pf, hist, wave, 8, kW - 8);
-                // head vectors: wave 4 pi + v takes vector v (q 2g, q 2g+1, k g, v g) of position pi
-                if (wave < 4 * npos) {
+                // head vectors: wave 4 pi + v takes vector v (q 2g, q 2g+1, k g, v g) of position pi.
+                // Polled (not from the table), the value vector is left to
+                // the computing waves, which wait for it only after the
+                // softmax: its columns come from the owners, which reach the
+                // q/k/v phase last (they end the down phase)
+                const bool tab = l == 0 && s > 1;
+                if (wave < 4 * npos && (tab || (wave & 3) != 3)) {
                     const int pi = wave >> 2, v = wave & 3;
                     const int col = v < 2 ? (2 * ug + v) * HD : (v == 2 ? (NQ + ug) * HD : (NQ + NKV + ug) * HD);
                     float* dst = nd + (pi * 4 + v) * HD;
@@ -565,19 +570,14 @@ __global__ __launch_bounds__(kThreadsF) void k_flow(Model m, RunArgs a, Recs rc,
                         const float rq = __builtin_amdgcn_rsqf(sq2[1] / static_cast<float>(HD) + eps);
                         const float a0 = gk[lane] * (k0 * rk), a1 = gk[lane + 64] * (k1 * rk);
                         const float kv0 = a0 * ca - a1 * sa, kv1 = a1 * ca + a0 * sa;
-                        const float vv0 = hv[3 * HD + lane], vv1 = hv[3 * HD + lane + 64];
+                        const size_t off = kvb + (static_cast<size_t>(p) * NKV + ug) * HD;
                         if (wave == 0) {
-                            const size_t off = kvb + (static_cast<size_t>(p) * NKV + ug) * HD;
                             st_act(m.kc + off + lane, kv0);
                             st_act(m.kc + off + lane + 64, kv1);
-                            st_act(m.vc + off + lane, vv0);
-                            st_act(m.vc + off + lane + 64, vv1);
                         }
                         // both waves write the same values before reading them
                         hist[p * HD + lane] = kv0;
                         hist[p * HD + lane + 64] = kv1;
-                        hist[2048 + p * HD + lane] = vv0;
-                        hist[2048 + p * HD + lane + 64] = vv1;
                         {
                             const float b0 = gq[lane] * (x0 * rq), b1 = gq[lane + 64] * (x1 * rq);
                             qw[lane] = b0 * ca - b1 * sa;
@@ -603,6 +603,26 @@ __global__ __launch_bounds__(kThreadsF) void k_flow(Model m, RunArgs a, Recs rc,
                         const float e = (kt <= p) ? __expf(sc - mx) : 0.f;
                         const float den = wave_sum((lane & 3) == 0 ? e : 0.f);
                         if ((lane & 3) == 0) ew[kt] = e;
+                        // this position's value vector joins the history (and
+                        // the cache): from the table, or awaited only now
+                        if (tab) {
+                            const float vv0 = hv[3 * HD + lane], vv1 = hv[3 * HD + lane + 64];
+                            if (wave == 0) {
+                                st_act(m.vc + off + lane, vv0);
+                                st_act(m.vc + off + lane + 64, vv1);
+                            }
+                            hist[2048 + p * HD + lane] = vv0;
+                            hist[2048 + p * HD + lane + 64] = vv1;
+                        } else {
+                            float* vrow = hist + 2048 + p * HD;
+                            stream::poll_head(rc.QKV + static_cast<size_t>(row) * NQKV + (NQ + NKV + ug) * HD,
+                                              tag_of(ph_layer(L, s, l, T_QKV)), vrow, err);
+                            if (wave == 0) {
+                                const float2 vv = *reinterpret_cast<const float2*>(vrow + 2 * lane);
+                                st_act(m.vc + off + 2 * lane, vv.x);
+                                st_act(m.vc + off + 2 * lane + 1, vv.y);
+                            }
+                        }
                         // weighted values, elements 2 lane and 2 lane + 1 (one
                         // record); each half's LDS reads issued before its products
                         float o0 = 0.f, o1 = 0.f;
