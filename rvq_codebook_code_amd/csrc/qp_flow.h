@@ -618,9 +618,10 @@ __global__ __launch_bounds__(kThreadsF) void k_flow(Model m, RunArgs a, Recs rc,
                             stream::poll_head(rc.QKV + static_cast<size_t>(row) * NQKV + (NQ + NKV + ug) * HD,
                                               tag_of(ph_layer(L, s, l, T_QKV)), vrow, err);
                             if (wave == 0) {
-                                const float2 vv = *reinterpret_cast<const float2*>(vrow + 2 * lane);
-                                st_act(m.vc + off + 2 * lane, vv.x);
-                                st_act(m.vc + off + 2 * lane + 1, vv.y);
+                                // one 8-byte store per lane: the wave writes the row's 512 bytes contiguously
+                                const uint64_t vv = *reinterpret_cast<const uint64_t*>(vrow + 2 * lane);
+                                __hip_atomic_store(reinterpret_cast<uint64_t*>(m.vc + off + 2 * lane), vv, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
                             }
                         }
                         // weighted values, elements 2 lane and 2 lane + 1 (one
