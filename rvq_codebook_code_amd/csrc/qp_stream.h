@@ -363,6 +363,10 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
     __shared__ float rope_s[2][kPositions * (HD / 2)];
     __shared__ float gains[kGainFloats];
     __shared__ LayerDev lay_s[kMaxL];
+    // the tokens fed at codebooks 0..15 (q0, then each step's), per request:
+    // the embedding sum gathers its 16 rows once, at the end of the frame,
+    // instead of one dependent load per step on the step's critical path
+    __shared__ int tok_s[kSteps + 1][BM];
 
     const int wg = blockIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -485,9 +489,20 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
         }
     };
 
-    // ---- INIT: q0, embedding sum start, H rows
-    float es = 0.f;  // wave 3: embedding-sum element (request lane/8, column 8*wg + lane%8)
+    // ---- INIT: q0, H rows
+    // wave 3 keeps the tokens fed at codebook j for the embedding sum
+    // (element: request lane/8, column 8*wg + lane%8), written and read by
+    // wave 3 alone
     const int eb = lane >> 3, ek = 8 * wg + (lane & 7);
+    auto keep_tokens = [&](int j) {
+        if (wave == 3 && lane < B) {
+            int fb = fed[0];
+#pragma unroll
+            for (int b = 1; b < BM; ++b)
+                if (b == lane) fb = fed[b];
+            tok_s[j][lane] = fb;
+        }
+    };
 #pragma unroll
     for (int b = 0; b < BM; ++b) {
         if (b < B) {
@@ -503,13 +518,7 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
             for (int i = 0; i < DT / 1024; ++i) d4[lane + 64 * i] = hr[lane + 64 * i];
         }
     }
-    if (wave == 3 && eb < B) {
-        int fb = fed[0];
-#pragma unroll
-        for (int b = 1; b < BM; ++b)
-            if (b == eb) fb = fed[b];
-        es = emb_elem(m, 0, fb, ek);
-    }
+    keep_tokens(0);
     __syncthreads();
     {
         const float* Hs = slot[0];
@@ -550,13 +559,7 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                     hist_dma(m.kc, m.vc, kvb, wg % NKV, s, slot[(ph + 1) & 1], wave, 0, kW);
                 }
                 decide(s - 1, ph_lm(L, s - 1));
-                if (wave == 3 && eb < B) {
-                    int fb = fed[0];
-#pragma unroll
-                    for (int b = 1; b < BM; ++b)
-                        if (b == eb) fb = fed[b];
-                    es += emb_elem(m, s - 1, fb, ek);
-                }
+                keep_tokens(s - 1);
 #pragma unroll
                 for (int r = 0; r < MR; ++r) xr[r] = 0.f;
 #pragma unroll
@@ -572,13 +575,7 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
                         gather_x(rc.X, B, tag_of(0), par);
                     } else {
                         decide(s - 1, ph_lm(L, s - 1));
-                        if (wave == 3 && eb < B) {
-                            int fb = fed[0];
-#pragma unroll
-                            for (int b = 1; b < BM; ++b)
-                                if (b == eb) fb = fed[b];
-                            es += emb_elem(m, s - 1, fb, ek);
-                        }
+                        keep_tokens(s - 1);
                     }
                     // rows fed by the codebook tables: P_{s-1}[fed], a quarter per wave
                     const int r0 = (s == 1) ? B : 0;
@@ -949,12 +946,15 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
     }
     // ================= FINAL: last token, embedding sum out =================
     decide(kSteps, ph_lm(L, kSteps));
+    keep_tokens(kSteps);
     if (wave == 3 && eb < B) {
-        int fb = fed[0];
+        // the 16 rows' elements requested together, summed in codebook order
+        float ev[kSteps + 1];
 #pragma unroll
-        for (int b = 1; b < BM; ++b)
-            if (b == eb) fb = fed[b];
-        es += emb_elem(m, kSteps, fb, ek);
+        for (int j = 0; j <= kSteps; ++j) ev[j] = emb_elem(m, j, tok_s[j][eb], ek);
+        float es = ev[0];
+#pragma unroll
+        for (int j = 1; j <= kSteps; ++j) es += ev[j];
         a.embsum[static_cast<size_t>(eb) * DT + ek] = es;
     }
 }
