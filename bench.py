@@ -285,14 +285,15 @@ def select_driver(g, B: int, args) -> str:
     return "generic"
 
 
-TRAFFIC_FILES = {"dataflow": "k_stream", "flow": "k_flow"}
+TRAFFIC_FILES = {"dataflow": "k_stream", "flow": "k_flow", "tiled": "k_tiled"}
 
 
 def measured_traffic(driver: str, workload: str):
-    """HBM bytes per launch of a dataflow kernel from the committed counter
-    summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy), or None when
-    there is none for this driver and workload or the kernel's sources have
-    changed since the counters were taken."""
+    """HBM bytes per launch of a dataflow kernel (per frame call of the
+    batched path: its staging copy, graph replay and output copy) from the
+    committed counter summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain
+    copy), or None when there is none for this driver and workload or the
+    kernel's sources have changed since the counters were taken."""
     import hashlib
     if driver not in TRAFFIC_FILES:
         return None
@@ -821,7 +822,9 @@ def measure(name, args, torch, dev, bd):
         # throughput batch: graded against the bf16 matrix-core peak
         achieved = nflops / (launch_ms / 1e3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "traffic": (measured_traffic(driver, wl.name)
+                                if B == wl.batch and not args.flush_mib else None),
                     "frac_end_to_end": round(nflops / (ms_per_step / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                     "frac_unreduced_model": round(nflops_full / (launch_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                     "algorithmic_flops_unreduced": nflops_full, "per": scope}

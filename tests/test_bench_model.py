@@ -193,3 +193,22 @@ def test_free_run_agreement_counts_tokens_and_decisive_prefixes():
     mg2[2, 3] = bench.DECISIVE_MARGIN
     r2 = bench.free_run_agreement([g], [(t, mg2, bench.DECISIVE_MARGIN)])
     assert r2["rows_equal_to_first_non_decisive_step"] == "2/3"   # row 1 still differs at step 10
+
+
+def test_measured_traffic_follows_the_sources(tmp_path, monkeypatch):
+    """The traffic figure is read from a counter summary only while the
+    sources it names hash to the recorded value."""
+    import hashlib
+    (tmp_path / "profiles").mkdir()
+    src = tmp_path / "k.h"
+    src.write_text("kernel source\n")
+    h = hashlib.sha256(src.read_bytes()).hexdigest()
+    (tmp_path / "profiles" / "k_tiled_b128_hbm_traffic.txt").write_text(
+        "# comment: with a colon\nkernel: frame call\nsources: k.h\n"
+        f"sources_sha256: {h}\ntraffic_bytes_per_launch: 12345\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.measured_traffic("tiled", "b128") == 12345
+    assert bench.measured_traffic("tiled", "b16") is None        # no summary for this workload
+    assert bench.measured_traffic("generic", "b128") is None     # no summary for this driver
+    src.write_text("kernel source, changed\n")
+    assert bench.measured_traffic("tiled", "b128") is None
