@@ -45,7 +45,11 @@
 //    (SwiGLU: its pair) and, except SwiGLU, NW = 8 up to 16 rows where K
 //    holds 16 pairs of 32-wide blocks, else 4; RT = 2 takes CT = 2 and
 //    NW = 4.  The NW waves split K and their partial tiles are summed through
-//    LDS in wave order.  The projection of H (small N) with two row
+//    LDS in wave order.  The sum and the epilogue are shared by four waves,
+//    wave i taking component i of every lane's accumulator (one row of each
+//    16-row fragment per lane), so they run four wide; the row scales reach
+//    them through LDS from the wave that summed the row's squares.  The
+//    projection of H (small N) with two row
 //    fragments also splits K across KS workgroups:
 //    every workgroup writes its partial tile, and the last to arrive (a
 //    counter per tile) sums the KS partials in order and runs the epilogue,
@@ -239,6 +243,7 @@ template <int WT, int RT, int SRC, int EPI, int NW, int CT>
 __global__ __launch_bounds__(64 * NW) void k_gemm(GemmArgs g) {
     static_assert(EPI != EPI_SWIGLU || CT == 2, "SwiGLU pairs a gate and an up fragment");
     __shared__ f32x4_t red[NW][RT][CT][64];
+    __shared__ float rinv_s[RT][16];   // RMSNorm row scales, for the component-split epilogue
     __shared__ int last_s;
 
     QP_TSTAMP(g.tl, 0);
@@ -284,6 +289,13 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(GemmArgs g) {
     // RMSNorm row scales of the row tiles this wave finishes, fetched before
     // the products: lane l sums a quarter of row (l % 16)'s tile sums, the
     // quarters are then combined across the lane groups (fixed order)
+    // Every product but the projection of H (which may split K over
+    // workgroups) finishes its tile with the four waves sharing the work:
+    // wave i < 4 takes component i of every lane's accumulator (row
+    // 4 (lane / 16) + i of each row fragment), so the reduction, the
+    // epilogue arithmetic and the stores run four wide instead of on one
+    // wave per row fragment.
+    constexpr bool kSplitEpi = EPI != EPI_BIAS;
     float rss[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -313,8 +325,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(GemmArgs g) {
             for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int m = m0 + 16 * rt + 4 * (lane >> 4) + i;
-                    xo[rt][c][i] = (EPI == EPI_RESID && rt % NW == wave && m < g.M)
+                    const int m = m0 + 16 * rt + 4 * (lane >> 4) + (kSplitEpi ? wave : i);
+                    const bool mine = kSplitEpi ? (i == 0 && wave < 4) : rt % NW == wave;
+                    xo[rt][c][i] = (EPI == EPI_RESID && mine && m < g.M)
                                        ? g.out[static_cast<size_t>(m) * g.ldo + n] : 0.f;
                 }
             }
@@ -411,7 +424,91 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(GemmArgs g) {
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int c = 0; c < CT; ++c) red[wave][rt][c][lane] = acc[rt][c];
+    if constexpr (kSplitEpi && SRC == SRC_BF16_NORM) {
+        // the wave that summed row fragment rt's squares publishes its 16 row scales
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            if (rt % NW != wave) continue;
+            float t = rss[rt];
+            t += __shfl_xor(t, 16, 64);
+            t += __shfl_xor(t, 32, 64);   // every lane: the sum for row lane % 16
+            if (lane < 16) rinv_s[rt][lane] = 1.0f / sqrtf(t / static_cast<float>(g.K) + g.eps);
+        }
+    }
     __syncthreads();
+
+    if constexpr (kSplitEpi) {
+        if (wave < 4) {
+            const int i = wave;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const int m = m0 + 16 * rt + 4 * (lane >> 4) + i;
+                float rinv = 1.f;
+                if constexpr (SRC == SRC_BF16_NORM) rinv = rinv_s[rt][4 * (lane >> 4) + i];
+                // component i of the NW partial tiles, summed in wave order
+                float v[CT];
+#pragma unroll
+                for (int c = 0; c < CT; ++c) {
+                    const float* r = reinterpret_cast<const float*>(&red[0][rt][c][lane]) + i;
+                    float t = r[0];
+#pragma unroll
+                    for (int w = 1; w < NW; ++w) t += r[w * RT * CT * 64 * 4];
+                    v[c] = t;
+                }
+                if constexpr (EPI == EPI_ARGMAX) {
+                    uint64_t key = 0;
+#pragma unroll
+                    for (int c = 0; c < CT; ++c) {
+                        const int n = nb[c] * 16 + (lane & 15);
+                        const float x = v[c] * rinv;
+                        if (g.logits && m < g.M) g.logits[m * g.logit_ld + n] = x;
+                        key = umax64(key, argmax_key(x, n));
+                    }
+#pragma unroll
+                    for (int o = 1; o < 16; o <<= 1) key = umax64(key, shfl_xor64(key, o));
+                    if ((lane & 15) == 0 && m < g.M) g.keys[static_cast<size_t>(m) * gridDim.x + bx] = key;
+                } else if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+                    for (int pp = 0; pp < CT / 2; ++pp) {
+                        const int n = nb[2 * pp] * 16 + (lane & 15);
+                        if (m < g.M) {
+                            const float gt = v[2 * pp] * rinv, ut = v[2 * pp + 1] * rinv;
+                            g.outb[act_index(m, n, g.N, g.frag)] = to_bf16((gt / (1.0f + expf(-gt))) * ut);
+                        }
+                    }
+                } else if constexpr (EPI == EPI_SCALE) {
+#pragma unroll
+                    for (int c = 0; c < CT; ++c) {
+                        const int n = nb[c] * 16 + (lane & 15);
+                        if (m < g.M) g.out[static_cast<size_t>(m) * g.ldo + n] = v[c] * rinv;
+                    }
+                } else {
+                    // residual stream rows: x (fp32), xg = bf16(g_next * x), and
+                    // the sum of x^2 over each 16-column fragment
+#pragma unroll
+                    for (int c = 0; c < CT; ++c) {
+                        const int n = nb[c] * 16 + (lane & 15);
+                        float sq = 0.f;
+                        if (m < g.M) {
+                            const float nv = xo[rt][c][0] + v[c];
+                            if (g.taps) {
+                                const int B = g.tap_B;
+                                const int pos = row_pos(g.tap_s, B, m), b = row_req(g.tap_s, B, m);
+                                g.taps[((static_cast<size_t>(pos) * g.tap_L + g.tap_l) * B + b) * g.ldo + n] = nv;
+                            }
+                            g.out[static_cast<size_t>(m) * g.ldo + n] = nv;
+                            g.xg[act_index(m, n, g.ldo, g.frag)] = to_bf16(gnx[c] * nv);
+                            sq = nv * nv;
+                        }
+                        const float t = sum16(sq);
+                        if ((lane & 15) == 0 && m < g.M) g.ss_out[static_cast<size_t>(m) * (g.ldo / 16) + nb[c]] = t;
+                    }
+                }
+            }
+        }
+        QP_TSTAMP(g.tl, 2);
+        return;
+    }
 
     // wave w finishes row tiles w, w + NW, ...
     f32x4_t tot[RT][CT];
