@@ -286,9 +286,12 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(GemmArgs g) {
                             : static_cast<size_t>(p) * g.K + akoff);
     }
 
-    // RMSNorm row scales of the row tiles this wave finishes, fetched before
-    // the products: lane l sums a quarter of row (l % 16)'s tile sums, the
-    // quarters are then combined across the lane groups (fixed order)
+    // RMSNorm row scales of the row tiles this wave finishes: lane l sums a
+    // quarter of row (l % 16)'s tile sums (q = nss / 4 of them, a multiple
+    // of 4 since dP % 256 == 0), the quarters are then combined across the
+    // lane groups (fixed order).  The first 32 are requested here, all at
+    // once, and summed after the K loop, so that their round trip overlaps
+    // the products instead of preceding them.
     // Every product but the projection of H (which may split K over
     // workgroups) finishes its tile with the four waves sharing the work:
     // wave i < 4 takes component i of every lane's accumulator (row
@@ -296,20 +299,22 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(GemmArgs g) {
     // epilogue arithmetic and the stores run four wide instead of on one
     // wave per row fragment.
     constexpr bool kSplitEpi = EPI != EPI_BIAS;
+    static_assert(RT <= NW, "a wave finishes at most one row fragment's scales");
+    constexpr int kRssHeld = 8;                  // float4 loads held across the K loop
     float rss[RT];
+    float4 rsv[kRssHeld];
+    const int rq = g.nss >> 2;
+    const int rsv_n = rq >> 2 < kRssHeld ? rq >> 2 : kRssHeld;
+    const bool rown = SRC == SRC_BF16_NORM && wave < RT && rok[wave < RT ? wave : 0];
+    const float* rsrc = (SRC == SRC_BF16_NORM && wave < RT)
+                            ? g.ss_in + static_cast<size_t>(m0 + 16 * wave + arow) * g.nss + (lane >> 4) * rq
+                            : nullptr;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        rss[rt] = 0.f;
-        if constexpr (SRC == SRC_BF16_NORM) {
-            if (rt % NW == wave && rok[rt]) {
-                const int q = g.nss >> 2;
-                const float* sr = g.ss_in + static_cast<size_t>(m0 + 16 * rt + arow) * g.nss + (lane >> 4) * q;
-                for (int t = 0; t < q; t += 2) {   // q = nss / 4 is even (dP % 256 == 0)
-                    const float2 v = *reinterpret_cast<const float2*>(sr + t);
-                    rss[rt] += v.x + v.y;
-                }
-            }
-        }
+    for (int rt = 0; rt < RT; ++rt) rss[rt] = 0.f;
+#pragma unroll
+    for (int j = 0; j < kRssHeld; ++j) {
+        rsv[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (rown && j < rsv_n) rsv[j] = *reinterpret_cast<const float4*>(rsrc + 4 * j);
     }
 
     // residual-stream epilogues: the old x tile, the next reader's gain and
@@ -419,6 +424,36 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(GemmArgs g) {
     for (; kb < kb1; kb += 2) batch(kb, std::integral_constant<int, 2>{});
 
     QP_TSTAMP(g.tl, 1);
+    if constexpr (SRC == SRC_BF16_NORM) {
+        // the row-scale sums, in pairs in column order (rows past M add zeros)
+        if (wave < RT) {
+            float t = 0.f;
+#pragma unroll
+            for (int j = 0; j < kRssHeld; ++j) {
+                if (j < rsv_n) {
+                    t += rsv[j].x + rsv[j].y;
+                    t += rsv[j].z + rsv[j].w;
+                }
+            }
+            // d > 2048: the rest, 32 at a time, each group requested together
+            for (int b = kRssHeld; rown && 4 * b < rq; b += kRssHeld) {
+                float4 v[kRssHeld];
+#pragma unroll
+                for (int j = 0; j < kRssHeld; ++j)
+                    if (4 * (b + j) < rq) v[j] = *reinterpret_cast<const float4*>(rsrc + 4 * (b + j));
+#pragma unroll
+                for (int j = 0; j < kRssHeld; ++j) {
+                    if (4 * (b + j) < rq) {
+                        t += v[j].x + v[j].y;
+                        t += v[j].z + v[j].w;
+                    }
+                }
+            }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                if (rt == wave) rss[rt] = t;
+        }
+    }
     // ---- reduce the four waves' K ranges, in wave order ----
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
