@@ -360,8 +360,8 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
     __shared__ float slot[2][SLOT];
     __shared__ float ssp[2][kW][MR];          // per-wave partial sums of squares
     __shared__ uint64_t lmk[kW][BM];          // per-wave lm_head keys
-    __shared__ float rope_s[2][kPositions * (HD / 2)];
-    __shared__ float gains[kGainFloats];
+    __shared__ __align__(16) float rope_s[2][kPositions * (HD / 2)];
+    __shared__ __align__(16) float gains[kGainFloats];
     __shared__ LayerDev lay_s[kMaxL];
     // the tokens fed at codebooks 0..15 (q0, then each step's), per request:
     // the embedding sum gathers its 16 rows once, at the end of the frame,
@@ -381,25 +381,27 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
     // create time: from step 2 on, layer 0 takes its head vectors from here
     const float* t0 = m.qkv0;
 
-    // ---- tables into LDS: layer pointers, norm gains, RoPE
+    // ---- tables into LDS: layer pointers, norm gains, RoPE.  The tables go
+    // straight into LDS, 16 bytes per lane, every request issued before any
+    // is awaited; they are complete at the barrier that ends INIT's staging
+    // (a wait for every load in flight precedes it).
+    auto dma_tab = [&](const float* src, float* dst, int n) {   // n: a multiple of 4 floats
+        for (int o = wave * 256; o < n; o += kW * 256)
+            if (o + 4 * lane < n)
+                __builtin_amdgcn_global_load_lds((gbl_void_t*)(src + o + 4 * lane), (lds_void_t*)(dst + o), 16, 0, 0);
+    };
+    dma_tab(m.rope_cos, rope_s[0], kPositions * (HD / 2));
+    dma_tab(m.rope_sin, rope_s[1], kPositions * (HD / 2));
+    dma_tab(m.out_norm, gains + 2 * kMaxL * DP, DP);
     if (threadIdx.x < L) lay_s[threadIdx.x] = m.layers[threadIdx.x];
     __syncthreads();
     const LayerDev* LD = lay_s;
-    for (int i = threadIdx.x; i < kPositions * (HD / 2); i += kThreadsS) {
-        rope_s[0][i] = m.rope_cos[i];
-        rope_s[1][i] = m.rope_sin[i];
+    for (int l = 0; l < L; ++l) {
+        dma_tab(LD[l].attn_norm, gains + (2 * l) * DP, DP);
+        dma_tab(LD[l].ffn_norm, gains + (2 * l + 1) * DP, DP);
+        dma_tab(LD[l].q_norm, gains + (2 * kMaxL + 1) * DP + (2 * l) * HD, HD);
+        dma_tab(LD[l].k_norm, gains + (2 * kMaxL + 1) * DP + (2 * l + 1) * HD, HD);
     }
-    for (int l = 0; l < L; ++l)
-        for (int i = threadIdx.x; i < DP; i += kThreadsS) {
-            gains[(2 * l) * DP + i] = LD[l].attn_norm[i];
-            gains[(2 * l + 1) * DP + i] = LD[l].ffn_norm[i];
-        }
-    for (int i = threadIdx.x; i < DP; i += kThreadsS) gains[2 * kMaxL * DP + i] = m.out_norm[i];
-    for (int l = 0; l < L; ++l)
-        for (int i = threadIdx.x; i < HD; i += kThreadsS) {
-            gains[(2 * kMaxL + 1) * DP + (2 * l) * HD + i] = LD[l].q_norm[i];
-            gains[(2 * kMaxL + 1) * DP + (2 * l + 1) * HD + i] = LD[l].k_norm[i];
-        }
     auto g_attn = [&](int l) { return gains + (2 * l) * DP; };
     auto g_ffn = [&](int l) { return gains + (2 * l + 1) * DP; };
     const float* g_out = gains + 2 * kMaxL * DP;
@@ -519,6 +521,7 @@ __global__ __launch_bounds__(kThreadsS) void k_stream(Model m, RunArgs a, Recs r
         }
     }
     keep_tokens(0);
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's table requests too
     __syncthreads();
     {
         const float* Hs = slot[0];
