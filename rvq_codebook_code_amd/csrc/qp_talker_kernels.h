@@ -175,6 +175,14 @@ __global__ __launch_bounds__(kThreadsK) void k_attn(AttnArgs a) {
         for (int j = 0; j < J; ++j) hv[j] = off >= 0 ? row[off + lane + 64 * j] : 0.f;
     }
 
+    // the norm gains and the RoPE row of this wave's head, requested before
+    // the history, so that the norm need not wait for it (the loads of a
+    // wave complete in order)
+    float hg[J];
+    qp::tiled::RopeRow<HD> hr;
+    qp::tiled::gain_fetch<HD>(wave < R ? a.q_norm : a.k_norm, hg);
+    qp::tiled::rope_fetch<HD>(a.rope_cos, a.rope_sin, p, hr);
+
     // 0. the chunk's cached keys and values, requested before anything else
     //    (they do not depend on this step): keys LP lanes per position, 16
     //    positions per pass; values one row per position, wave w taking
@@ -206,12 +214,12 @@ __global__ __launch_bounds__(kThreadsK) void k_attn(AttnArgs a) {
     //    and value, rounded to bf16 into the cache
     if (wave < R) {
         float o[J];
-        qp::tiled::norm_rope_regs<HD>(hv, a.q_norm, a.eps, p, a.rope_cos, a.rope_sin, o);
+        qp::tiled::norm_rope_apply<HD>(hv, hg, hr, a.eps, o);
 #pragma unroll
         for (int j = 0; j < J; ++j) q_s[wave][lane + 64 * j] = o[j];
     } else if (has_new && wave == 2) {
         float o[J];
-        qp::tiled::norm_rope_regs<HD>(hv, a.k_norm, a.eps, p, a.rope_cos, a.rope_sin, o);
+        qp::tiled::norm_rope_apply<HD>(hv, hg, hr, a.eps, o);
         uint16_t* dst = a.kc + (hbase + p) * HD;
 #pragma unroll
         for (int j = 0; j < J; ++j) {

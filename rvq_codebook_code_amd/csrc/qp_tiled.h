@@ -758,9 +758,39 @@ __device__ __forceinline__ void load_emb(const TokArgs& ta, int t, float (&e)[kM
 
 // Per-head RMSNorm then rotate-half RoPE of a head vector held by one wave
 // (element lane + 64 j in v[j]); the pair of element i is element i + hd/2.
+// The gains and a position's rotation factors are fetched apart from the
+// arithmetic, so that a caller can request them with its first reads (none
+// depends on the data).
 template <int HD>
-__device__ __forceinline__ void norm_rope_regs(const float (&v)[HD / 64], const float* gain, float eps, int pos,
-                                               const float* rcos, const float* rsin, float (&out)[HD / 64]) {
+struct RopeRow {
+    static constexpr int H2 = HD / 128 > 0 ? HD / 128 : 1;
+    float c[H2], s[H2];
+};
+template <int HD>
+__device__ __forceinline__ void gain_fetch(const float* gain, float (&g)[HD / 64]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < HD / 64; ++j) g[j] = gain[lane + 64 * j];
+}
+template <int HD>
+__device__ __forceinline__ void rope_fetch(const float* rcos, const float* rsin, int pos, RopeRow<HD>& r) {
+    const int lane = threadIdx.x & 63;
+    const float* cp = rcos + pos * (HD / 2);
+    const float* sp = rsin + pos * (HD / 2);
+    if constexpr (HD / 64 == 1) {
+        r.c[0] = cp[lane & 31];
+        r.s[0] = sp[lane & 31];
+    } else {
+#pragma unroll
+        for (int j = 0; j < RopeRow<HD>::H2; ++j) {
+            r.c[j] = cp[lane + 64 * j];
+            r.s[j] = sp[lane + 64 * j];
+        }
+    }
+}
+template <int HD>
+__device__ __forceinline__ void norm_rope_apply(const float (&v)[HD / 64], const float (&g)[HD / 64],
+                                                const RopeRow<HD>& r, float eps, float (&out)[HD / 64]) {
     constexpr int J = HD / 64;
     const int lane = threadIdx.x & 63;
     float ss = 0.f;
@@ -770,20 +800,16 @@ __device__ __forceinline__ void norm_rope_regs(const float (&v)[HD / 64], const 
     const float rinv = 1.0f / sqrtf(ss / static_cast<float>(HD) + eps);
     float w[J];
 #pragma unroll
-    for (int j = 0; j < J; ++j) w[j] = gain[lane + 64 * j] * (v[j] * rinv);
-    const float* cp = rcos + pos * (HD / 2);
-    const float* sp = rsin + pos * (HD / 2);
+    for (int j = 0; j < J; ++j) w[j] = g[j] * (v[j] * rinv);
     if constexpr (J == 1) {
         const float partner = __shfl_xor(w[0], 32, 64);
-        const int i = lane & 31;
-        const float c = cp[i], sn = sp[i];
+        const float c = r.c[0], sn = r.s[0];
         out[0] = (lane < 32) ? (w[0] * c - partner * sn) : (w[0] * c + partner * sn);
     } else {
         constexpr int H2 = J / 2;
 #pragma unroll
         for (int j = 0; j < H2; ++j) {
-            const int i = lane + 64 * j;
-            const float c = cp[i], sn = sp[i];
+            const float c = r.c[j], sn = r.s[j];
             out[j] = w[j] * c - w[j + H2] * sn;
             out[j + H2] = w[j + H2] * c + w[j] * sn;
         }
@@ -924,6 +950,25 @@ __global__ __launch_bounds__(kThreadsT, HD <= 128 ? 4 : 3) void k_attn(AttnArgs 
         const int r = (s == 1) ? pi * B + b : b;
         return fed >= 0 ? ta.qkv0 + static_cast<size_t>(fed) * m.nqkv : m.qkv + static_cast<size_t>(r) * m.nqkv;
     };
+    // the per-head norm gains and the RoPE rows of the step's positions,
+    // requested ahead of the head vectors (with them, they were requested
+    // only after the history had been awaited: one more round trip for the
+    // key, another after the barrier for the queries)
+    float gk[J], gq[J];
+    RopeRow<HD> rp[2];
+    gain_fetch<HD>(m.k_norm, gk);
+    gain_fetch<HD>(m.q_norm, gq);
+#pragma unroll
+    for (int pi = 0; pi < 2; ++pi) rope_fetch<HD>(m.rope_cos, m.rope_sin, pf + (pi < npos ? pi : 0), rp[pi]);
+    auto rope_of = [&](int pi) {
+        RopeRow<HD> r;
+#pragma unroll
+        for (int h = 0; h < RopeRow<HD>::H2; ++h) {
+            r.c[h] = pi ? rp[1].c[h] : rp[0].c[h];
+            r.s[h] = pi ? rp[1].s[h] : rp[0].s[h];
+        }
+        return r;
+    };
     // wave 0: the step's key rows, wave 1: value rows, wave w: query head
     // g * grp + w (later heads of a large group are read when used)
     float pin[2][J];
@@ -968,21 +1013,14 @@ __global__ __launch_bounds__(kThreadsT, HD <= 128 ? 4 : 3) void k_attn(AttnArgs 
     for (int pi = 0; pi < npos; ++pi) {
         const int p = pf + pi;
         const int r = (s == 1) ? pi * B + b : b;
-        const size_t off = kvb + (static_cast<size_t>(p) * nkv + g) * HD;
+        float kr[J];
         if (wave == 0) {
-            float kr[J];
-            norm_rope_regs<HD>(pin[pi], m.k_norm, m.eps, p, m.rope_cos, m.rope_sin, kr);
+            norm_rope_apply<HD>(pin[pi], gk, rope_of(pi), m.eps, kr);
 #pragma unroll
-            for (int j = 0; j < J; ++j) {
-                Ks[p][lane + 64 * j] = kr[j];
-                m.kc[off + lane + 64 * j] = kr[j];
-            }
+            for (int j = 0; j < J; ++j) Ks[p][lane + 64 * j] = kr[j];
         } else if (wave == 1) {
 #pragma unroll
-            for (int j = 0; j < J; ++j) {
-                Vs[p][lane + 64 * j] = pin[pi][j];
-                m.vc[off + lane + 64 * j] = pin[pi][j];
-            }
+            for (int j = 0; j < J; ++j) Vs[p][lane + 64 * j] = pin[pi][j];
         }
         __syncthreads();
         if (pi == 0) QP_TSTAMP(m.tl, 1);
@@ -997,7 +1035,7 @@ __global__ __launch_bounds__(kThreadsT, HD <= 128 ? 4 : 3) void k_attn(AttnArgs 
 #pragma unroll
                 for (int j = 0; j < J; ++j) qv[j] = row[lane + 64 * j];
             }
-            norm_rope_regs<HD>(qv, m.q_norm, m.eps, p, m.rope_cos, m.rope_sin, q);
+            norm_rope_apply<HD>(qv, gq, rope_of(pi), m.eps, q);
 #pragma unroll
             for (int j = 0; j < J; ++j) qs[wave][lane + 64 * j] = q[j];
             const int kt = lane >> 2, k0 = (lane & 3) * SL;
@@ -1038,6 +1076,17 @@ __global__ __launch_bounds__(kThreadsT, HD <= 128 ? 4 : 3) void k_attn(AttnArgs 
             const int ostep = m.frag ? 1024 : 64;
 #pragma unroll
             for (int j = 0; j < J; ++j) op[j * ostep] = to_bf16(o[j] / den);
+        }
+        // this position's key and value into the cache, after the position's
+        // reads: a wave's loads and stores complete in one order, so a store
+        // ahead of them made their waits wait for it too
+        const size_t off = kvb + (static_cast<size_t>(p) * nkv + g) * HD;
+        if (wave == 0) {
+#pragma unroll
+            for (int j = 0; j < J; ++j) m.kc[off + lane + 64 * j] = kr[j];
+        } else if (wave == 1) {
+#pragma unroll
+            for (int j = 0; j < J; ++j) m.vc[off + lane + 64 * j] = pin[pi][j];
         }
         __syncthreads();
     }
