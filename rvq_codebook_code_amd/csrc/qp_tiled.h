@@ -595,9 +595,17 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(GemmArgs g) {
             if (rt % NW != wave) continue;
 #pragma unroll
             for (int c = 0; c < CT; ++c) {
+                // every partial requested first, then summed in kz order
+                f32x4_t pz[kMaxKS];
+#pragma unroll
+                for (int z = 0; z < kMaxKS; ++z)
+                    if (z < g.KS)
+                        pz[z] = __builtin_bit_cast(f32x4_t,
+                                                   __builtin_amdgcn_raw_buffer_load_b128(pr, poff(z, rt, c), 0u, kDevScope));
                 f32x4_t t = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                for (int z = 0; z < g.KS; ++z)
-                    t += __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(pr, poff(z, rt, c), 0u, kDevScope));
+#pragma unroll
+                for (int z = 0; z < kMaxKS; ++z)
+                    if (z < g.KS) t += pz[z];
                 tot[rt][c] = t;
             }
         }
