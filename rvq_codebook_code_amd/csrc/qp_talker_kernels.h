@@ -444,6 +444,17 @@ __global__ __launch_bounds__(kThreadsK) void k_final(FinArgs a) {
     const int b = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nf = a.d / 16;
+    // the first 8 * kThreadsK elements of the row and the gains, requested
+    // with the sums below (one round trip for the whole kernel at d <= 2048)
+    constexpr int kU = 8;
+    const float* xrow = a.x + static_cast<size_t>(b) * a.d;
+    float xv[kU], gv[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+        const int c = min(u * kThreadsK + static_cast<int>(threadIdx.x), a.d - 1);
+        xv[u] = xrow[c];
+        gv[u] = a.g_out[c];
+    }
     float t = 0.f;
     for (int f = threadIdx.x; f < nf; f += kThreadsK) t += a.ss[static_cast<size_t>(b) * nf + f];
     t = wave_sum(t);
@@ -458,8 +469,25 @@ __global__ __launch_bounds__(kThreadsK) void k_final(FinArgs a) {
     __syncthreads();
     const float tot = ((red[0] + red[1]) + red[2]) + red[3];
     const float rinv = 1.0f / sqrtf(tot / static_cast<float>(a.d) + a.eps);
-    for (int c = threadIdx.x; c < a.d; c += kThreadsK)
-        a.H_out[static_cast<size_t>(b) * a.d + c] = a.g_out[c] * (a.x[static_cast<size_t>(b) * a.d + c] * rinv);
+    float* hrow = a.H_out + static_cast<size_t>(b) * a.d;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+        const int c = u * kThreadsK + static_cast<int>(threadIdx.x);
+        if (c < a.d) hrow[c] = gv[u] * (xv[u] * rinv);
+    }
+    for (int c0 = kU * kThreadsK; c0 < a.d; c0 += kU * kThreadsK) {   // d > 2048: the rest, 8 at a time
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int c = min(c0 + u * kThreadsK + static_cast<int>(threadIdx.x), a.d - 1);
+            xv[u] = xrow[c];
+            gv[u] = a.g_out[c];
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int c = c0 + u * kThreadsK + static_cast<int>(threadIdx.x);
+            if (c < a.d) hrow[c] = gv[u] * (xv[u] * rinv);
+        }
+    }
     if (threadIdx.x == 0) {
         unsigned long long kk = kred[0];
         for (int w = 1; w < kThreadsK / 64; ++w) kk = qp::tiled::umax64(kk, kred[w]);
