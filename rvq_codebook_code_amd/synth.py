@@ -359,6 +359,13 @@ TALKER_WORKLOADS: Dict[str, TalkerWorkload] = {
                        vocab=384, rms_eps=1e-6, rope_base=1e4, weight_dtype="q4_0"),
         batch=3, context=40, weight_seed=3012, input_seed=4012,
         description="tiny Talker, Q4_0 weights, B=3, 40 positions of history"),
+    "talker_wide": TalkerWorkload(
+        "talker_wide",
+        TalkerGeometry(d_model=2560, n_layers=1, n_q_heads=4, n_kv_heads=2, head_dim=64, d_ffn=768,
+                       vocab=384, rms_eps=1e-6, rope_base=1e4, weight_dtype="bf16"),
+        batch=3, context=40, weight_seed=3005, input_seed=4005,
+        description="one-layer Talker wider than 2048 (the products' RMSNorm row sums and the final "
+                    "kernel's row in more than one group of loads), bf16 weights, B=3"),
     "talker_l2": TalkerWorkload(
         "talker_l2", TalkerGeometry(n_layers=2, weight_dtype="bf16", **_TALKER_17B),
         batch=4, context=300, weight_seed=3002, input_seed=4002,

@@ -264,12 +264,14 @@ def _run_and_compare(name, model, tk, geom, slots, hist, X, max_batch_rows=None,
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("name", ["talker_tiny", "talker_tiny_q8", "talker_tiny_q4", "talker_l2"])
+@pytest.mark.parametrize("name", ["talker_tiny", "talker_tiny_q8", "talker_tiny_q4", "talker_wide", "talker_l2"])
 def test_talker_steps_against_oracle(name):
     """Rows in permuted slots with histories of different lengths (empty,
     short, several attention splits), three consecutive steps each; bf16,
     Q8_0 and Q4_0 weights (the quantised codes enter the products exactly,
-    as on the predictor's batched path)."""
+    as on the predictor's batched path); and a width above 2048, where the
+    products' RMSNorm row sums and the final kernel's row take more than one
+    group of loads."""
     _torch_dev()
     from rvq_codebook_code_amd import binding as bd
     wl = synth.TALKER_WORKLOADS[name]
