@@ -184,29 +184,20 @@ __global__ __launch_bounds__(kThreadsK) void k_attn(AttnArgs a) {
     qp::tiled::rope_fetch<HD>(a.rope_cos, a.rope_sin, p, hr);
 
     // 0. the chunk's cached keys and values, requested before anything else
-    //    (they do not depend on this step): keys LP lanes per position, 16
-    //    positions per pass; values one row per position, wave w taking
-    //    positions w, w+4, ...
+    //    (they do not depend on this step): LP lanes per position, 8
+    //    elements (16 bytes) each, PPW positions per wave per pass, the same
+    //    positions for keys and values
     constexpr int KP = kMaxCh / (4 * PPW);
-    constexpr int VP = kMaxCh / 4;
     const int grp = lane / LP, sub = lane % LP;
-    uint4 kraw[KP];
-    uint32_t vraw[VP];
+    uint4 kraw[KP], vraw[KP];
 #pragma unroll
     for (int i = 0; i < KP; ++i) {
         const int t = i * 4 * PPW + wave * PPW + grp;
         kraw[i] = make_uint4(0u, 0u, 0u, 0u);
-        if (t < cnt && p0 + t != p)
-            kraw[i] = *reinterpret_cast<const uint4*>(kh + static_cast<size_t>(p0 + t) * HD + sub * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < VP; ++i) {
-        const int t = wave + 4 * i;
-        vraw[i] = 0u;
+        vraw[i] = make_uint4(0u, 0u, 0u, 0u);
         if (t < cnt && p0 + t != p) {
-            const uint16_t* src = vh + static_cast<size_t>(p0 + t) * HD + lane * J;
-            if constexpr (J == 2) vraw[i] = *reinterpret_cast<const uint32_t*>(src);
-            else vraw[i] = src[0];
+            kraw[i] = *reinterpret_cast<const uint4*>(kh + static_cast<size_t>(p0 + t) * HD + sub * 8);
+            vraw[i] = *reinterpret_cast<const uint4*>(vh + static_cast<size_t>(p0 + t) * HD + sub * 8);
         }
     }
 
@@ -294,40 +285,52 @@ __global__ __launch_bounds__(kThreadsK) void k_attn(AttnArgs a) {
     }
     __syncthreads();
 
-    // 4. weighted values: wave w takes positions w, w+4, ...; lane holds
-    //    elements lane*J .. lane*J+J-1 (one coalesced row per position)
-    float acc[R][J];
+    // 4. weighted values, over the positions of the scores: a lane sums
+    //    elements sub*8 .. +7 over its positions, the PPW position groups of
+    //    a wave are then added across lanes (the same result in every lane
+    //    of a column), and the four waves through LDS in wave order
+    float acc[R][8];
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int j = 0; j < J; ++j) acc[r][j] = 0.f;
+        for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
 #pragma unroll
-    for (int i = 0; i < VP; ++i) {
-        const int t = wave + 4 * i;
-        if (t >= cnt) break;
-        float v[J];
-        if (p0 + t != p) {
-            if constexpr (J == 2) {
-                v[0] = __uint_as_float(vraw[i] << 16);
-                v[1] = __uint_as_float(vraw[i] & 0xFFFF0000u);
+    for (int i = 0; i < KP; ++i) {
+        const int t = i * 4 * PPW + wave * PPW + grp;
+        if (t < cnt) {
+            float v8[8];
+            if (p0 + t != p) {
+                const uint32_t w4[4] = {vraw[i].x, vraw[i].y, vraw[i].z, vraw[i].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v8[2 * e] = __uint_as_float(w4[e] << 16);
+                    v8[2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u);
+                }
             } else {
-                v[0] = bf16_to_f32(vraw[i]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v8[e] = vn_s[sub * 8 + e];
             }
-        } else {
 #pragma unroll
-            for (int j = 0; j < J; ++j) v[j] = vn_s[lane * J + j];
-        }
+            for (int r = 0; r < R; ++r) {
+                const float w = w_s[r][t];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const float w = w_s[r][t];
-#pragma unroll
-            for (int j = 0; j < J; ++j) acc[r][j] = fmaf(w, v[j], acc[r][j]);
+                for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(w, v8[e], acc[r][e]);
+            }
         }
     }
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int j = 0; j < J; ++j) red_s[wave][r][lane * J + j] = acc[r][j];
+        for (int e = 0; e < 8; ++e) {
+#pragma unroll
+            for (int o = LP; o < 64; o <<= 1) acc[r][e] += __shfl_xor(acc[r][e], o, 64);
+        }
+    if (grp == 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) red_s[wave][r][sub * 8 + e] = acc[r][e];
+    }
     __syncthreads();
     float o[J];
     if (wave < R) {
